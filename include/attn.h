@@ -1,0 +1,138 @@
+/*
+ * attn.h -- C ABI of the exact fused attention library (libattn.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * computed one tile at a time with an online softmax, so that the N x N
+ * score matrix S and probability matrix P never reach device memory
+ * ("13% more FLOPs, 5.7x faster: how FlashAttention's online softmax keeps
+ * the NxN matrix out of HBM", sections "Softmax is the anti-tiling
+ * operation" and "FlashAttention's move: rescale the output, too";
+ * "FlashAttention" explainer, Steps 3-4 and "What is FlashAttention?").
+ * The forward saves only O and one statistic per row, and the backward
+ * rebuilds S and P from Q, K, V and that statistic (same blog post,
+ * section "The backward pass: recompute instead of read").
+ *
+ * Conventions shared by every entry point
+ *  - Tensors q, k, v, o, dO, dq, dk, dv are device pointers to contiguous
+ *    row-major [B, H, N, d] arrays (d fastest) of the element type `dtype`.
+ *    lse is a device pointer to a contiguous [B, H, N] float array.  Every
+ *    pointer must be 16-byte aligned.
+ *  - d is 64 or 128.  B, H, N >= 0; if any of them is 0 the call does
+ *    nothing and returns ATTN_OK (pointers are then not examined).
+ *    N * d must stay below 2^30 elements per head.
+ *  - scale is any finite float (usually 1/sqrt(d)).  causal is 0 (every key
+ *    visible) or 1 (query i sees keys 0..i; Q and K have the same length so
+ *    the mask is the lower triangle).
+ *  - The caller owns all memory.  The library allocates nothing, frees
+ *    nothing and does not synchronise: work is enqueued on `stream` (a
+ *    hipStream_t; NULL is the default stream) and the call returns once it
+ *    is enqueued.  Outputs are overwritten entirely (never accumulated into)
+ *    and must not overlap any input.
+ *  - Arguments are validated before anything is enqueued: a negative
+ *    status means nothing was launched and no output was touched, except
+ *    ATTN_ERR_LAUNCH, which reports a failed kernel launch
+ *    (hipGetLastError) after enqueueing.
+ *  - There is no global mutable state; calls are thread-safe.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, o, dO, dq, dk, dv.  Products are accumulated in
+ * fp32 on the matrix cores; outputs are rounded once, to nearest even. */
+typedef enum attn_dtype {
+    ATTN_F16 = 0,  /* IEEE binary16 */
+    ATTN_BF16 = 1  /* bfloat16 */
+} attn_dtype_t;
+
+/* Status codes (0 = success). */
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,     /* B, H or N negative, or N*d too large */
+    ATTN_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
+    ATTN_ERR_DTYPE = -4,     /* dtype is not ATTN_F16 or ATTN_BF16 */
+    ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+    ATTN_ERR_WORKSPACE = -6, /* backward workspace missing or too small */
+    ATTN_ERR_LAUNCH = -7,    /* the HIP runtime rejected a kernel launch */
+    ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite */
+    ATTN_ERR_CAUSAL = -9,    /* causal is neither 0 nor 1 */
+    ATTN_ERR_ALIAS = -10     /* an output overlaps an input or another output */
+};
+
+/*
+ * attn_fwd -- forward pass.
+ *
+ * For every (b, h) and query row i, with A(i) = {0..N-1}, or {0..i} when
+ * causal:
+ *     s_ij   = scale * q_i . k_j                    (j in A(i))
+ *     o_i    = sum_j exp(s_ij - m_i) v_j / l_i
+ *     lse_i  = m_i + ln(l_i)
+ * where m_i = max_j s_ij and l_i = sum_j exp(s_ij - m_i): the running
+ * maximum and normaliser of the online softmax ("Softmax is the anti-tiling
+ * operation"), saved in logsumexp form as the per-row statistic the
+ * backward needs ("The backward pass: recompute instead of read").
+ *
+ *   q, k, v : inputs, [B, H, N, d] of `dtype`
+ *   o       : output, [B, H, N, d] of `dtype`
+ *   lse     : output, [B, H, N] float (natural-log logsumexp of the scaled,
+ *             masked scores of each row)
+ *   stream  : hipStream_t to enqueue on
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
+ * these sizes (0 when there is nothing to do; otherwise a multiple of 256).
+ * Returns 0 for invalid arguments as well; attn_bwd validates them.
+ */
+size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/*
+ * attn_bwd -- backward pass with recomputation.
+ *
+ * Gradients of L = sum(O * dO) with respect to q, k, v.  S and P are
+ * recomputed tile by tile from q, k and the saved lse ("The backward pass:
+ * recompute instead of read"; explainer Step 5 "IO Savings"):
+ *     P_ij  = exp(s_ij - lse_i)  (0 for masked j)
+ *     D_i   = dO_i . o_i
+ *     dv_j  = sum_i P_ij dO_i
+ *     dS_ij = P_ij (dO_i . v_j - D_i)
+ *     dq_i  = scale * sum_j dS_ij k_j
+ *     dk_j  = scale * sum_i dS_ij q_i
+ *
+ *   q, k, v   : the forward's inputs
+ *   o, lse    : the forward's outputs (from attn_fwd with the same scale
+ *               and causal flag)
+ *   dO        : upstream gradient, [B, H, N, d] of `dtype`
+ *   dq, dk, dv: outputs, [B, H, N, d] of `dtype`
+ *   workspace : device scratch of at least attn_bwd_workspace_size(...)
+ *               bytes, 16-byte aligned; its contents on entry do not matter
+ *               and are undefined on return
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+             int dtype, void* stream);
+
+/* attn_status_str -- static, human-readable name of a status code. */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

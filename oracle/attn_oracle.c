@@ -1,0 +1,295 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU oracle for exact scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls
+ * this file; it exists so that tests, the smoke check and the bench's CPU
+ * baseline can compare the HIP kernels against an obviously correct
+ * definition.  It shares no code, header, table or helper with the HIP path.
+ *
+ * What it computes (pages cited by title and section):
+ *
+ *  - oracle_fwd: the definition of attention, O = softmax(S) V with
+ *    S = scale * Q K^T ("FlashAttention" explainer, "What is FlashAttention?"
+ *    and Step 2 "Standard Attention"), the softmax taken row by row as the
+ *    numerically safe three-pass softmax (max, sum of exp(x - m), divide)
+ *    written out in "13% more FLOPs, 5.7x faster", section "Softmax is the
+ *    anti-tiling operation".  The per-row statistic it saves is
+ *    lse = m + ln(l) (natural log), the logsumexp form of the pair (m, l)
+ *    that the same page's section "The backward pass: recompute instead of
+ *    read" says the forward keeps.  Causal masking keeps keys j <= i.
+ *
+ *  - oracle_bwd: the gradient of L = sum(O * dO) with respect to Q, K, V.
+ *    The pages say only that the backward regenerates S and P from Q, K, V
+ *    and the saved statistics; the formulas are the plain chain rule through
+ *    the softmax Jacobian diag(p) - p p^T:
+ *        P_ij  = exp(s_ij - lse_i)            (0 for masked j)
+ *        dV_j  = sum_i P_ij dO_i
+ *        dP_ij = dO_i . V_j
+ *        D_i   = sum_j P_ij dP_ij
+ *        dS_ij = P_ij (dP_ij - D_i)
+ *        dQ_i  = scale * sum_j dS_ij K_j
+ *        dK_j  = scale * sum_i dS_ij Q_i
+ *    These are pinned by central finite differences in the tests, not by
+ *    re-typing them.
+ *
+ *  - oracle_online_softmax / oracle_fwd_online: the pages' online method in
+ *    fp64 -- running max m and normaliser l updated chunk by chunk with the
+ *    factor exp(m_old - m_new) ("Softmax is the anti-tiling operation"), and
+ *    the output accumulator rescaled by the same factor and divided by l
+ *    after the last tile ("FlashAttention's move: rescale the output, too";
+ *    explainer Step 4 "Online Softmax").  The state starts at m = -inf,
+ *    l = 0 with no rescale on the first chunk (explainer Step 4).  These
+ *    serve the pages' worked examples (the 8-score chunked softmax, and the
+ *    Step 6 exactness check of tiled against standard attention).
+ *
+ * All arithmetic is IEEE double with libm exp/log; loops run in the plain
+ * index order of the formulas.  OpenMP only splits independent rows (forward)
+ * or independent heads (backward) across threads.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of keys row i may attend to: all N, or i+1 under the causal mask. */
+static int64_t keys_for_row(int64_t i, int64_t N, int causal) {
+    return causal ? (i + 1) : N;
+}
+
+/* One query row of the forward definition.
+ * qi: d values; kh, vh: N x d of this (batch, head); s: scratch of N doubles.
+ * Writes oi (d values) and *lse_i. */
+static void fwd_row(const double* qi, const double* kh, const double* vh,
+                    int64_t i, int64_t N, int64_t d, double scale, int causal,
+                    double* s, double* oi, double* lse_i) {
+    int64_t nk = keys_for_row(i, N, causal);
+    /* scores s_j = scale * q_i . k_j */
+    for (int64_t j = 0; j < nk; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < d; ++c) acc += qi[c] * kh[j * d + c];
+        s[j] = scale * acc;
+    }
+    /* pass 1: row max */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nk; ++j)
+        if (s[j] > m) m = s[j];
+    /* pass 2: normaliser */
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; ++j) l += exp(s[j] - m);
+    /* pass 3: normalised weights applied to V */
+    for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        double p = exp(s[j] - m) / l;
+        for (int64_t c = 0; c < d; ++c) oi[c] += p * vh[j * d + c];
+    }
+    *lse_i = m + log(l);
+}
+
+/*
+ * oracle_fwd
+ *   q, k, v : [BH, N, d] fp64, row-major (d fastest)
+ *   rows    : flattened row ids r = bh * N + i to compute, or NULL for all
+ *             BH*N rows in order
+ *   o       : [n_rows, d] fp64 output (row order of `rows`)
+ *   lse     : [n_rows] fp64 output
+ *   threads : OpenMP threads to use (<= 0: library default)
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_fwd(const double* q, const double* k, const double* v,
+               double* o, double* lse,
+               int64_t BH, int64_t N, int64_t d, double scale, int causal,
+               const int64_t* rows, int64_t n_rows, int threads) {
+    if (!q || !k || !v || !o || !lse || BH < 0 || N < 0 || d <= 0) return -1;
+    if (!rows) n_rows = BH * N;
+    if (n_rows < 0) return -1;
+    if (rows)
+        for (int64_t t = 0; t < n_rows; ++t)
+            if (rows[t] < 0 || rows[t] >= BH * N) return -1;
+#ifdef _OPENMP
+    if (threads <= 0) threads = omp_get_max_threads();
+#else
+    (void)threads;
+#endif
+    int failed = 0;
+#pragma omp parallel num_threads(threads) reduction(| : failed)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (!s) {
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t t = 0; t < n_rows; ++t) {
+                int64_t r = rows ? rows[t] : t;
+                int64_t bh = r / N, i = r % N;
+                const double* kh = k + bh * N * d;
+                const double* vh = v + bh * N * d;
+                fwd_row(q + r * d, kh, vh, i, N, d, scale, causal, s, o + t * d, lse + t);
+            }
+            free(s);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * oracle_bwd
+ *   q, k, v, dO : [BH, N, d] fp64
+ *   o, lse      : [BH, N, d] and [BH, N] fp64 outputs (the oracle's own forward)
+ *   dq, dk, dv  : [BH, N, d] fp64 outputs
+ * Each head is independent; one thread owns a whole head, so dK and dV
+ * accumulate without races.  Row by row: recompute s and the forward
+ * statistics, form P, dP, D, dS, then add the row's terms to dQ, dK, dV.
+ */
+int oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
+               double* o, double* lse, double* dq, double* dk, double* dv,
+               int64_t BH, int64_t N, int64_t d, double scale, int causal, int threads) {
+    if (!q || !k || !v || !dO || !o || !lse || !dq || !dk || !dv || BH < 0 || N < 0 || d <= 0)
+        return -1;
+#ifdef _OPENMP
+    if (threads <= 0) threads = omp_get_max_threads();
+#else
+    (void)threads;
+#endif
+    int failed = 0;
+#pragma omp parallel num_threads(threads) reduction(| : failed)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* p = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* dp = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (!s || !p || !dp) {
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < BH; ++bh) {
+                const double* qh = q + bh * N * d;
+                const double* kh = k + bh * N * d;
+                const double* vh = v + bh * N * d;
+                const double* gh = dO + bh * N * d;
+                double* oh = o + bh * N * d;
+                double* lh = lse + bh * N;
+                double* dqh = dq + bh * N * d;
+                double* dkh = dk + bh * N * d;
+                double* dvh = dv + bh * N * d;
+                memset(dkh, 0, sizeof(double) * (size_t)(N * d));
+                memset(dvh, 0, sizeof(double) * (size_t)(N * d));
+                for (int64_t i = 0; i < N; ++i) {
+                    int64_t nk = keys_for_row(i, N, causal);
+                    const double* qi = qh + i * d;
+                    const double* gi = gh + i * d;
+                    /* forward quantities of this row: o_i and lse_i */
+                    fwd_row(qi, kh, vh, i, N, d, scale, causal, s, oh + i * d, lh + i);
+                    /* s was overwritten by fwd_row with the scaled scores; P from lse */
+                    for (int64_t j = 0; j < nk; ++j) p[j] = exp(s[j] - lh[i]);
+                    /* dP_ij = dO_i . v_j */
+                    for (int64_t j = 0; j < nk; ++j) {
+                        double acc = 0.0;
+                        for (int64_t c = 0; c < d; ++c) acc += gi[c] * vh[j * d + c];
+                        dp[j] = acc;
+                    }
+                    /* D_i = sum_j P_ij dP_ij */
+                    double Di = 0.0;
+                    for (int64_t j = 0; j < nk; ++j) Di += p[j] * dp[j];
+                    /* dS, then the three gradient sums */
+                    for (int64_t c = 0; c < d; ++c) dqh[i * d + c] = 0.0;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        double ds = p[j] * (dp[j] - Di);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dqh[i * d + c] += scale * ds * kh[j * d + c];
+                            dkh[j * d + c] += scale * ds * qi[c];
+                            dvh[j * d + c] += p[j] * gi[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(s);
+        free(p);
+        free(dp);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * oracle_online_softmax: softmax of x[0..n) by the pages' one-pass update,
+ * reading `chunk` scores at a time.
+ *   y        : n outputs, the final probabilities exp(x_j - m) / l
+ *   states   : optional [n_chunks][3] = (m, l, rescale factor) after each
+ *              chunk; the factor is reported as NAN for the first chunk,
+ *              whose history is empty ("none yet")
+ * Returns the number of chunks, or -1 on a bad argument.
+ */
+int64_t oracle_online_softmax(const double* x, int64_t n, int64_t chunk,
+                              double* y, double* states) {
+    if (!x || !y || n < 0 || chunk <= 0) return -1;
+    double m = -INFINITY, l = 0.0;
+    int64_t nc = 0;
+    for (int64_t c0 = 0; c0 < n; c0 += chunk, ++nc) {
+        int64_t c1 = c0 + chunk < n ? c0 + chunk : n;
+        double mb = -INFINITY;
+        for (int64_t j = c0; j < c1; ++j)
+            if (x[j] > mb) mb = x[j];
+        double m_new = mb > m ? mb : m;
+        double lb = 0.0;
+        for (int64_t j = c0; j < c1; ++j) lb += exp(x[j] - m_new);
+        /* empty history: nothing to rescale */
+        double alpha = (m == -INFINITY) ? NAN : exp(m - m_new);
+        l = (m == -INFINITY ? 0.0 : alpha * l) + lb;
+        m = m_new;
+        if (states) {
+            states[3 * nc + 0] = m;
+            states[3 * nc + 1] = l;
+            states[3 * nc + 2] = alpha;
+        }
+    }
+    for (int64_t j = 0; j < n; ++j) y[j] = exp(x[j] - m) / l;
+    return nc;
+}
+
+/*
+ * oracle_fwd_online: the tiled forward of the pages in fp64 for one head.
+ * For each query row, K/V tiles of `tile` keys are visited in order; each
+ * tile updates (m, l) and rescales the unnormalised output accumulator by
+ * exp(m_old - m_new) before adding the tile's sum of exp(s - m_new) * v;
+ * the accumulator is divided by l after the last tile.
+ *   q, k, v : [N, d]; o : [N, d]; lse : [N]
+ */
+int oracle_fwd_online(const double* q, const double* k, const double* v,
+                      double* o, double* lse, int64_t N, int64_t d,
+                      double scale, int causal, int64_t tile) {
+    if (!q || !k || !v || !o || !lse || N < 0 || d <= 0 || tile <= 0) return -1;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(tile));
+    if (!s) return -1;
+    for (int64_t i = 0; i < N; ++i) {
+        int64_t nk = keys_for_row(i, N, causal);
+        double m = -INFINITY, l = 0.0;
+        double* oi = o + i * d;
+        for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+        for (int64_t j0 = 0; j0 < nk; j0 += tile) {
+            int64_t j1 = j0 + tile < nk ? j0 + tile : nk;
+            double mb = -INFINITY;
+            for (int64_t j = j0; j < j1; ++j) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c) acc += q[i * d + c] * k[j * d + c];
+                s[j - j0] = scale * acc;
+                if (s[j - j0] > mb) mb = s[j - j0];
+            }
+            double m_new = mb > m ? mb : m;
+            double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+            l *= alpha;
+            for (int64_t c = 0; c < d; ++c) oi[c] *= alpha;
+            for (int64_t j = j0; j < j1; ++j) {
+                double pj = exp(s[j - j0] - m_new);
+                l += pj;
+                for (int64_t c = 0; c < d; ++c) oi[c] += pj * v[j * d + c];
+            }
+            m = m_new;
+        }
+        for (int64_t c = 0; c < d; ++c) oi[c] /= l;
+        lse[i] = m + log(l);
+    }
+    free(s);
+    return 0;
+}

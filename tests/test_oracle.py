@@ -1,0 +1,298 @@
+"""Pins for the fp64 CPU oracle.
+
+Each test ties the oracle to something other than itself: values the pages
+print, closed forms, invariants of the mathematics, an independent library
+routine (torch's CPU scaled_dot_product_attention in fp64), an independent
+materialised NumPy implementation, or finite differences.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# The pages' worked examples
+# ---------------------------------------------------------------------------
+
+def _page_example():
+    with open(os.path.join(GOLDEN, "online_softmax_8.json")) as f:
+        return json.load(f)
+
+
+def test_online_softmax_page_example():
+    """Explainer Step 4: eight scores read two at a time; the result shown
+    to two decimals is the full softmax."""
+    g = _page_example()
+    x = np.array(g["scores"])
+    y, st = oracle.online_softmax(x, g["chunk"])
+    assert len(st) == g["n_chunks"] == 4
+    np.testing.assert_array_equal(np.round(y, 2), np.array(g["full_softmax_2dp"]))
+    # running max after each chunk is the max of the prefix read so far
+    np.testing.assert_array_equal(st[:, 0], [3.0, 3.0, 4.5, 4.5])
+    # first chunk: empty history, no rescale ("none yet")
+    assert math.isnan(st[0, 2])
+    # chunk 2 (2.1 after 0.4) and chunk 4 keep the max: factor exactly 1
+    assert st[1, 2] == 1.0 and st[3, 2] == 1.0
+    # chunk 3 lifts the max from 3.0 to 4.5: factor e^(3.0 - 4.5)
+    assert st[2, 2] == pytest.approx(math.exp(-1.5), rel=1e-15)
+    # probabilities sum to one
+    assert abs(y.sum() - 1.0) < 1e-15
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 4, 5, 8, 100])
+def test_online_softmax_chunk_invariance(chunk):
+    """'Exact, not approximate': any chunking gives the one-shot softmax."""
+    g = _page_example()
+    x = np.array(g["scores"])
+    y_ref, _ = oracle.online_softmax(x, len(x))
+    y, _ = oracle.online_softmax(x, chunk)
+    np.testing.assert_allclose(y, y_ref, rtol=0, atol=2e-16)
+
+
+def test_attention_probe_exposes_softmax():
+    """With q = e0, k_j = x_j e0, one-hot v_j = e_j and scale 1, row 0 of O
+    is the softmax of the page's eight scores."""
+    g = _page_example()
+    x = np.array(g["scores"])
+    N = d = 8
+    q = np.zeros((N, d)); q[:, 0] = 1.0
+    k = np.zeros((N, d)); k[:, 0] = x
+    v = np.eye(N)
+    o, lse = oracle.fwd(q, k, v, 1.0)
+    np.testing.assert_array_equal(np.round(o[0], 2), np.array(g["full_softmax_2dp"]))
+    y, _ = oracle.online_softmax(x, 2)
+    np.testing.assert_allclose(o[0], y, rtol=0, atol=1e-15)
+    # every row sees the same scores here
+    np.testing.assert_allclose(o, np.tile(o[0], (N, 1)), rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_equals_standard_page_check(causal):
+    """Explainer Step 6: d = 8, four tiles of up to four keys; the tiled
+    online-softmax output differs from standard attention only by rounding
+    (the page shows 2.2e-16)."""
+    N, d = 16, 8
+    q, k, v = rand((N, d), 1), rand((N, d), 2), rand((N, d), 3)
+    o_t, lse_t = oracle.fwd_online(q, k, v, 1 / math.sqrt(d), causal, tile=4)
+    o, lse = oracle.fwd(q, k, v, 1 / math.sqrt(d), causal)
+    assert np.abs(o_t - o).max() <= 1e-15
+    assert np.abs(lse_t - lse).max() <= 1e-14
+    o_b, lse_b, _ = brute.fwd(q, k, v, 1 / math.sqrt(d), causal)
+    assert np.abs(o_t - o_b).max() <= 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants of the forward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_p_sum_to_one(causal):
+    """A column of ones in V comes out as ones: every row of P sums to 1."""
+    B, H, N, d = 2, 3, 37, 16
+    q, k, v = rand((B, H, N, d), 4) * 3, rand((B, H, N, d), 5) * 3, rand((B, H, N, d), 6)
+    v[..., 0] = 1.0
+    o, _ = oracle.fwd(q, k, v, 0.7, causal)
+    assert np.abs(o[..., 0] - 1.0).max() <= 1e-15
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_scores_give_mean_v(causal):
+    """Q = 0 makes every score equal: O is the mean of the visible V rows and
+    lse = ln(number of visible keys)."""
+    B, H, N, d = 1, 2, 29, 8
+    q = np.zeros((B, H, N, d))
+    k, v = rand((B, H, N, d), 7), rand((B, H, N, d), 8)
+    o, lse = oracle.fwd(q, k, v, 0.5, causal)
+    if causal:
+        counts = np.arange(1, N + 1)
+        mean = np.cumsum(v, axis=-2) / counts[:, None]
+        np.testing.assert_allclose(lse, np.broadcast_to(np.log(counts), lse.shape), atol=1e-15)
+    else:
+        mean = np.broadcast_to(v.mean(axis=-2, keepdims=True), v.shape)
+        np.testing.assert_allclose(lse, math.log(N), atol=1e-15)
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-15)
+
+
+def test_single_key():
+    """N = 1: the only key takes all the weight; lse is that key's score."""
+    q, k, v = rand((3, 1, 16), 9), rand((3, 1, 16), 10), rand((3, 1, 16), 11)
+    for causal in (False, True):
+        o, lse = oracle.fwd(q, k, v, 0.25, causal)
+        np.testing.assert_array_equal(o, v)
+        np.testing.assert_allclose(lse[:, 0], 0.25 * np.sum(q[:, 0] * k[:, 0], axis=-1), rtol=1e-15)
+
+
+def test_causal_row_zero_is_v0():
+    q, k, v = rand((2, 20, 8), 12), rand((2, 20, 8), 13), rand((2, 20, 8), 14)
+    o, _ = oracle.fwd(q, k, v, 1.0, True)
+    np.testing.assert_array_equal(o[:, 0], v[:, 0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_affine_in_v(causal):
+    """Rows of P sum to one, so O(a V + b) = a O(V) + b."""
+    q, k, v = rand((2, 33, 8), 15), rand((2, 33, 8), 16), rand((2, 33, 8), 17)
+    o, _ = oracle.fwd(q, k, v, 0.3, causal)
+    o2, _ = oracle.fwd(q, k, 2.5 * v - 1.25, 0.3, causal)
+    np.testing.assert_allclose(o2, 2.5 * o - 1.25, rtol=0, atol=1e-14)
+
+
+def test_key_permutation_invariance():
+    """Without a mask, reordering the (k_j, v_j) pairs changes nothing."""
+    N, d = 41, 8
+    q, k, v = rand((N, d), 18), rand((N, d), 19), rand((N, d), 20)
+    perm = np.random.default_rng(21).permutation(N)
+    o, lse = oracle.fwd(q, k, v, 0.4, False)
+    o2, lse2 = oracle.fwd(q, k[perm], v[perm], 0.4, False)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_of_keys(causal):
+    """Adding a vector c to every key adds scale*q_i.c to row i's scores:
+    O is unchanged and lse moves by exactly that amount."""
+    N, d = 23, 8
+    q, k, v = rand((N, d), 22), rand((N, d), 23), rand((N, d), 24)
+    c = rand((d,), 25) * 4
+    o, lse = oracle.fwd(q, k, v, 0.6, causal)
+    o2, lse2 = oracle.fwd(q, k + c, v, 0.6, causal)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse + 0.6 * (q @ c), rtol=0, atol=1e-12)
+
+
+def test_large_logits_are_stable():
+    """Scores near +-1000 would overflow exp without the max subtraction
+    (explainer Step 4: fp16 overflows above e^11.1); the oracle stays finite
+    and matches the same problem with every score shifted down."""
+    N, d = 16, 4
+    q = np.zeros((N, d)); q[:, 0] = 1.0
+    k = rand((N, d), 26); k[:, 0] = 1000.0 + np.arange(N) * 0.5
+    v = rand((N, d), 27)
+    o, lse = oracle.fwd(q, k, v, 1.0, False)
+    k2 = k.copy(); k2[:, 0] -= 1000.0
+    o2, lse2 = oracle.fwd(q, k2, v, 1.0, False)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse - 1000.0, lse2, rtol=0, atol=1e-12)
+
+
+def test_row_subset_matches_full():
+    B, H, N, d = 2, 2, 50, 8
+    q, k, v = rand((B, H, N, d), 28), rand((B, H, N, d), 29), rand((B, H, N, d), 30)
+    for causal in (False, True):
+        o, lse = oracle.fwd(q, k, v, 0.35, causal)
+        rows = np.array([0, 7, 49, 50, 123, 199])
+        o_s, lse_s = oracle.fwd(q, k, v, 0.35, causal, rows=rows)
+        np.testing.assert_array_equal(o_s, o.reshape(-1, d)[rows])
+        np.testing.assert_array_equal(lse_s, lse.reshape(-1)[rows])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 4), (1, 2, 5, 8), (2, 1, 17, 16), (1, 3, 64, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_materialised_brute_force(shape, causal):
+    q, k, v = rand(shape, 31) * 2, rand(shape, 32) * 2, rand(shape, 33)
+    o, lse = oracle.fwd(q, k, v, 0.8, causal)
+    o_b, lse_b, _ = brute.fwd(q, k, v, 0.8, causal)
+    assert np.abs(o - o_b).max() <= 1e-12
+    assert np.abs(lse - lse_b).max() <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_sdpa_fp64(causal):
+    """torch's CPU scaled_dot_product_attention in fp64 is an independent
+    library implementation of the same definition."""
+    shape = (2, 3, 45, 16)
+    q, k, v = rand(shape, 34), rand(shape, 35), rand(shape, 36)
+    scale = 1 / math.sqrt(16)
+    o, _ = oracle.fwd(q, k, v, scale, causal)
+    t = [torch.from_numpy(a) for a in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=scale)
+    assert np.abs(o - ref.numpy()).max() <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, v, dO, scale, causal):
+    o, _ = oracle.fwd(q, k, v, scale, causal)
+    return float(np.sum(o * dO))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 3), (5, 4), (8, 2)])
+def test_backward_finite_differences(causal, N, d):
+    """Central differences of L = sum(O * dO) pin the gradient formulas
+    without restating them."""
+    rng = np.random.default_rng(37 + N)
+    q, k, v, dO = (rng.standard_normal((N, d)) for _ in range(4))
+    scale = 0.9
+    _, _, dq, dk, dv = oracle.bwd(q, k, v, dO, scale, causal)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], dO, scale, causal)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], dO, scale, causal)
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.abs(num - g).max() / max(1.0, np.abs(g).max())
+        assert err <= 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """Rows of dS sum to zero, so the key gradients sum to zero; the value
+    gradients sum to the summed upstream gradient (rows of P sum to one)."""
+    shape = (2, 2, 40, 8)
+    q, k, v, dO = (rand(shape, s) for s in (40, 41, 42, 43))
+    o, lse, dq, dk, dv = oracle.bwd(q, k, v, dO, 0.5, causal)
+    assert np.abs(dk.sum(axis=-2)).max() <= 1e-12
+    np.testing.assert_allclose(dv.sum(axis=-2), dO.sum(axis=-2), rtol=0, atol=1e-12)
+    o_f, lse_f = oracle.fwd(q, k, v, 0.5, causal)
+    np.testing.assert_array_equal(o, o_f)
+    np.testing.assert_array_equal(lse, lse_f)
+
+
+def test_backward_single_key():
+    """N = 1: P = 1 so dq = dk = 0 and dv = dO."""
+    q, k, v, dO = (rand((3, 1, 8), s) for s in (44, 45, 46, 47))
+    for causal in (False, True):
+        _, _, dq, dk, dv = oracle.bwd(q, k, v, dO, 0.7, causal)
+        assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+        np.testing.assert_array_equal(dv, dO)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_brute_and_autograd(causal):
+    shape = (2, 2, 33, 16)
+    q, k, v, dO = (rand(shape, s) for s in (48, 49, 50, 51))
+    scale = 0.25
+    _, _, dq, dk, dv = oracle.bwd(q, k, v, dO, scale, causal)
+    _, _, dq_b, dk_b, dv_b = brute.bwd(q, k, v, dO, scale, causal)
+    for a, b in ((dq, dq_b), (dk, dk_b), (dv, dv_b)):
+        assert np.abs(a - b).max() <= 1e-12
+    t = [torch.from_numpy(a).requires_grad_(True) for a in (q, k, v)]
+    out = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=scale)
+    out.backward(torch.from_numpy(dO))
+    for a, tt in ((dq, t[0]), (dk, t[1]), (dv, t[2])):
+        assert np.abs(a - tt.grad.numpy()).max() <= 1e-12
