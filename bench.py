@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact fused attention path on one MI355X.
+
+One step is one pass of the whole hot path over one batch: the fused
+forward (O and lse) followed by the recomputing backward (dq, dk, dv) on
+the seven-billion-parameter-layer-shaped workload (B=4, H=32, N=4096,
+d=128, bf16, causal, 1% of K rows x8), inputs resident in HBM.
+
+Prints ONE JSON line: TFLOP/s of the step (credited FLOPs: forward
+4*B*H*N^2*d/2 under the causal mask, backward 2.5x that), with a per-phase
+breakdown, the roofline of the dominant kernel measured live with HIP events
+on the launch stream, a sampled parity check against the fp64 oracle, and
+the oracle itself timed on the host cores on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import exact_io_aware_40_amd as attn  # noqa: E402
+from exact_io_aware_40_amd import inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16/fp16 matrix peak
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_io_aware_40_amd/csrc/attn_fwd.hip",
+                  "exact_io_aware_40_amd/csrc/attn_bwd.hip",
+                  "exact_io_aware_40_amd/csrc/attn_common.h"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_layer_fwd",
+                    help="shape of the batch (default: the 7B-layer-shaped workload)")
+    ap.add_argument("--phase", choices=["step", "fwd", "bwd"], default="step",
+                    help="time the whole step (default) or one phase only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of each oracle sample")
+    ap.add_argument("--no-parity", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, t, scale, budget_s):
+    """The fp64 oracle on this host's cores over a bounded sample of the
+    same workload: sampled query rows for the forward, whole heads for the
+    backward.  Returns the JSON object."""
+    import oracle
+    cores = oracle.default_threads()
+    B, H, N, d = w.B, w.H, w.N, w.d
+    BH = B * H
+    rng = np.random.default_rng(12345)
+    # forward: rows drawn uniformly over all heads and positions
+    q64 = t["q"].reshape(BH, N, d)
+    k64 = t["k"].reshape(BH, N, d)
+    v64 = t["v"].reshape(BH, N, d)
+    heads = rng.choice(BH, size=min(BH, 8), replace=False)
+    sub = lambda x: x[heads].double().numpy()  # noqa: E731
+    qs, ks, vs = sub(q64), sub(k64), sub(v64)
+    # calibrate on a small batch, then size the sample to the budget
+    n_cal = 64 * cores
+    rows = rng.choice(len(heads) * N, size=n_cal, replace=False)
+    t0 = time.perf_counter()
+    oracle.fwd(qs, ks, vs, scale, w.causal, rows=rows, threads=cores)
+    t_cal = time.perf_counter() - t0
+    n_rows = int(min(len(heads) * N, max(n_cal, n_cal * budget_s / max(t_cal, 1e-3))))
+    rows = rng.choice(len(heads) * N, size=n_rows, replace=False)
+    t0 = time.perf_counter()
+    oracle.fwd(qs, ks, vs, scale, w.causal, rows=rows, threads=cores)
+    t_fwd = time.perf_counter() - t0
+    i = rows % N
+    keys = (i + 1) if w.causal else np.full_like(i, N)
+    f_fwd = float(np.sum(4.0 * keys * d))
+    # backward: whole heads (the oracle splits heads across threads)
+    nh = cores
+    bheads = rng.choice(BH, size=min(BH, nh), replace=False)
+    g64 = inputs.normal((B, H, N, d), w.seed, inputs.TENSOR_IDS["dO"], w.torch_dtype).reshape(BH, N, d)
+    subb = lambda x: x[bheads].double().numpy()  # noqa: E731
+    t0 = time.perf_counter()
+    oracle.bwd(subb(q64), subb(k64), subb(v64), subb(g64), scale, w.causal, threads=cores)
+    t_bwd = time.perf_counter() - t0
+    f_bwd = len(bheads) * 2.5 * 4.0 * N * N * d * (0.5 if w.causal else 1.0)
+    val = (f_fwd + f_bwd) / (t_fwd + t_bwd) / 1e12
+    return {
+        "value": val, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{n_rows} query rows from {len(heads)} heads (forward, {t_fwd:.1f} s) and "
+                   f"{len(bheads)} whole heads (backward, {t_bwd:.1f} s) of {w.name}; fp64; "
+                   f"credited FLOPs as on the GPU"),
+        "fwd_tflops": f_fwd / t_fwd / 1e12, "bwd_tflops": f_bwd / t_bwd / 1e12,
+    }
+
+
+def sampled_parity(w, t, o, lse, scale):
+    import oracle
+    BH, N, d = w.B * w.H, w.N, w.d
+    rng = np.random.default_rng(7)
+    heads = [0, BH - 1] + list(rng.choice(BH, size=2, replace=False))
+    rows = []
+    for hd in heads:
+        rows += [hd * N + r for r in (0, N // 2, N - 1)] + list(hd * N + rng.choice(N, 13, replace=False))
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    o_ref, l_ref = oracle.fwd(t["q"].reshape(BH, N, d).double().numpy(),
+                              t["k"].reshape(BH, N, d).double().numpy(),
+                              t["v"].reshape(BH, N, d).double().numpy(),
+                              scale, w.causal, rows=rows)
+    idx = torch.from_numpy(rows).to(o.device)
+    og = o.reshape(-1, d)[idx].double().cpu().numpy()
+    lg = lse.reshape(-1)[idx].double().cpu().numpy()
+    return {"rows": int(len(rows)), "max_abs_o": float(np.abs(og - o_ref).max()),
+            "max_abs_lse": float(np.abs(lg - l_ref).max())}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    scale = 1.0 / math.sqrt(w.d)
+    scale32 = float(np.float32(scale))
+    t = inputs.make_inputs(w)
+    if "dO" not in t:
+        t["dO"] = inputs.normal((w.B, w.H, w.N, w.d), w.seed, inputs.TENSOR_IDS["dO"], w.torch_dtype)
+    q, k, v, dO = (t[x].to(dev) for x in ("q", "k", "v", "dO"))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    code = attn.ATTN_BF16 if w.dtype == "bf16" else attn.ATTN_F16
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(max(256, attn.attn_bwd_workspace_size(B, H, N, d, code)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    causal = int(w.causal)
+
+    def fwd():
+        st = attn.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           B, H, N, d, scale, causal, code, code, sp)
+        if st:
+            raise attn.AttnError(st, "attn_fwd")
+
+    def bwd():
+        st = attn.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           ws.data_ptr(), ws.numel(), B, H, N, d, scale, causal, code, code, sp)
+        if st:
+            raise attn.AttnError(st, "attn_bwd")
+
+    f_fwd = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
+    f_bwd = 2.5 * f_fwd
+    phases = {"step": (fwd, bwd), "fwd": (fwd,), "bwd": (bwd,)}[args.phase]
+    if args.phase == "bwd":
+        fwd()
+    flops_step = {"step": f_fwd + f_bwd, "fwd": f_fwd, "bwd": f_bwd}[args.phase]
+
+    for _ in range(args.warmup):
+        for p in phases:
+            p()
+    torch.cuda.synchronize()
+
+    # timed region: events around every call on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for j, p in enumerate(phases):
+            p()
+            ev[s][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([[ev[s][j].elapsed_time(ev[s][j + 1]) for j in range(len(phases))]
+                    for s in range(args.steps)])  # ms
+    ms_step = wall * 1e3 / args.steps
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    names = {"step": ["fwd", "bwd"], "fwd": ["fwd"], "bwd": ["bwd"]}[args.phase]
+    phase_flops = {"fwd": f_fwd, "bwd": f_bwd}
+    breakdown = {}
+    for j, nm in enumerate(names):
+        mean_ms = float(per[:, j].mean())
+        breakdown[nm] = {"ms_mean": mean_ms, "ms_min": float(per[:, j].min()),
+                         "tflops": phase_flops[nm] / (mean_ms * 1e-3) / 1e12,
+                         "frac_of_peak": phase_flops[nm] / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    # roofline of the forward kernel (one launch per attn_fwd call)
+    dom = "fwd" if "fwd" in breakdown else "bwd"
+    dom_ms = breakdown[dom]["ms_mean"]
+    dom_flops = phase_flops[dom]
+    traffic = None
+    tp = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tp):
+        try:
+            rec = json.load(open(tp))
+            entry = rec.get(w.name, {}).get(dom)
+            if entry and entry.get("source_hash") == source_hash():
+                traffic = entry.get("bytes")
+        except (ValueError, OSError):
+            traffic = None
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": {"fwd": "fwd_kernel", "bwd": "dq_kernel+dkdv_kernel"}[dom],
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s at 1 GPU + % of bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}; step = {'+'.join(names)}",
+                   "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
+                   "causal": w.causal, "parallelism": "none (1 GPU)"},
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "phases": breakdown,
+        "roofline": roofline,
+        "kernel_source_hash": source_hash(),
+    }
+    if not args.no_parity:
+        if args.phase == "bwd":
+            fwd()
+        torch.cuda.synchronize()
+        out["parity"] = sampled_parity(w, t, o, lse, scale32)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, t, scale32, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""Exact fused attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libattn.so`` (declared in
+``include/attn.h``).  It only marshals arguments: every step of the
+computation runs in the library's HIP kernels.  torch supplies device
+memory and the current stream.
+
+Low level (same names and argument order as the C ABI, raw integers and
+device pointers):  :func:`attn_fwd`, :func:`attn_bwd`,
+:func:`attn_bwd_workspace_size`, :func:`attn_status_str`.
+
+Tensor level:  :func:`forward` and :func:`backward`.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_status_str",
+    "forward", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
+]
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+ATTN_F32 = 2
+_DTYPE_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+_OUT_CODE = {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by the attention library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_str(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or python exact_io_aware_40_amd/csrc/build.py) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                             ctypes.c_size_t)
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd.argtypes = [vp] * 10 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [i32]
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# C ABI, one to one
+# ---------------------------------------------------------------------------
+
+def attn_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+             scale: float, causal: int, dtype: int, out_dtype: int, stream: int) -> int:
+    return _load().attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, out_dtype, stream)
+
+
+def attn_bwd_workspace_size(B: int, H: int, N: int, d: int, dtype: int) -> int:
+    return _load().attn_bwd_workspace_size(B, H, N, d, dtype)
+
+
+def attn_bwd(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, dk: int, dv: int,
+             workspace: int, workspace_bytes: int, B: int, H: int, N: int, d: int,
+             scale: float, causal: int, dtype: int, out_dtype: int, stream: int) -> int:
+    return _load().attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes,
+                            B, H, N, d, scale, causal, dtype, out_dtype, stream)
+
+
+def attn_status_str(status: int) -> str:
+    return _load().attn_status_str(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# Tensor level
+# ---------------------------------------------------------------------------
+
+def _check(t: torch.Tensor, name: str, like: Optional[torch.Tensor] = None, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if like is not None:
+        want = like.dtype if dtype is None else dtype
+        if t.shape != like.shape or t.dtype != want or t.device != like.device:
+            raise ValueError(f"{name} must be {want} and match q in shape and device")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _out_dtype(q: torch.Tensor, out_dtype) -> torch.dtype:
+    od = q.dtype if out_dtype is None else out_dtype
+    if od not in (q.dtype, torch.float32):
+        raise ValueError(f"out_dtype must be {q.dtype} or torch.float32, got {od}")
+    return od
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+            scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+            out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact attention forward.  q, k, v: [B, H, N, d] fp16/bf16 on the GPU.
+
+    Returns (o [B, H, N, d], lse [B, H, N] float32); o has q's dtype unless
+    out_dtype=torch.float32.  scale defaults to 1/sqrt(d).  The work is
+    enqueued on torch's current stream.
+    """
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"dtype must be float16 or bfloat16, got {q.dtype}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    od = _out_dtype(q, out_dtype if out is None else out[0].dtype)
+    if out is None:
+        o = torch.empty(q.shape, dtype=od, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _check(o, "o", q, od)
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous float32 [B, H, N]")
+    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype], _OUT_CODE[od],
+                  _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return o, lse
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             lse: torch.Tensor, dO: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dq, dk, dv) of sum(o * dO) from the forward's o and lse.
+
+    The backward recomputes S and P from q, k and lse.  The gradients have
+    o's dtype (q's dtype, or float32 when the forward wrote float32).
+    `workspace` (a uint8 device tensor of at least attn_bwd_workspace_size
+    bytes) may be passed to avoid an allocation per call.
+    """
+    _check(q, "q")
+    od = _out_dtype(q, o.dtype)
+    for t, n in ((k, "k"), (v, "v"), (dO, "dO")):
+        _check(t, n, q)
+    _check(o, "o", q, od)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"dtype must be float16 or bfloat16, got {q.dtype}")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _DTYPE_CODE[q.dtype]
+    need = attn_bwd_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty(q.shape, dtype=od, device=q.device) for _ in range(3))
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
+                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                  workspace.data_ptr(), workspace.numel(), B, H, N, d, float(scale),
+                  int(bool(causal)), code, _OUT_CODE[od], _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

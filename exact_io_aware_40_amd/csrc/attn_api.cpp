@@ -1,0 +1,166 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h: argument
+// validation, launch configuration and dispatch to the kernel instances.
+// Validation runs before any HIP call, so every error path is reachable
+// (and testable) without a GPU.
+#include "attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxHeadElems = int64_t(1) << 30;  // N * d per head
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range(const void* p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+// Common checks of sizes, flags and scale.  Returns ATTN_OK or an error;
+// sets *empty when there is nothing to compute.
+int check_common(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+                 int out_dtype, bool* empty) {
+    *empty = false;
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (out_dtype != dtype && out_dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (B == 0 || H == 0 || N == 0) {
+        *empty = true;
+        return ATTN_OK;
+    }
+    if (N * d >= kMaxHeadElems) return ATTN_ERR_SHAPE;
+    // total elements must index with 64-bit offsets and the grid must fit
+    if (B > (int64_t(1) << 31) / H) return ATTN_ERR_SHAPE;
+    const int64_t BH = B * H;
+    if (BH > (int64_t(1) << 62) / (N * d)) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: B, H or N out of range";
+        case ATTN_ERR_HEAD_DIM: return "ATTN_ERR_HEAD_DIM: d must be 64 or 128";
+        case ATTN_ERR_DTYPE:
+            return "ATTN_ERR_DTYPE: dtype must be ATTN_F16 or ATTN_BF16, out_dtype dtype or ATTN_F32";
+        case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: pointers must be 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+        case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
+        case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale must be finite";
+        case ATTN_ERR_CAUSAL: return "ATTN_ERR_CAUSAL: causal must be 0 or 1";
+        case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: an output overlaps an input or another output";
+        default: return "unknown attn status";
+    }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
+             void* stream) {
+    bool empty = false;
+    int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const size_t tbytes = size_t(BH * N * d) * 2;
+    const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
+    const Range ro = range(o, obytes), rl = range(lse, size_t(BH * N) * 4);
+    const Range in[3] = {range(q, tbytes), range(k, tbytes), range(v, tbytes)};
+    for (const Range& r : in)
+        if (overlap(ro, r) || overlap(rl, r)) return ATTN_ERR_ALIAS;
+    if (overlap(ro, rl)) return ATTN_ERR_ALIAS;
+
+    attn::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.N = int(N);
+    const int br = attn::fwd_block_rows();
+    a.nqb = int((N + br - 1) / br);
+    const int64_t total = BH * a.nqb;
+    if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
+    a.total = int(total);
+    a.c = fabsf(scale) * kLog2e;
+    a.negate = scale < 0.f;
+    hipError_t e = attn::launch_fwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    bool empty = false;
+    if (check_common(B, H, N, d, 1.0f, 0, dtype, dtype, &empty) != ATTN_OK || empty) return 0;
+    return attn::bwd_workspace_bytes(B * H, N);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+             int causal, int dtype, int out_dtype, void* stream) {
+    bool empty = false;
+    int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const size_t need = attn::bwd_workspace_bytes(BH, N);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    const size_t tbytes = size_t(BH * N * d) * 2;
+    const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
+    const Range outs[4] = {range(dq, obytes), range(dk, obytes), range(dv, obytes),
+                           range(workspace, need)};
+    const Range ins[6] = {range(q, tbytes), range(k, tbytes), range(v, tbytes),
+                          range(o, obytes), range(dO, tbytes), range(lse, size_t(BH * N) * 4)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+    }
+
+    attn::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dO = dO;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = static_cast<float*>(workspace);
+    a.N = int(N);
+    if (BH > 0x7fffffff / ((N + 63) / 64)) return ATTN_ERR_SHAPE;
+    a.BH = int(BH);
+    a.c = fabsf(scale) * kLog2e;
+    a.scale = scale;
+    a.negate = scale < 0.f;
+    hipError_t e = attn::launch_bwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// attn_common.h -- device-side building blocks shared by the forward and
+// backward attention kernels for gfx950 (CDNA4, wave64).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_{bf16,f16},
+// D[32x32] += A[32x16] * B[16x32], fp32 accumulate), for lane l of a wave:
+//   A operand: 8 elements A[m = l%32][k = 8*(l/32) + e], e = 0..7
+//   B operand: 8 elements B[k = 8*(l/32) + e][n = l%32]
+//   C/D      : 16 floats  D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32], r = 0..15
+// A contraction may visit its k index in any order as long as A and B agree,
+// which lets a probability tile produced in accumulator layout feed the next
+// product as a B operand without any data movement.
+//
+// LDS transpose reads (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane t receives element (t % 4) of the 4-element vector addressed by lane
+// (t / 4 + 4 j) as its element j.  Pointing the 16 lanes of a group at a 4x4
+// arrangement of 4-element row pieces therefore delivers columns, which is
+// how a row-major [key][d] tile is read as the k-contiguous operand of a
+// product that contracts over keys.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Per-element-type pieces: operand vector types, the 32x32x16 product, and
+// round-to-nearest-even conversion of four floats.
+template <typename T> struct Elem;
+
+template <> struct Elem<__bf16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ v4 cvt4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+};
+
+template <> struct Elem<_Float16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ v4 cvt4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+};
+
+template <typename V, typename U> __device__ __forceinline__ V bit_cast(U u) {
+    static_assert(sizeof(V) == sizeof(U), "size mismatch");
+    return __builtin_bit_cast(V, u);
+}
+
+// Value of x held by lane l ^ 32, combined symmetrically: the permlane32
+// swap hands each lane the pair (x[l & 31], x[(l & 31) + 32]).
+__device__ __forceinline__ f32x2 pair32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    f32x2 out;
+    out[0] = __uint_as_float(r[0]);
+    out[1] = __uint_as_float(r[1]);
+    return out;
+}
+__device__ __forceinline__ float max32(float x) {
+    f32x2 p = pair32(x);
+    return fmaxf(p[0], p[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+    f32x2 p = pair32(x);
+    return p[0] + p[1];
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// 8-byte transposing LDS read at byte address `addr` of the LDS window.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* base, int addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + addr));
+}
+
+// Two 4-element pieces -> one 8-element operand.
+template <typename V8>
+__device__ __forceinline__ V8 join8(i16x4 a, i16x4 b) {
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return bit_cast<V8>(v);
+}
+
+// LDS placement of 16-byte granule g of row r in a [rows][D] tile of 16-bit
+// elements.  Tiles are read two ways: 16-byte reads of 8 consecutive rows at
+// one granule column (operands whose k index runs along d), and transposing
+// 8-byte reads of 4 aligned consecutive rows by 2 adjacent granules
+// (operands whose k index runs along the rows).  The XOR key's low three
+// bits differ across any 8 consecutive rows and its bits 1-2 differ across
+// any 4 aligned rows, so neither pattern piles onto one bank group.
+template <int D> __device__ __forceinline__ int t_off(int r, int g) {
+    return r * (D * 2) + ((g ^ (((r & 3) << 1) | ((r >> 2) & 1))) << 4);
+}
+
+// Output element stores: four fp32 values, rounded once to nearest even for
+// a 16-bit output type, written as they are for an fp32 output.
+template <typename TO> __device__ __forceinline__ void store4(TO* p, f32x4 x);
+template <> __device__ __forceinline__ void store4<__bf16>(__bf16* p, f32x4 x) {
+    *(bf16x4*)p = __builtin_convertvector(x, bf16x4);
+}
+template <> __device__ __forceinline__ void store4<_Float16>(_Float16* p, f32x4 x) {
+    *(f16x4*)p = __builtin_convertvector(x, f16x4);
+}
+template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 x) { *(f32x4*)p = x; }
+
+// Workgroup id -> logical work item, so that consecutive logical items land
+// on the same XCD.  The dispatcher hands workgroup ids to the 8 XCDs in
+// round-robin order; XCD x receives logical items [base(x), base(x)+count(x)).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+    const int per = total >> 3, rem = total & 7, x = id & 7;
+    return x * per + (x < rem ? x : rem) + (id >> 3);
+}
+
+}  // namespace attn

@@ -1,0 +1,274 @@
+// attn_fwd.hip -- fused attention forward for gfx950.
+//
+// One workgroup owns one block of BR = 128 query rows of one (batch, head);
+// each of its four waves owns 32 of those rows for the whole kernel and
+// writes their output once ("FlashAttention" explainer, Step 3 "Tiling":
+// one Q block stays on chip while K/V tiles stream past, and each block's
+// output is written once).  K/V tiles of BC = 64 keys are staged in LDS with
+// coalesced 16-byte loads; the next tile is fetched into registers while the
+// current one is consumed.
+//
+// Per tile and wave (the pages' online softmax: "13% more FLOPs, 5.7x
+// faster", sections "Softmax is the anti-tiling operation" and
+// "FlashAttention's move: rescale the output, too"; explainer Step 4):
+//   S^T = K Q^T         on the matrix cores (keys x queries, fp32)
+//   mask                causal and ragged-tail tiles only
+//   m_new = max(m, rowmax S)     lanes own query rows; one cross-lane step
+//   alpha = 2^((m - m_new) c),   c = |scale| log2(e), alpha = 0 on the
+//                                first tile (empty history)
+//   P = 2^(S c - m_new c),  l = alpha l + rowsum P
+//   O^T = alpha O^T + V^T P^T    V^T read from the row-major tile with
+//                                transposing LDS reads
+// and after the last tile O = O^T / l (rounded once), lse = m scale + ln l.
+// S and P exist only in registers; nothing of size N x N touches memory.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int BR = 128;   // query rows per workgroup
+constexpr int BC = 64;    // keys per K/V tile
+constexpr int NT = 256;   // threads per workgroup (4 waves)
+
+template <typename T, typename TO, int D, bool CAUSAL>
+__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
+    typedef typename Elem<T>::v8 v8;
+    constexpr int GR = D / 8;              // 16-byte granules per row
+    constexpr int RPP = NT / GR;           // tile rows per load pass
+    constexpr int LOADS = BC / RPP;        // load passes per tile
+    constexpr int KB = BC / 32;            // 32-key blocks per tile
+    constexpr int DK = D / 16;             // k-steps of the S product
+    constexpr int DB = D / 32;             // 32-wide output column blocks
+
+    __shared__ __attribute__((aligned(16))) char sK[BC * D * 2];
+    __shared__ __attribute__((aligned(16))) char sV[BC * D * 2];
+
+    const int N = a.N;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int L = xcd_remap(blockIdx.x, a.total);
+    const int bh = L / a.nqb;
+    int qb = L - bh * a.nqb;
+    if (CAUSAL) qb = a.nqb - 1 - qb;  // heaviest query blocks first
+    const int q0 = qb * BR;
+    const size_t head = (size_t)bh * N * D;
+    const T* __restrict__ Qh = (const T*)a.q + head;
+    const T* __restrict__ Kh = (const T*)a.k + head;
+    const T* __restrict__ Vh = (const T*)a.v + head;
+
+    // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
+    const int qlo = q0 + 32 * w;
+    const int qrow = qlo + l32;
+    i32x4 qf[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) {
+        i32x4 x = {0, 0, 0, 0};
+        if (qrow < N) x = *(const i32x4*)(Qh + (size_t)qrow * D + 16 * kk + 8 * h);
+        if (a.negate) x ^= (int)0x80008000;   // scale < 0: use -Q and |scale|
+        qf[kk] = x;
+    }
+
+    const int kend = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kend + BC - 1) / BC;
+
+    // global -> register staging of one K/V tile
+    const int g_col = tid % GR, g_row = tid / GR;
+    i32x4 kreg[LOADS], vreg[LOADS];
+    auto gload = [&](int j0) {
+#pragma unroll
+        for (int p = 0; p < LOADS; ++p) {
+            const int row = j0 + g_row + p * RPP;
+            i32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+            if (row < N) {
+                kx = *(const i32x4*)(Kh + (size_t)row * D + g_col * 8);
+                vx = *(const i32x4*)(Vh + (size_t)row * D + g_col * 8);
+            }
+            kreg[p] = kx;
+            vreg[p] = vx;
+        }
+    };
+    auto sstore = [&]() {
+#pragma unroll
+        for (int p = 0; p < LOADS; ++p) {
+            const int row = g_row + p * RPP;
+            *(i32x4*)(sK + t_off<D>(row, g_col)) = kreg[p];
+            *(i32x4*)(sV + t_off<D>(row, g_col)) = vreg[p];
+        }
+    };
+
+    const float c = a.c;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    gload(0);
+    sstore();
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * BC;
+        if (t + 1 < ntiles) gload(j0 + BC);
+
+        // 32-key blocks of this tile that hold any key visible to this wave
+        int nb = KB;
+        if (CAUSAL) {
+            const int lim = qlo + 31 - j0;  // last visible key offset in the tile
+            nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
+        }
+        nb = min(nb, (N - j0 + 31) / 32);
+
+        f32x16 s[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
+            if (b < nb) {
+                const int krow = 32 * b + l32;
+#pragma unroll
+                for (int kk = 0; kk < DK; ++kk) {
+                    const i32x4 kx = *(const i32x4*)(sK + t_off<D>(krow, 2 * kk + h));
+                    s[b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), s[b]);
+                }
+            }
+        }
+
+        const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
+        float mloc = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                if (b < nb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const bool ok = key < N && (!CAUSAL || key <= qrow);
+                        s[b][r] = ok ? s[b][r] : -INFINITY;
+                        mloc = fmaxf(mloc, s[b][r]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+                if (b < nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[b][r]);
+        }
+        const float m_new = fmaxf(m_run, max32(mloc));
+        const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run * c - mc);
+
+        float lsum = 0.f;
+        v8 pb[KB][2];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            if (b < nb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    // a masked score is -inf; its exponent is forced to -inf so
+                    // that a zero scale cannot turn it into NaN
+                    float e = fmaf(s[b][r], c, -mc);
+                    if (need_mask) e = (s[b][r] == -INFINITY) ? -INFINITY : e;
+                    const float p = fast_exp2(e);
+                    s[b][r] = p;
+                    lsum += p;
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    f32x4 lo = {s[b][8 * q + 0], s[b][8 * q + 1], s[b][8 * q + 2], s[b][8 * q + 3]};
+                    f32x4 hi = {s[b][8 * q + 4], s[b][8 * q + 5], s[b][8 * q + 6], s[b][8 * q + 7]};
+                    auto l4 = Elem<T>::cvt4(lo);
+                    auto h4 = Elem<T>::cvt4(hi);
+                    pb[b][q] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
+        }
+        l_run = alpha * l_run + lsum;
+        m_run = m_new;
+        if (!__all(alpha == 1.f)) {
+#pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        }
+
+        // O^T += V^T P^T.  B operand chunk (b, q) holds, at k = 8h + e, the
+        // probability of key 32b + 16q + 8(e/4) + 4h + e%4; the transposing
+        // reads fetch V at exactly those keys.
+        const int s16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+            const int gcol = col >> 3, within = (col & 7) * 2;
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                if (b < nb) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int row = 32 * b + 16 * q + 4 * h + (s16 >> 2);
+                        const i16x4 lo = lds_read_tr16(sV, t_off<D>(row, gcol) + within);
+                        const i16x4 hi = lds_read_tr16(sV, t_off<D>(row + 8, gcol) + within);
+                        oacc[cb] = Elem<T>::mma(join8<v8>(lo, hi), pb[b][q], oacc[cb]);
+                    }
+                }
+            }
+        }
+
+        if (t + 1 < ntiles) {
+            __syncthreads();
+            sstore();
+            __syncthreads();
+        }
+    }
+
+    // epilogue: O = O^T / l, one rounding; lse = (m c + log2 l) ln 2
+    const float l_tot = sum32(l_run);
+    const float inv = fast_rcp(l_tot);
+    if (qrow < N) {
+        TO* __restrict__ orow = (TO*)a.o + head + (size_t)qrow * D;
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
+                           oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv};
+                store4<TO>(orow + 32 * cb + 8 * g + 4 * h, x);
+            }
+        }
+        if (h == 0) {
+            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+            a.lse[(size_t)bh * N + qrow] = (mc + fast_log2(l_tot)) * 0.69314718055994531f;
+        }
+    }
+}
+
+template <typename T, typename TO, int D, bool CAUSAL>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, typename TO>
+hipError_t launch_t(const FwdArgs& a, int d, int causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch<T, TO, 64, true>(a, stream) : launch<T, TO, 64, false>(a, stream);
+    return causal ? launch<T, TO, 128, true>(a, stream) : launch<T, TO, 128, false>(a, stream);
+}
+
+}  // namespace
+
+int fwd_block_rows() { return BR; }
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream) {
+    if (dtype == 1)
+        return out_f32 ? launch_t<__bf16, float>(a, d, causal, stream)
+                       : launch_t<__bf16, __bf16>(a, d, causal, stream);
+    return out_f32 ? launch_t<_Float16, float>(a, d, causal, stream)
+                   : launch_t<_Float16, _Float16>(a, d, causal, stream);
+}
+
+}  // namespace attn

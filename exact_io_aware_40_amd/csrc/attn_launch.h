@@ -1,0 +1,49 @@
+// attn_launch.h -- internal interface between the C ABI (attn_api.cpp) and
+// the kernel translation units.  Arguments reaching these functions have
+// already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int N;        // sequence length
+    int nqb;      // query blocks per (batch, head)
+    int total;    // workgroups = B * H * nqb
+    float c;      // |scale| * log2(e): exponent units of the kernel
+    int negate;   // scale < 0: the kernel multiplies Q by -1 (exact)
+};
+
+int fwd_block_rows();
+hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dO;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;   // workspace: D_i = dO_i . o_i, [B*H*N]
+    int N;
+    int BH;
+    float c;        // |scale| * log2(e)
+    float scale;    // the caller's scale (gradient factor)
+    int negate;
+};
+
+size_t bwd_workspace_bytes(int64_t BH, int64_t N);
+hipError_t launch_bwd(const BwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
+
+}  // namespace attn

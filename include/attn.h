@@ -16,7 +16,8 @@
  *
  * Conventions shared by every entry point
  *  - Tensors q, k, v, o, dO, dq, dk, dv are device pointers to contiguous
- *    row-major [B, H, N, d] arrays (d fastest) of the element type `dtype`.
+ *    row-major [B, H, N, d] arrays (d fastest): q, k, v, dO of element type
+ *    `dtype`, o, dq, dk, dv of element type `out_dtype`.
  *    lse is a device pointer to a contiguous [B, H, N] float array.  Every
  *    pointer must be 16-byte aligned.
  *  - d is 64 or 128.  B, H, N >= 0; if any of them is 0 the call does
@@ -46,11 +47,15 @@
 extern "C" {
 #endif
 
-/* Element type of q, k, v, o, dO, dq, dk, dv.  Products are accumulated in
- * fp32 on the matrix cores; outputs are rounded once, to nearest even. */
+/* Element types.  `dtype` (the inputs q, k, v, dO) is ATTN_F16 or ATTN_BF16.
+ * `out_dtype` (the forward's o, which attn_bwd reads back, and the gradients
+ * dq, dk, dv) is either the same as `dtype` or ATTN_F32.  Products are
+ * accumulated in fp32 on the matrix cores; a 16-bit output is rounded once,
+ * to nearest even, from the fp32 result an ATTN_F32 output would hold. */
 typedef enum attn_dtype {
     ATTN_F16 = 0,  /* IEEE binary16 */
-    ATTN_BF16 = 1  /* bfloat16 */
+    ATTN_BF16 = 1, /* bfloat16 */
+    ATTN_F32 = 2   /* IEEE binary32 (outputs only) */
 } attn_dtype_t;
 
 /* Status codes (0 = success). */
@@ -59,7 +64,7 @@ enum attn_status {
     ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
     ATTN_ERR_SHAPE = -2,     /* B, H or N negative, or N*d too large */
     ATTN_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
-    ATTN_ERR_DTYPE = -4,     /* dtype is not ATTN_F16 or ATTN_BF16 */
+    ATTN_ERR_DTYPE = -4,     /* bad dtype, or out_dtype neither dtype nor ATTN_F32 */
     ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = -6, /* backward workspace missing or too small */
     ATTN_ERR_LAUNCH = -7,    /* the HIP runtime rejected a kernel launch */
@@ -82,7 +87,7 @@ enum attn_status {
  * backward needs ("The backward pass: recompute instead of read").
  *
  *   q, k, v : inputs, [B, H, N, d] of `dtype`
- *   o       : output, [B, H, N, d] of `dtype`
+ *   o       : output, [B, H, N, d] of `out_dtype`
  *   lse     : output, [B, H, N] float (natural-log logsumexp of the scaled,
  *             masked scores of each row)
  *   stream  : hipStream_t to enqueue on
@@ -90,7 +95,7 @@ enum attn_status {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-             int dtype, void* stream);
+             int dtype, int out_dtype, void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
@@ -113,10 +118,10 @@ size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int d
  *     dk_j  = scale * sum_i dS_ij q_i
  *
  *   q, k, v   : the forward's inputs
- *   o, lse    : the forward's outputs (from attn_fwd with the same scale
- *               and causal flag)
+ *   o, lse    : the forward's outputs (from attn_fwd with the same scale,
+ *               causal flag and out_dtype); o is [B, H, N, d] of `out_dtype`
  *   dO        : upstream gradient, [B, H, N, d] of `dtype`
- *   dq, dk, dv: outputs, [B, H, N, d] of `dtype`
+ *   dq, dk, dv: outputs, [B, H, N, d] of `out_dtype`
  *   workspace : device scratch of at least attn_bwd_workspace_size(...)
  *               bytes, 16-byte aligned; its contents on entry do not matter
  *               and are undefined on return
@@ -126,7 +131,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-             int dtype, void* stream);
+             int dtype, int out_dtype, void* stream);
 
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);

@@ -44,8 +44,8 @@ def _load():
                                ctypes.c_int64, ctypes.c_double, ctypes.c_int, _i64p,
                                ctypes.c_int64, ctypes.c_int]
     lib.oracle_bwd.restype = ctypes.c_int
-    lib.oracle_bwd.argtypes = [_dp] * 9 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                           ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.oracle_bwd.argtypes = [_dp] * 10 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_double, ctypes.c_int, ctypes.c_int]
     lib.oracle_online_softmax.restype = ctypes.c_int64
     lib.oracle_online_softmax.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
     lib.oracle_fwd_online.restype = ctypes.c_int
@@ -101,21 +101,30 @@ def fwd(q, k, v, scale, causal=False, rows=None, threads=None):
     return o, lse
 
 
-def bwd(q, k, v, dO, scale, causal=False, threads=None):
-    """Gradients of sum(O * dO).  Returns (o, lse, dq, dk, dv), all fp64."""
+def bwd(q, k, v, dO, scale, causal=False, threads=None, o_in=None):
+    """Gradients of sum(O * dO).  Returns (o, lse, dq, dk, dv), all fp64.
+
+    o_in: optional stored forward output; when given, D_i = dO_i . o_in_i
+    (the library's backward contract) instead of sum_j P_ij dP_ij.
+    """
     lib = _load()
     q, k, v, dO = _c(q), _c(k), _c(v), _c(dO)
     lead, N, d = q.shape[:-2], q.shape[-2], q.shape[-1]
     for t in (k, v, dO):
         if t.shape != q.shape:
             raise ValueError("q, k, v, dO must share one shape")
+    if o_in is not None:
+        o_in = _c(o_in)
+        if o_in.shape != q.shape:
+            raise ValueError("o_in must have q's shape")
     BH = int(np.prod(lead)) if lead else 1
     o = np.empty(q.shape, np.float64)
     lse = np.empty(q.shape[:-1], np.float64)
     dq = np.empty(q.shape, np.float64)
     dk = np.empty(q.shape, np.float64)
     dv = np.empty(q.shape, np.float64)
-    rc = lib.oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(o), _ptr(lse), _ptr(dq),
+    rc = lib.oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO),
+                        _ptr(o_in) if o_in is not None else None, _ptr(o), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), BH, N, d, float(scale), int(bool(causal)),
                         int(threads or default_threads()))
     if rc != 0:

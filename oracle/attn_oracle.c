@@ -30,7 +30,10 @@
  *        dQ_i  = scale * sum_j dS_ij K_j
  *        dK_j  = scale * sum_i dS_ij Q_i
  *    These are pinned by central finite differences in the tests, not by
- *    re-typing them.
+ *    re-typing them.  The backward of the library takes the forward's stored
+ *    output o as an input and forms D_i = dO_i . o_i from it; when a caller
+ *    passes that stored o (o_in below), the oracle does the same, which for
+ *    the exact o is the same number as sum_j P_ij dP_ij.
  *
  *  - oracle_online_softmax / oracle_fwd_online: the pages' online method in
  *    fp64 -- running max m and normaliser l updated chunk by chunk with the
@@ -137,6 +140,8 @@ int oracle_fwd(const double* q, const double* k, const double* v,
 /*
  * oracle_bwd
  *   q, k, v, dO : [BH, N, d] fp64
+ *   o_in        : NULL, or [BH, N, d] fp64: a stored forward output to form
+ *                 D_i = dO_i . o_in_i from (instead of sum_j P_ij dP_ij)
  *   o, lse      : [BH, N, d] and [BH, N] fp64 outputs (the oracle's own forward)
  *   dq, dk, dv  : [BH, N, d] fp64 outputs
  * Each head is independent; one thread owns a whole head, so dK and dV
@@ -144,6 +149,7 @@ int oracle_fwd(const double* q, const double* k, const double* v,
  * statistics, form P, dP, D, dS, then add the row's terms to dQ, dK, dV.
  */
 int oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
+               const double* o_in,
                double* o, double* lse, double* dq, double* dk, double* dv,
                int64_t BH, int64_t N, int64_t d, double scale, int causal, int threads) {
     if (!q || !k || !v || !dO || !o || !lse || !dq || !dk || !dv || BH < 0 || N < 0 || d <= 0)
@@ -189,9 +195,14 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
                         for (int64_t c = 0; c < d; ++c) acc += gi[c] * vh[j * d + c];
                         dp[j] = acc;
                     }
-                    /* D_i = sum_j P_ij dP_ij */
+                    /* D_i = sum_j P_ij dP_ij, or dO_i . o_i for a given stored o */
                     double Di = 0.0;
-                    for (int64_t j = 0; j < nk; ++j) Di += p[j] * dp[j];
+                    if (o_in) {
+                        const double* oi = o_in + (bh * N + i) * d;
+                        for (int64_t c = 0; c < d; ++c) Di += gi[c] * oi[c];
+                    } else {
+                        for (int64_t j = 0; j < nk; ++j) Di += p[j] * dp[j];
+                    }
                     /* dS, then the three gradient sums */
                     for (int64_t c = 0; c < d; ++c) dqh[i * d + c] = 0.0;
                     for (int64_t j = 0; j < nk; ++j) {

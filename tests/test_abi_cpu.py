@@ -1,0 +1,117 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments before touching the HIP runtime.
+
+Only calls that fail validation (or have nothing to do) are made here; the
+fake device addresses below are never dereferenced or handed to a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_40_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# status codes as declared in the header
+OK, E_NULL, E_SHAPE, E_HD, E_DT, E_ALIGN, E_WS, E_LAUNCH, E_SCALE, E_CAUSAL, E_ALIAS = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+
+# fake, 16-byte aligned, far-apart addresses (validation only)
+P = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
+                                    "attn_status_str"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(attn.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (OK, E_NULL, E_SHAPE, E_HD, E_DT, E_ALIGN, E_WS, E_LAUNCH, E_SCALE, E_CAUSAL,
+                 E_ALIAS):
+        s = attn.attn_status_str(code)
+        assert s.startswith("ATTN_")
+    assert "unknown" in attn.attn_status_str(12345)
+
+
+def fwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, N=100, d=128, scale=0.1,
+             causal=0, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                         a["d"], a["scale"], a["causal"], a["dtype"], od, a["stream"])
+
+
+def bwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8],
+             ws=P[9], wsb=1 << 20, B=2, H=3, N=100, d=128, scale=0.1, causal=1, dtype=1,
+             out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"], a["dk"],
+                         a["dv"], a["ws"], a["wsb"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                         a["causal"], a["dtype"], od, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), E_NULL), (dict(k=0), E_NULL), (dict(v=0), E_NULL), (dict(o=0), E_NULL),
+    (dict(lse=0), E_NULL),
+    (dict(B=-1), E_SHAPE), (dict(H=-2), E_SHAPE), (dict(N=-5), E_SHAPE),
+    (dict(N=1 << 23), E_SHAPE),
+    (dict(d=96), E_HD), (dict(d=0), E_HD), (dict(d=256), E_HD),
+    (dict(dtype=2), E_DT), (dict(dtype=-1), E_DT), (dict(dtype=1, out_dtype=0), E_DT),
+    (dict(dtype=0, out_dtype=1), E_DT), (dict(out_dtype=3), E_DT),
+    (dict(out_dtype=2, o=P[4] - 200000), E_ALIAS),   # fp32 o reaches lse
+    (dict(q=P[0] + 8), E_ALIGN), (dict(o=P[3] + 2), E_ALIGN), (dict(lse=P[4] + 4), E_ALIGN),
+    (dict(scale=float("nan")), E_SCALE), (dict(scale=float("inf")), E_SCALE),
+    (dict(causal=2), E_CAUSAL), (dict(causal=-1), E_CAUSAL),
+    (dict(o=P[0]), E_ALIAS), (dict(lse=P[1] + 64), E_ALIAS), (dict(lse=P[3] + 128), E_ALIAS),
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=0, o=0)])
+def test_fwd_empty_is_noop(kw):
+    assert fwd(**kw) == OK
+
+
+def test_workspace_size():
+    assert attn.attn_bwd_workspace_size(2, 3, 100, 128, 1) == 2560   # 600 floats -> 256-multiple
+    assert attn.attn_bwd_workspace_size(8, 16, 2048, 128, 1) == 8 * 16 * 2048 * 4
+    assert attn.attn_bwd_workspace_size(0, 3, 100, 128, 1) == 0
+    assert attn.attn_bwd_workspace_size(1, 1, 100, 96, 1) == 0
+    assert attn.attn_bwd_workspace_size(1, 1, 100, 64, 7) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=0), E_NULL), (dict(lse=0), E_NULL), (dict(dq=0), E_NULL), (dict(dv=0), E_NULL),
+    (dict(ws=0), E_WS), (dict(wsb=2559), E_WS),
+    (dict(d=32), E_HD), (dict(dtype=5), E_DT), (dict(N=-1), E_SHAPE),
+    (dict(ws=P[9] + 4), E_ALIGN), (dict(dk=P[7] + 8), E_ALIGN),
+    (dict(scale=float("-inf")), E_SCALE), (dict(causal=3), E_CAUSAL),
+    (dict(dq=P[0]), E_ALIAS), (dict(dk=P[6] + 4096), E_ALIAS), (dict(ws=P[8] + 1024), E_ALIAS),
+    (dict(dv=P[5]), E_ALIAS), (dict(out_dtype=0), E_DT), (dict(dtype=2, out_dtype=2), E_DT),
+    (dict(out_dtype=2, dq=P[7] - 200000), E_ALIAS),   # fp32 dq reaches dk
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_empty_is_noop():
+    assert bwd(B=0, ws=0, wsb=0) == OK

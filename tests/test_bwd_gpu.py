@@ -1,0 +1,137 @@
+"""GPU parity of the backward kernels against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's o and lse (the real pipeline);
+the oracle computes everything in fp64 from the same rounded inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_40_amd as attn
+import oracle
+from exact_io_aware_40_amd import inputs
+from tests._util import TOL, announce, f64, randn, report, report_rounded
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def s32(x):
+    return float(np.float32(x))
+
+
+def gpu_fwd_bwd(q, k, v, dO, causal, scale, out_dtype=None, keep_o=False):
+    """The pipeline as a user runs it: forward, then backward from its o and lse."""
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dO))
+    o, lse = attn.forward(qd, kd, vd, causal=causal, scale=scale, out_dtype=out_dtype)
+    dq, dk, dv = attn.backward(qd, kd, vd, o, lse, gd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return (dq, dk, dv, o) if keep_o else (dq, dk, dv)
+
+
+def compare(q, k, v, dO, causal, scale, tag):
+    """fp32 outputs meet the stated tolerance element by element against the
+    plain definition.  With 16-bit outputs the backward forms D_i from the
+    stored (rounded) o, as its contract says, so the oracle is given that o;
+    the error may then exceed the tolerance by at most the rounding of the
+    exact value to the output type, half an ulp."""
+    announce(f"bwd {tag} shape={tuple(q.shape)} {q.dtype} causal={causal} scale={scale}")
+    _, _, rq, rk, rv = oracle.bwd(f64(q), f64(k), f64(v), f64(dO), s32(scale), causal)
+    tol = TOL[q.dtype]
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, dO, causal, scale, out_dtype=torch.float32)
+    report(f"{tag} dq(fp32 out)", f64(dq), rq, tol)
+    report(f"{tag} dk(fp32 out)", f64(dk), rk, tol)
+    report(f"{tag} dv(fp32 out)", f64(dv), rv, tol)
+    hq, hk, hv, ho = gpu_fwd_bwd(q, k, v, dO, causal, scale, keep_o=True)
+    _, _, sq, sk, sv = oracle.bwd(f64(q), f64(k), f64(v), f64(dO), s32(scale), causal, o_in=f64(ho))
+    report_rounded(f"{tag} dq", f64(hq), sq, tol, q.dtype)
+    report_rounded(f"{tag} dk", f64(hk), sk, tol, q.dtype)
+    report_rounded(f"{tag} dv", f64(hv), sv, tol, q.dtype)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 129, 200, 256])
+def test_small_shapes(dtype, d, causal, N):
+    seed = 2000 + N + d + (7 if causal else 0)
+    q, k, v, dO = (randn((2, 2, N, d), dtype, seed + i) for i in range(4))
+    compare(q, k, v, dO, causal, 1 / math.sqrt(d), f"small N={N}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_several_blocks(causal):
+    q, k, v, dO = (randn((1, 2, 555, 128), torch.bfloat16, 300 + i) for i in range(4))
+    compare(q, k, v, dO, causal, 1 / math.sqrt(128), "multi-block")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_zero_and_negative_scale(scale):
+    q, k, v, dO = (randn((1, 2, 150, 64), torch.float16, 310 + i) for i in range(4))
+    for causal in (False, True):
+        compare(q, k, v, dO, causal, scale, f"scale={scale}")
+
+
+def test_single_key_closed_form():
+    """N = 1: P = 1, so dq = dk = 0 and dv = dO.  dv is exact; dq and dk are
+    scale * (dO.v - D) k with D = dO.o, two fp32 dot products of the same
+    vectors summed in different orders, so they vanish up to fp32 rounding."""
+    q, k, v, dO = (randn((3, 2, 1, 128), torch.bfloat16, 320 + i) for i in range(4))
+    announce("bwd N=1")
+    for od in (None, torch.float32):
+        dq, dk, dv = gpu_fwd_bwd(q, k, v, dO, True, 0.1, out_dtype=od)
+        assert float(dq.abs().max()) <= 1e-5 and float(dk.abs().max()) <= 1e-5
+        assert torch.equal(dv.cpu().to(torch.bfloat16), dO)
+
+
+def test_gradient_invariants():
+    """Key gradients sum to ~0 per head; value gradients sum to sum(dO)."""
+    q, k, v, dO = (randn((2, 2, 640, 128), torch.bfloat16, 330 + i) for i in range(4))
+    announce("bwd invariants")
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, dO, True, 1 / math.sqrt(128))
+    sk = dk.double().sum(dim=2).abs().max().item()
+    sv = (dv.double().sum(dim=2) - dO.to(DEV).double().sum(dim=2)).abs().max().item()
+    # bounded by 1% of the summed magnitudes (the sums cancel; rounding does not)
+    bk = 1e-2 * dk.double().abs().sum(dim=2).max().item()
+    bv = 1e-2 * dv.double().abs().sum(dim=2).max().item()
+    assert sk <= bk and sv <= bv, (sk, bk, sv, bv)
+
+
+def test_repeatable_bitwise():
+    q, k, v, dO = (randn((1, 4, 700, 128), torch.bfloat16, 340 + i) for i in range(4))
+    announce("bwd repeatability")
+    a = gpu_fwd_bwd(q, k, v, dO, True, 0.1)
+    b = gpu_fwd_bwd(q, k, v, dO, True, 0.1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_workload_full_size():
+    """The backward workload at full size; the oracle checks whole heads."""
+    w = inputs.WORKLOADS["recompute_bwd"]
+    t = inputs.make_inputs(w)
+    scale = 1 / math.sqrt(w.d)
+    announce(f"bwd workload {w.describe()}")
+    BH = w.B * w.H
+    heads = [0, 37, 90, BH - 1]
+    sel = lambda x: f64(x.reshape(BH, w.N, w.d)[heads])  # noqa: E731
+    _, _, rq, rk, rv = oracle.bwd(sel(t["q"]), sel(t["k"]), sel(t["v"]), sel(t["dO"]),
+                                  s32(scale), w.causal)
+    tol = TOL[w.torch_dtype]
+    dq, dk, dv = gpu_fwd_bwd(t["q"], t["k"], t["v"], t["dO"], w.causal, scale,
+                             out_dtype=torch.float32)
+    for g in (dq, dk, dv):
+        assert bool(torch.isfinite(g).all())
+    report("full dq(fp32 out)", sel(dq), rq, tol)
+    report("full dk(fp32 out)", sel(dk), rk, tol)
+    report("full dv(fp32 out)", sel(dv), rv, tol)
+    del dq, dk, dv
+    hq, hk, hv, ho = gpu_fwd_bwd(t["q"], t["k"], t["v"], t["dO"], w.causal, scale, keep_o=True)
+    _, _, sq, sk, sv = oracle.bwd(sel(t["q"]), sel(t["k"]), sel(t["v"]), sel(t["dO"]),
+                                  s32(scale), w.causal, o_in=sel(ho))
+    report_rounded("full dq", sel(hq), sq, tol, w.torch_dtype)
+    report_rounded("full dk", sel(hk), sk, tol, w.torch_dtype)
+    report_rounded("full dv", sel(hv), sv, tol, w.torch_dtype)

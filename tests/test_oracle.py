@@ -273,6 +273,26 @@ def test_backward_invariants(causal):
     np.testing.assert_array_equal(lse, lse_f)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_with_stored_output(causal):
+    """Given the exact forward output, D_i = dO_i . o_i equals
+    sum_j P_ij dP_ij, so the gradients do not change; given a perturbed o,
+    dv (which does not involve D) is unchanged and dq moves by exactly
+    -scale * dD_i * sum_j P_ij k_j."""
+    shape = (2, 2, 30, 8)
+    q, k, v, dO = (rand(shape, s) for s in (60, 61, 62, 63))
+    o, lse, dq, dk, dv = oracle.bwd(q, k, v, dO, 0.5, causal)
+    _, _, dq2, dk2, dv2 = oracle.bwd(q, k, v, dO, 0.5, causal, o_in=o)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert np.abs(a - b).max() <= 1e-13
+    eps = rand(shape, 64) * 1e-3
+    _, _, dq3, dk3, dv3 = oracle.bwd(q, k, v, dO, 0.5, causal, o_in=o + eps)
+    np.testing.assert_array_equal(dv3, dv)
+    dD = np.sum(dO * eps, axis=-1)                       # change of D_i
+    _, _, p = brute.fwd(q, k, v, 0.5, causal)
+    np.testing.assert_allclose(dq3 - dq, -0.5 * dD[..., None] * (p @ k), rtol=0, atol=1e-12)
+
+
 def test_backward_single_key():
     """N = 1: P = 1 so dq = dk = 0 and dv = dO."""
     q, k, v, dO = (rand((3, 1, 8), s) for s in (44, 45, 46, 47))
