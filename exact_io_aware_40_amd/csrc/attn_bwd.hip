@@ -57,6 +57,27 @@ __device__ __forceinline__ typename Elem<T>::v8 pack8(const f32x16& x, int q) {
     return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Residual of pack8: x - (float)hi, rounded to T.  Used when T is fp16 to
+// carry dS into the dQ and dK products as hi + lo, which keeps the rounding
+// of dS to the operand type (relative 2^-11) out of those gradients; bf16
+// operands keep the single rounding (their tolerance is 7.5x wider).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::v8 pack8_lo(const f32x16& x, int q,
+                                                        typename Elem<T>::v8 hi) {
+    f32x4 lo, hi4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = x[8 * q + e] - (float)hi[e];
+        hi4[e] = x[8 * q + 4 + e] - (float)hi[4 + e];
+    }
+    auto l4 = Elem<T>::cvt4(lo);
+    auto h4 = Elem<T>::cvt4(hi4);
+    return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <typename T> struct SplitDS { static constexpr bool value = false; };
+template <> struct SplitDS<_Float16> { static constexpr bool value = true; };
+
 // Store a 32-row x D accumulator set in "lane = row, 16 columns per block"
 // layout (the C layout of a product whose n index is the row), times f.
 template <typename TO, int D>
@@ -197,7 +218,8 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
         nb = min(nb, (N - j0 + 31) / 32);
         const bool need_mask = (j0 + BKT > N) || (CAUSAL && j0 + BKT - 1 > qlo);
 
-        v8 dsb[KB][2];
+        constexpr bool SPLIT = SplitDS<T>::value;
+        v8 dsb[KB][2], dsl[KB][2];
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
             if (b < nb) {
@@ -230,6 +252,10 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
                 }
                 dsb[b][0] = pack8<T>(s, 0);
                 dsb[b][1] = pack8<T>(s, 1);
+                if (SPLIT) {
+                    dsl[b][0] = pack8_lo<T>(s, 0, dsb[b][0]);
+                    dsl[b][1] = pack8_lo<T>(s, 1, dsb[b][1]);
+                }
             }
         }
         // dQ^T += K^T dS^T (K^T through transposing reads of the K tile)
@@ -245,7 +271,9 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
                         const int row = 32 * b + 16 * q + 4 * h + (s16 >> 2);
                         const i16x4 lo = lds_read_tr16(sK, t_off<D>(row, gcol) + within);
                         const i16x4 hi = lds_read_tr16(sK, t_off<D>(row + 8, gcol) + within);
-                        acc[cb] = Elem<T>::mma(join8<v8>(lo, hi), dsb[b][q], acc[cb]);
+                        const v8 kt = join8<v8>(lo, hi);
+                        acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
+                        if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
                     }
                 }
             }
@@ -407,8 +435,14 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
                     s[r] = pv * (dp[r] - d4[e]);   // dS
                 }
             }
+            constexpr bool SPLIT = SplitDS<T>::value;
             const v8 pb0 = pack8<T>(p, 0), pb1 = pack8<T>(p, 1);
             const v8 db0 = pack8<T>(s, 0), db1 = pack8<T>(s, 1);
+            v8 dl0 = db0, dl1 = db1;
+            if (SPLIT) {
+                dl0 = pack8_lo<T>(s, 0, db0);
+                dl1 = pack8_lo<T>(s, 1, db1);
+            }
             // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles)
 #pragma unroll
             for (int cb = 0; cb < DB; ++cb) {
@@ -422,7 +456,9 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
                     dv[cb] = Elem<T>::mma(join8<v8>(glo, ghi), q ? pb1 : pb0, dv[cb]);
                     const i16x4 qlo = lds_read_tr16(sQ, t_off<D>(row, gcol) + within);
                     const i16x4 qhi = lds_read_tr16(sQ, t_off<D>(row + 8, gcol) + within);
-                    dk[cb] = Elem<T>::mma(join8<v8>(qlo, qhi), q ? db1 : db0, dk[cb]);
+                    const v8 qt = join8<v8>(qlo, qhi);
+                    dk[cb] = Elem<T>::mma(qt, q ? db1 : db0, dk[cb]);
+                    if (SPLIT) dk[cb] = Elem<T>::mma(qt, q ? dl1 : dl0, dk[cb]);
                 }
             }
         }

@@ -35,6 +35,23 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at `base`: loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes, read at
+// byte offset `voff` of the buffer, land at lds_base + 16 l (lds_base must be
+// the same for the whole wave).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds_base, unsigned voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// direct-to-LDS copies) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Per-element-type pieces: operand vector types, the 32x32x16 product, and
 // round-to-nearest-even conversion of four floats.

@@ -4,9 +4,12 @@
 // each of its four waves owns 32 of those rows for the whole kernel and
 // writes their output once ("FlashAttention" explainer, Step 3 "Tiling":
 // one Q block stays on chip while K/V tiles stream past, and each block's
-// output is written once).  K/V tiles of BC = 64 keys are staged in LDS with
-// coalesced 16-byte loads; the next tile is fetched into registers while the
-// current one is consumed.
+// output is written once).  K/V tiles of BC = 64 keys go straight from
+// global memory into one of two LDS stages (16-byte direct-to-LDS copies,
+// coalesced, zero-filled past the end of the sequence by the buffer bounds
+// check): tile t+1 is in flight while tile t is consumed, with one barrier
+// per tile.  Two workgroups share a CU, so one wave's softmax can overlap
+// another's matrix products.
 //
 // Per tile and wave (the pages' online softmax: "13% more FLOPs, 5.7x
 // faster", sections "Softmax is the anti-tiling operation" and
@@ -32,21 +35,22 @@ constexpr int BC = 64;    // keys per K/V tile
 constexpr int NT = 256;   // threads per workgroup (4 waves)
 
 template <typename T, typename TO, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     typedef typename Elem<T>::v8 v8;
     constexpr int GR = D / 8;              // 16-byte granules per row
-    constexpr int RPP = NT / GR;           // tile rows per load pass
-    constexpr int LOADS = BC / RPP;        // load passes per tile
+    constexpr int TILE = BC * D * 2;       // bytes of one K (or V) tile
+    constexpr int LOADS = TILE / (NT * 16);  // copies per thread per tile and tensor
     constexpr int KB = BC / 32;            // 32-key blocks per tile
     constexpr int DK = D / 16;             // k-steps of the S product
     constexpr int DB = D / 32;             // 32-wide output column blocks
 
-    __shared__ __attribute__((aligned(16))) char sK[BC * D * 2];
-    __shared__ __attribute__((aligned(16))) char sV[BC * D * 2];
+    // [stage][K | V][tile]
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
 
     const int N = a.N;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
+    const int s16 = lane & 15, grp = lane >> 4;
 
     const int L = xcd_remap(blockIdx.x, a.total);
     const int bh = L / a.nqb;
@@ -55,8 +59,9 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
     const int q0 = qb * BR;
     const size_t head = (size_t)bh * N * D;
     const T* __restrict__ Qh = (const T*)a.q + head;
-    const T* __restrict__ Kh = (const T*)a.k + head;
-    const T* __restrict__ Vh = (const T*)a.v + head;
+    const unsigned head_bytes = (unsigned)N * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
 
     // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
     const int qlo = q0 + 32 * w;
@@ -73,28 +78,24 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
 
-    // global -> register staging of one K/V tile
-    const int g_col = tid % GR, g_row = tid / GR;
-    i32x4 kreg[LOADS], vreg[LOADS];
-    auto gload = [&](int j0) {
+    // Copy p of this thread fills LDS slot (p*4 + w)*64 + lane of the tile:
+    // tile row `row`, physical granule pg, which holds logical granule
+    // pg ^ key(row) of that row (the t_off placement).
+    unsigned src_off[LOADS];
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+        const int slot = (p * 4 + w) * 64 + lane;
+        const int row = slot / GR, pg = slot % GR;
+        const int g = (t_off<D>(row, pg) - row * D * 2) >> 4;   // pg ^ key(row)
+        src_off[p] = (unsigned)(row * D * 2 + g * 16);
+    }
+    auto issue = [&](int t) {
+        char* st = smem + (t & 1) * 2 * TILE;
+        const unsigned base = (unsigned)t * BC * D * 2;
 #pragma unroll
         for (int p = 0; p < LOADS; ++p) {
-            const int row = j0 + g_row + p * RPP;
-            i32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-            if (row < N) {
-                kx = *(const i32x4*)(Kh + (size_t)row * D + g_col * 8);
-                vx = *(const i32x4*)(Vh + (size_t)row * D + g_col * 8);
-            }
-            kreg[p] = kx;
-            vreg[p] = vx;
-        }
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            const int row = g_row + p * RPP;
-            *(i32x4*)(sK + t_off<D>(row, g_col)) = kreg[p];
-            *(i32x4*)(sV + t_off<D>(row, g_col)) = vreg[p];
+            dma16(krs, st + (p * 4 + w) * 1024, base + src_off[p]);
+            dma16(vrs, st + TILE + (p * 4 + w) * 1024, base + src_off[p]);
         }
     };
 
@@ -106,13 +107,15 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    gload(0);
-    sstore();
+    issue(0);
+    wait_vmem();
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * BC;
-        if (t + 1 < ntiles) gload(j0 + BC);
+        if (t + 1 < ntiles) issue(t + 1);
+        const char* sK = smem + (t & 1) * 2 * TILE;
+        const char* sV = sK + TILE;
 
         // 32-key blocks of this tile that hold any key visible to this wave
         int nb = KB;
@@ -148,17 +151,15 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
                         const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
                         const bool ok = key < N && (!CAUSAL || key <= qrow);
                         s[b][r] = ok ? s[b][r] : -INFINITY;
-                        mloc = fmaxf(mloc, s[b][r]);
                     }
                 }
             }
-        } else {
-#pragma unroll
-            for (int b = 0; b < KB; ++b)
-                if (b < nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[b][r]);
         }
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+            if (b < nb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(s[b][r], s[b][r + 1]));
         const float m_new = fmaxf(m_run, max32(mloc));
         const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
         const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run * c - mc);
@@ -200,7 +201,6 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
         // O^T += V^T P^T.  B operand chunk (b, q) holds, at k = 8h + e, the
         // probability of key 32b + 16q + 8(e/4) + 4h + e%4; the transposing
         // reads fetch V at exactly those keys.
-        const int s16 = lane & 15, grp = lane >> 4;
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb) {
             const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
@@ -219,11 +219,9 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
             }
         }
 
-        if (t + 1 < ntiles) {
-            __syncthreads();
-            sstore();
-            __syncthreads();
-        }
+        // tile t+1 has landed and every wave is done with tile t's stage
+        wait_vmem();
+        __syncthreads();
     }
 
     // epilogue: O = O^T / l, one rounding; lse = (m c + log2 l) ln 2

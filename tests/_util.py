@@ -12,9 +12,23 @@ TOL = {torch.float16: 2e-3, torch.bfloat16: 1.5e-2}
 LSE_TOL = 1e-3
 
 
+PYTEST_CONFIG = None   # set by conftest.pytest_configure
+
+
+def _emit(line: str):
+    """Write past pytest's output capture, flushed, so the line survives
+    even if the process dies in the next GPU call."""
+    capman = PYTEST_CONFIG.pluginmanager.getplugin("capturemanager") if PYTEST_CONFIG else None
+    if capman is not None:
+        with capman.global_and_fixture_disabled():
+            print(line, file=sys.stderr, flush=True)
+    else:
+        print(line, file=sys.stderr, flush=True)
+
+
 def announce(msg: str):
-    """Name the case on the real stderr before any GPU work, flushed."""
-    print(f"[case] {msg}", file=sys.__stderr__, flush=True)
+    """Name the case on the real stderr before any GPU work."""
+    _emit(f"[case] {msg}")
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
@@ -31,6 +45,7 @@ def report(name, got, ref, tol):
     err = np.abs(got - ref)
     i = np.unravel_index(np.argmax(err), err.shape) if err.size else ()
     m = float(err.max()) if err.size else 0.0
+    _emit(f"[err] {name}: max|gpu-oracle| = {m:.3e} (tol {tol:.1e})")
     assert m <= tol, (f"{name}: max|gpu-oracle| = {m:.3e} > {tol:.1e} at {i} "
                       f"(gpu {got[i]:.6f}, oracle {ref[i]:.6f})")
     return m
@@ -53,6 +68,10 @@ def report_rounded(name, got, ref, tol, dtype):
     format at the exact value (the error of rounding the exact result)."""
     allow = tol + half_ulp(ref, dtype)
     excess = np.abs(got - ref) - allow
+    if excess.size:
+        _emit(f"[err] {name}: max|gpu-oracle| = {np.abs(got - ref).max():.3e}, "
+              f"{int((np.abs(got - ref) > tol).sum())} elements beyond tol, "
+              f"max excess over tol+half-ulp {excess.max():.2e}")
     i = np.unravel_index(np.argmax(excess), excess.shape) if excess.size else ()
     assert excess.size == 0 or excess.max() <= 0, (
         f"{name}: |gpu-oracle| = {abs(got[i] - ref[i]):.3e} > tol + half-ulp = {allow[i]:.3e} "

@@ -10,6 +10,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    from tests import _util
+    _util.PYTEST_CONFIG = config
 
 
 @pytest.fixture(scope="session")
