@@ -57,6 +57,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // round-to-nearest-even conversion of four floats.
 template <typename T> struct Elem;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <> struct Elem<__bf16> {
     typedef bf16x8 v8;
     typedef bf16x4 v4;
@@ -64,6 +67,16 @@ template <> struct Elem<__bf16> {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ v4 cvt4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+    // acc + x[0] + ... + x[7] of an 8-element operand (fp32 accumulation)
+    static __device__ __forceinline__ float sum8(v8 x, float acc) {
+        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x2 pr = {x[2 * i], x[2 * i + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+        }
+        return acc;
+    }
 };
 
 template <> struct Elem<_Float16> {
@@ -73,6 +86,15 @@ template <> struct Elem<_Float16> {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ v4 cvt4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+    static __device__ __forceinline__ float sum8(v8 x, float acc) {
+        const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2 pr = {x[2 * i], x[2 * i + 1]};
+            acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+        }
+        return acc;
+    }
 };
 
 template <typename V, typename U> __device__ __forceinline__ V bit_cast(U u) {
@@ -116,14 +138,27 @@ __device__ __forceinline__ V8 join8(i16x4 a, i16x4 b) {
 }
 
 // LDS placement of 16-byte granule g of row r in a [rows][D] tile of 16-bit
-// elements.  Tiles are read two ways: 16-byte reads of 8 consecutive rows at
+// elements.  Tiles are read two ways: 16-byte reads of consecutive rows at
 // one granule column (operands whose k index runs along d), and transposing
-// 8-byte reads of 4 aligned consecutive rows by 2 adjacent granules
-// (operands whose k index runs along the rows).  The XOR key's low three
-// bits differ across any 8 consecutive rows and its bits 1-2 differ across
-// any 4 aligned rows, so neither pattern piles onto one bank group.
+// 8-byte reads of 4 aligned consecutive rows by 2-4 adjacent granules
+// (operands whose k index runs along the rows).  The row's granules are
+// permuted by XOR with a key chosen so that the lanes the LDS serves
+// together (256 bytes per clock, 64 banks) touch distinct banks in both
+// patterns: for 128-byte rows two rows share a 256-byte line, so the key
+// also depends on the row's half.
+#ifndef ATTN_LDS_BANKS
+#define ATTN_LDS_BANKS 64
+#endif
+template <int D> __device__ __forceinline__ int lds_key(int r) {
+#if ATTN_LDS_BANKS == 64
+    if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+#else
+    return ((r & 3) << 1) | ((r >> 2) & 1);
+#endif
+}
 template <int D> __device__ __forceinline__ int t_off(int r, int g) {
-    return r * (D * 2) + ((g ^ (((r & 3) << 1) | ((r >> 2) & 1))) << 4);
+    return r * (D * 2) + ((g ^ lds_key<D>(r)) << 4);
 }
 
 // Output element stores: four fp32 values, rounded once to nearest even for

@@ -16,14 +16,21 @@
 // "FlashAttention's move: rescale the output, too"; explainer Step 4):
 //   S^T = K Q^T         on the matrix cores (keys x queries, fp32)
 //   mask                causal and ragged-tail tiles only
-//   m_new = max(m, rowmax S)     lanes own query rows; one cross-lane step
-//   alpha = 2^((m - m_new) c),   c = |scale| log2(e), alpha = 0 on the
-//                                first tile (empty history)
-//   P = 2^(S c - m_new c),  l = alpha l + rowsum P
+//   m_t = rowmax S               lanes own query rows; one cross-lane step
+//   reference mc: the scaled running maximum, moved to m_t c only when
+//                 that exceeds it by more than kTau binades (the first
+//                 tile always moves it); alpha = 2^(mc_old - mc_new)
+//   P = 2^(S c - mc),  c = |scale| log2(e);  l = alpha l + rowsum P
 //   O^T = alpha O^T + V^T P^T    V^T read from the row-major tile with
 //                                transposing LDS reads
-// and after the last tile O = O^T / l (rounded once), lse = m scale + ln l.
+// and after the last tile O = O^T / l (rounded once), lse = (mc + log2 l) ln 2.
+// Any reference point gives the same O and lse (2^(x - m) = 2^(x - m')
+// 2^(m' - m), the identity behind the pages' rescale); keeping it within
+// kTau binades of the true maximum bounds P by 2^kTau, so nothing overflows,
+// and lets most tiles skip the rescale of the accumulator.
 // S and P exist only in registers; nothing of size N x N touches memory.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -33,12 +40,18 @@ namespace {
 constexpr int BR = 128;   // query rows per workgroup
 constexpr int BC = 64;    // keys per K/V tile
 constexpr int NT = 256;   // threads per workgroup (4 waves)
+// The exponent's reference point moves only when a row's maximum rises by
+// more than kTau binades, so P <= 2^kTau and most tiles skip the rescale.
+constexpr float kTau = 8.f;
+
+template <int V> using IC = std::integral_constant<int, V>;
 
 template <typename T, typename TO, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     typedef typename Elem<T>::v8 v8;
+    constexpr int ROWB = D * 2;            // bytes per tile row
     constexpr int GR = D / 8;              // 16-byte granules per row
-    constexpr int TILE = BC * D * 2;       // bytes of one K (or V) tile
+    constexpr int TILE = BC * ROWB;        // bytes of one K (or V) tile
     constexpr int LOADS = TILE / (NT * 16);  // copies per thread per tile and tensor
     constexpr int KB = BC / 32;            // 32-key blocks per tile
     constexpr int DK = D / 16;             // k-steps of the S product
@@ -59,7 +72,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int q0 = qb * BR;
     const size_t head = (size_t)bh * N * D;
     const T* __restrict__ Qh = (const T*)a.q + head;
-    const unsigned head_bytes = (unsigned)N * D * 2;
+    const unsigned head_bytes = (unsigned)N * ROWB;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
 
@@ -86,12 +99,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     for (int p = 0; p < LOADS; ++p) {
         const int slot = (p * 4 + w) * 64 + lane;
         const int row = slot / GR, pg = slot % GR;
-        const int g = (t_off<D>(row, pg) - row * D * 2) >> 4;   // pg ^ key(row)
-        src_off[p] = (unsigned)(row * D * 2 + g * 16);
+        src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
     }
-    auto issue = [&](int t) {
-        char* st = smem + (t & 1) * 2 * TILE;
-        const unsigned base = (unsigned)t * BC * D * 2;
+    auto issue = [&](auto stg, int t) {
+        char* st = smem + decltype(stg)::value * 2 * TILE;
+        const unsigned base = (unsigned)t * TILE;
 #pragma unroll
         for (int p = 0; p < LOADS; ++p) {
             dma16(krs, st + (p * 4 + w) * 1024, base + src_off[p]);
@@ -99,99 +111,117 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         }
     };
 
+    // Loop-invariant LDS offsets of this lane's operand reads; the block,
+    // half-tile and stage parts are added as immediates (the swizzle key
+    // depends on the row modulo 16 only).
+    int koff[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) koff[kk] = t_off<D>(l32, 2 * kk + h);
+    int voff[2][DB];
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+        const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+        const int r0 = 4 * h + (s16 >> 2);
+        voff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
+        voff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+    }
+
     const float c = a.c;
     f32x16 oacc[DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float mc_run = -INFINITY;   // exponent reference (scaled units) of this row
+    // this lane's share of the row's normaliser, twice: the sum of P as
+    // rounded for the P.V product (it normalises O, so O's weights sum to
+    // one exactly as used) and the fp32 sum of P (it gives lse)
+    float l_run = 0.f, lf_run = 0.f;
 
-    issue(0);
-    wait_vmem();
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * BC;
-        if (t + 1 < ntiles) issue(t + 1);
-        const char* sK = smem + (t & 1) * 2 * TILE;
+    // One K/V tile for this wave's 32 rows.  MASK: causal diagonal or the
+    // ragged last tile; otherwise every key of the tile is visible.
+    auto tile = [&](auto stg, auto mask, int j0) {
+        constexpr int STG = decltype(stg)::value;
+        constexpr bool MASK = decltype(mask)::value;
+        const char* sK = smem + STG * 2 * TILE;
         const char* sV = sK + TILE;
 
-        // 32-key blocks of this tile that hold any key visible to this wave
-        int nb = KB;
-        if (CAUSAL) {
-            const int lim = qlo + 31 - j0;  // last visible key offset in the tile
-            nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
+        int nb = KB;  // 32-key blocks holding any key visible to this wave
+        if (MASK) {
+            if (CAUSAL) {
+                const int lim = qlo + 31 - j0;
+                nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
+            }
+            nb = min(nb, (N - j0 + 31) / 32);
         }
-        nb = min(nb, (N - j0 + 31) / 32);
 
+        // S^T = K Q^T
         f32x16 s[KB];
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
+            if (MASK && b >= nb) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
-            if (b < nb) {
-                const int krow = 32 * b + l32;
-#pragma unroll
-                for (int kk = 0; kk < DK; ++kk) {
-                    const i32x4 kx = *(const i32x4*)(sK + t_off<D>(krow, 2 * kk + h));
-                    s[b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), s[b]);
-                }
+            for (int kk = 0; kk < DK; ++kk) {
+                const i32x4 kx = *(const i32x4*)(sK + koff[kk] + 32 * b * ROWB);
+                const f32x16 acc = kk == 0 ? f32x16{} : s[b];
+                s[b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), acc);
             }
         }
-
-        const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
-        float mloc = -INFINITY;
-        if (need_mask) {
+        if (MASK) {
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                if (b < nb) {
+                if (b >= nb) continue;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool ok = key < N && (!CAUSAL || key <= qrow);
-                        s[b][r] = ok ? s[b][r] : -INFINITY;
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool ok = key < N && (!CAUSAL || key <= qrow);
+                    s[b][r] = ok ? s[b][r] : -INFINITY;
                 }
             }
         }
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-            if (b < nb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(s[b][r], s[b][r + 1]));
-        const float m_new = fmaxf(m_run, max32(mloc));
-        const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run * c - mc);
 
-        float lsum = 0.f;
-        v8 pb[KB][2];
+        // row maximum of the tile; move the reference only past kTau
+        float mt = -INFINITY;
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-            if (b < nb) {
+            if (MASK && b >= nb) continue;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    // a masked score is -inf; its exponent is forced to -inf so
-                    // that a zero scale cannot turn it into NaN
-                    float e = fmaf(s[b][r], c, -mc);
-                    if (need_mask) e = (s[b][r] == -INFINITY) ? -INFINITY : e;
-                    const float p = fast_exp2(e);
-                    s[b][r] = p;
-                    lsum += p;
-                }
+            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[b][r], s[b][r + 1]));
+        }
+        mt = max32(mt);
+        const float tc = (mt == -INFINITY) ? -INFINITY : mt * c;
+        const bool upd = tc > mc_run + kTau;
+        const float mc = upd ? tc : mc_run;
+        const float alpha = upd ? fast_exp2(mc_run - mc) : 1.f;
+        mc_run = mc;
+
+        // P = 2^(S c - mc), packed to the operand type
+        v8 pb[KB][2];
+        float lsum = 0.f, lfsum = 0.f;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    f32x4 lo = {s[b][8 * q + 0], s[b][8 * q + 1], s[b][8 * q + 2], s[b][8 * q + 3]};
-                    f32x4 hi = {s[b][8 * q + 4], s[b][8 * q + 5], s[b][8 * q + 6], s[b][8 * q + 7]};
-                    auto l4 = Elem<T>::cvt4(lo);
-                    auto h4 = Elem<T>::cvt4(hi);
-                    pb[b][q] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
+        for (int b = 0; b < KB; ++b) {
+            if (MASK && b >= nb) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float e = fmaf(s[b][r], c, -mc);
+                // a masked score's exponent is -inf even when c == 0
+                if (MASK) e = (s[b][r] == -INFINITY) ? -INFINITY : e;
+                s[b][r] = fast_exp2(e);
+                lfsum += s[b][r];
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const f32x4 lo = {s[b][8 * q + 0], s[b][8 * q + 1], s[b][8 * q + 2], s[b][8 * q + 3]};
+                const f32x4 hi = {s[b][8 * q + 4], s[b][8 * q + 5], s[b][8 * q + 6], s[b][8 * q + 7]};
+                const auto l4 = Elem<T>::cvt4(lo);
+                const auto h4 = Elem<T>::cvt4(hi);
+                pb[b][q] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+                lsum = Elem<T>::sum8(pb[b][q], lsum);
             }
         }
         l_run = alpha * l_run + lsum;
-        m_run = m_new;
-        if (!__all(alpha == 1.f)) {
+        lf_run = alpha * lf_run + lfsum;
+        if (__ballot(upd) != 0) [[unlikely]] {
 #pragma unroll
             for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
@@ -203,29 +233,48 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         // reads fetch V at exactly those keys.
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb) {
-            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-            const int gcol = col >> 3, within = (col & 7) * 2;
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                if (b < nb) {
+                if (MASK && b >= nb) continue;
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int row = 32 * b + 16 * q + 4 * h + (s16 >> 2);
-                        const i16x4 lo = lds_read_tr16(sV, t_off<D>(row, gcol) + within);
-                        const i16x4 hi = lds_read_tr16(sV, t_off<D>(row + 8, gcol) + within);
-                        oacc[cb] = Elem<T>::mma(join8<v8>(lo, hi), pb[b][q], oacc[cb]);
-                    }
+                for (int q = 0; q < 2; ++q) {
+                    const int roff = (32 * b + 16 * q) * ROWB;
+                    const i16x4 lo = lds_read_tr16(sV, voff[0][cb] + roff);
+                    const i16x4 hi = lds_read_tr16(sV, voff[1][cb] + roff);
+                    oacc[cb] = Elem<T>::mma(join8<v8>(lo, hi), pb[b][q], oacc[cb]);
                 }
             }
         }
+    };
 
-        // tile t+1 has landed and every wave is done with tile t's stage
+    // One pipeline step: start the copy of tile t+1 into the other stage,
+    // consume tile t, then wait for the copy and for every wave.
+    auto step = [&](auto stg, int t) {
+        constexpr int STG = decltype(stg)::value;
+        if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
+        const int j0 = t * BC;
+        const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
+        if (need_mask)
+            tile(stg, std::true_type{}, j0);
+        else
+            tile(stg, std::false_type{}, j0);
         wait_vmem();
         __syncthreads();
-    }
+    };
 
-    // epilogue: O = O^T / l, one rounding; lse = (m c + log2 l) ln 2
+    issue(IC<0>{}, 0);
+    wait_vmem();
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(IC<0>{}, t);
+        step(IC<1>{}, t + 1);
+    }
+    if (t < ntiles) step(IC<0>{}, t);
+
+    // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
     const float l_tot = sum32(l_run);
+    const float lf_tot = sum32(lf_run);
     const float inv = fast_rcp(l_tot);
     if (qrow < N) {
         TO* __restrict__ orow = (TO*)a.o + head + (size_t)qrow * D;
@@ -238,10 +287,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
                 store4<TO>(orow + 32 * cb + 8 * g + 4 * h, x);
             }
         }
-        if (h == 0) {
-            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-            a.lse[(size_t)bh * N + qrow] = (mc + fast_log2(l_tot)) * 0.69314718055994531f;
-        }
+        if (h == 0) a.lse[(size_t)bh * N + qrow] = (mc_run + fast_log2(lf_tot)) * 0.69314718055994531f;
     }
 }
 

@@ -12,17 +12,21 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-BUILD = os.path.join(ROOT, "_build", "attn")
-LIB = os.path.join(PKG, "libattn.so")
+BUILD = os.environ.get("ATTN_BUILD_DIR", os.path.join(ROOT, "_build", "attn"))
+LIB = os.environ.get("ATTN_LIB_OUT", os.path.join(PKG, "libattn.so"))
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# The kernels never create NaN (masked scores are -inf, and every exponent
+# is finite or -inf), so max/min need no NaN canonicalisation: that lets
+# the row maximum use v_max3 directly.  Infinities are still honoured.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-I", os.path.join(ROOT, "include"), "-I", HERE,
     "-Wall", "-Wno-unused-function",
-]
+] + os.environ.get("ATTN_EXTRA_FLAGS", "").split()
 
 
 def _compile(src: str, verbose: bool) -> str:
