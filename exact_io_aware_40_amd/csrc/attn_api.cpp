@@ -151,7 +151,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.delta = static_cast<float*>(workspace);
+    a.ws = static_cast<float*>(workspace);
     a.N = int(N);
     if (BH > 0x7fffffff / ((N + 63) / 64)) return ATTN_ERR_SHAPE;
     a.BH = int(BH);

@@ -12,9 +12,15 @@
 // Two kernels, both deterministic (every output element is owned by one
 // lane of one wave, no atomics):
 //   dq_kernel   one workgroup per 128 query rows; streams K/V tiles.  It
-//               also computes D_i for its rows and stores it in the
+//               also stores D_i and lse_i log2(e) of its rows in the
 //               workspace for the second kernel.
-//   dkdv_kernel one workgroup per 128 keys; streams Q/dO tiles.
+//   dkdv_kernel one workgroup per 128 keys; streams Q/dO tiles together
+//               with their D and lse values.
+// Tiles move global -> LDS with 16-byte direct copies into two stages
+// (one barrier per tile); loads past the end of the sequence read zeros,
+// which makes such rows contribute nothing (their dO, Q, lse and D are 0).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -26,7 +32,12 @@ constexpr int BQ = 128;         // dq_kernel: query rows per workgroup
 constexpr int BKT = 64;         // dq_kernel: keys per K/V tile
 constexpr int BK = 128;         // dkdv_kernel: keys per workgroup
 constexpr int BQT = 64;         // dkdv_kernel: queries per Q/dO tile
+constexpr int PADR = 64;        // workspace rows per head are padded to this
 constexpr float kLog2e = 1.4426950408889634f;
+
+template <int V> using IC = std::integral_constant<int, V>;
+
+__host__ __device__ inline int padded_rows(int N) { return (N + PADR - 1) / PADR * PADR; }
 
 template <typename T> __device__ __forceinline__ float to_f32(unsigned short x);
 template <> __device__ __forceinline__ float to_f32<__bf16>(unsigned short x) {
@@ -115,19 +126,34 @@ template <typename T> struct RowDot<T, float> {
     }
 };
 
+// LDS slot source offsets for a [64][D] tile copied by 256 threads: copy p
+// of this thread fills slot (p*4 + w)*64 + lane = tile row `row`, physical
+// granule pg, which holds logical granule pg ^ key(row).
+template <int D, int LOADS>
+__device__ __forceinline__ void tile_sources(unsigned* src, int w, int lane) {
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+        const int slot = (p * 4 + w) * 64 + lane;
+        const int row = slot / (D / 8), pg = slot % (D / 8);
+        src[p] = (unsigned)(row * D * 2 + (pg ^ lds_key<D>(row)) * 16);
+    }
+}
+
 // --------------------------------------------------------------------------
-// dq_kernel
+// dq_kernel: dQ for 128 query rows; K/V tiles stream past.
+//   S^T = K Q^T, dP^T = V dO^T (keys x queries), P^T = 2^(S^T c - lse2),
+//   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 // --------------------------------------------------------------------------
 template <typename T, typename TO, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
+__global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total) {
     typedef typename Elem<T>::v8 v8;
-    constexpr int GR = D / 8, RPP = NT / GR, LOADS = BKT / RPP;
+    constexpr int ROWB = D * 2, TILE = BKT * ROWB, LOADS = TILE / (NT * 16);
     constexpr int KB = BKT / 32, DK = D / 16, DB = D / 32;
+    constexpr bool SPLIT = SplitDS<T>::value;
 
-    __shared__ __attribute__((aligned(16))) char sK[BKT * D * 2];
-    __shared__ __attribute__((aligned(16))) char sV[BKT * D * 2];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // [stage][K | V]
 
-    const int N = a.N;
+    const int N = a.N, NP = padded_rows(N);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
@@ -135,14 +161,15 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
     const int L = xcd_remap(blockIdx.x, total);
     const int bh = L / nqb;
     int qb = L - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;
+    if (CAUSAL) qb = nqb - 1 - qb;     // heaviest query blocks first
     const int q0 = qb * BQ;
     const size_t head = (size_t)bh * N * D;
     const T* __restrict__ Qh = (const T*)a.q + head;
-    const T* __restrict__ Kh = (const T*)a.k + head;
-    const T* __restrict__ Vh = (const T*)a.v + head;
-    const TO* __restrict__ Oh = (const TO*)a.o + head;
     const T* __restrict__ Gh = (const T*)a.dO + head;
+    const TO* __restrict__ Oh = (const TO*)a.o + head;
+    const unsigned head_bytes = (unsigned)N * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
 
     const int qlo = q0 + 32 * w;
     const int qrow = qlo + l32;
@@ -166,34 +193,38 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
     }
     const float delta = sum32(dpart);
     const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
-    if (live && h == 0) a.delta[(size_t)bh * N + qrow] = delta;
+    if (live && h == 0) {
+        a.ws[(size_t)bh * NP + qrow] = delta;
+        a.ws[((size_t)a.BH + bh) * NP + qrow] = lse2;
+    }
 
     const int kend = CAUSAL ? min(N, q0 + BQ) : N;
     const int ntiles = (kend + BKT - 1) / BKT;
 
-    const int g_col = tid % GR, g_row = tid / GR;
-    i32x4 kreg[LOADS], vreg[LOADS];
-    auto gload = [&](int j0) {
+    unsigned src_off[LOADS];
+    tile_sources<D, LOADS>(src_off, w, lane);
+    auto issue = [&](auto stg, int t) {
+        char* st = smem + decltype(stg)::value * 2 * TILE;
+        const unsigned base = (unsigned)t * TILE;
 #pragma unroll
         for (int p = 0; p < LOADS; ++p) {
-            const int row = j0 + g_row + p * RPP;
-            i32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-            if (row < N) {
-                kx = *(const i32x4*)(Kh + (size_t)row * D + g_col * 8);
-                vx = *(const i32x4*)(Vh + (size_t)row * D + g_col * 8);
-            }
-            kreg[p] = kx;
-            vreg[p] = vx;
+            dma16(krs, st + (p * 4 + w) * 1024, base + src_off[p]);
+            dma16(vrs, st + TILE + (p * 4 + w) * 1024, base + src_off[p]);
         }
     };
-    auto sstore = [&]() {
+
+    // K and V rows as A operands (16-byte reads), K^T through transposing reads
+    int roff[DK];
 #pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            const int row = g_row + p * RPP;
-            *(i32x4*)(sK + t_off<D>(row, g_col)) = kreg[p];
-            *(i32x4*)(sV + t_off<D>(row, g_col)) = vreg[p];
-        }
-    };
+    for (int kk = 0; kk < DK; ++kk) roff[kk] = t_off<D>(l32, 2 * kk + h);
+    int toff[2][DB];
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+        const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+        const int r0 = 4 * h + (s16 >> 2);
+        toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
+        toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+    }
 
     const float c = a.c;
     f32x16 acc[DB];
@@ -202,106 +233,111 @@ __global__ __launch_bounds__(NT) void dq_kernel(BwdArgs a, int nqb, int total) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
 
-    gload(0);
-    sstore();
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * BKT;
-        if (t + 1 < ntiles) gload(j0 + BKT);
-
+    auto tile = [&](auto stg, auto mask, int j0) {
+        constexpr int STG = decltype(stg)::value;
+        constexpr bool MASK = decltype(mask)::value;
+        const char* sK = smem + STG * 2 * TILE;
+        const char* sV = sK + TILE;
         int nb = KB;
-        if (CAUSAL) {
-            const int lim = qlo + 31 - j0;
-            nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
+        if (MASK) {
+            if (CAUSAL) {
+                const int lim = qlo + 31 - j0;
+                nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
+            }
+            nb = min(nb, (N - j0 + 31) / 32);
         }
-        nb = min(nb, (N - j0 + 31) / 32);
-        const bool need_mask = (j0 + BKT > N) || (CAUSAL && j0 + BKT - 1 > qlo);
-
-        constexpr bool SPLIT = SplitDS<T>::value;
         v8 dsb[KB][2], dsl[KB][2];
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-            if (b < nb) {
-                f32x16 s, dp;
+            if (MASK && b >= nb) continue;
+            f32x16 s, dp;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[r] = 0.f;
-                    dp[r] = 0.f;
-                }
-                const int krow = 32 * b + l32;
+            for (int kk = 0; kk < DK; ++kk) {
+                const i32x4 kx = *(const i32x4*)(sK + roff[kk] + 32 * b * ROWB);
+                s = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
+            }
 #pragma unroll
-                for (int kk = 0; kk < DK; ++kk) {
-                    const i32x4 kx = *(const i32x4*)(sK + t_off<D>(krow, 2 * kk + h));
-                    s = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), s);
-                }
+            for (int kk = 0; kk < DK; ++kk) {
+                const i32x4 vx = *(const i32x4*)(sV + roff[kk] + 32 * b * ROWB);
+                dp = Elem<T>::mma(bit_cast<v8>(vx), bit_cast<v8>(gf[kk]), kk == 0 ? f32x16{} : dp);
+            }
 #pragma unroll
-                for (int kk = 0; kk < DK; ++kk) {
-                    const i32x4 vx = *(const i32x4*)(sV + t_off<D>(krow, 2 * kk + h));
-                    dp = Elem<T>::mma(bit_cast<v8>(vx), bit_cast<v8>(gf[kk]), dp);
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(s[r], c, -lse2));
+                if (MASK) {
+                    const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool ok = key < N && (!CAUSAL || key <= qrow);
+                    p = ok ? p : 0.f;
                 }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[r], c, -lse2));
-                    if (need_mask) {
-                        const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool ok = key < N && (!CAUSAL || key <= qrow);
-                        p = ok ? p : 0.f;
-                    }
-                    s[r] = p * (dp[r] - delta);
-                }
-                dsb[b][0] = pack8<T>(s, 0);
-                dsb[b][1] = pack8<T>(s, 1);
-                if (SPLIT) {
-                    dsl[b][0] = pack8_lo<T>(s, 0, dsb[b][0]);
-                    dsl[b][1] = pack8_lo<T>(s, 1, dsb[b][1]);
-                }
+                s[r] = p * (dp[r] - delta);
+            }
+            dsb[b][0] = pack8<T>(s, 0);
+            dsb[b][1] = pack8<T>(s, 1);
+            if (SPLIT) {
+                dsl[b][0] = pack8_lo<T>(s, 0, dsb[b][0]);
+                dsl[b][1] = pack8_lo<T>(s, 1, dsb[b][1]);
             }
         }
-        // dQ^T += K^T dS^T (K^T through transposing reads of the K tile)
+        // dQ^T += K^T dS^T
 #pragma unroll
         for (int cb = 0; cb < DB; ++cb) {
-            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-            const int gcol = col >> 3, within = (col & 7) * 2;
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                if (b < nb) {
+                if (MASK && b >= nb) continue;
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int row = 32 * b + 16 * q + 4 * h + (s16 >> 2);
-                        const i16x4 lo = lds_read_tr16(sK, t_off<D>(row, gcol) + within);
-                        const i16x4 hi = lds_read_tr16(sK, t_off<D>(row + 8, gcol) + within);
-                        const v8 kt = join8<v8>(lo, hi);
-                        acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
-                        if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
-                    }
+                for (int q = 0; q < 2; ++q) {
+                    const int ro = (32 * b + 16 * q) * ROWB;
+                    const v8 kt = join8<v8>(lds_read_tr16(sK, toff[0][cb] + ro),
+                                            lds_read_tr16(sK, toff[1][cb] + ro));
+                    acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
+                    if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
                 }
             }
         }
-        if (t + 1 < ntiles) {
-            __syncthreads();
-            sstore();
-            __syncthreads();
-        }
+    };
+
+    auto step = [&](auto stg, int t) {
+        constexpr int STG = decltype(stg)::value;
+        if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
+        const int j0 = t * BKT;
+        const bool need_mask = (j0 + BKT > N) || (CAUSAL && j0 + BKT - 1 > qlo);
+        if (need_mask)
+            tile(stg, std::true_type{}, j0);
+        else
+            tile(stg, std::false_type{}, j0);
+        wait_vmem();
+        __syncthreads();
+    };
+
+    issue(IC<0>{}, 0);
+    wait_vmem();
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(IC<0>{}, t);
+        step(IC<1>{}, t + 1);
     }
+    if (t < ntiles) step(IC<0>{}, t);
+
     if (live) store_rows<TO, D>((TO*)a.dq + head + (size_t)qrow * D, acc, a.scale, h);
 }
 
 // --------------------------------------------------------------------------
-// dkdv_kernel
+// dkdv_kernel: dK, dV for 128 keys (32 per wave); Q/dO tiles stream past.
+//   S = Q K^T, dP = dO V^T (queries x keys), P = 2^(S c - lse2),
+//   dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
 // --------------------------------------------------------------------------
 template <typename T, typename TO, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total) {
     typedef typename Elem<T>::v8 v8;
-    constexpr int GR = D / 8, RPP = NT / GR, LOADS = BQT / RPP;
+    constexpr int ROWB = D * 2, TILE = BQT * ROWB, LOADS = TILE / (NT * 16);
     constexpr int QB = BQT / 32, DK = D / 16, DB = D / 32;
+    constexpr int STAGE = 2 * TILE + 2 * BQT * 4;   // Q tile, dO tile, lse2, D
+    constexpr bool SPLIT = SplitDS<T>::value;
 
-    __shared__ __attribute__((aligned(16))) char sQ[BQT * D * 2];
-    __shared__ __attribute__((aligned(16))) char sG[BQT * D * 2];
-    __shared__ __attribute__((aligned(16))) float sL[BQT];
-    __shared__ __attribute__((aligned(16))) float sD[BQT];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-    const int N = a.N;
+    const int N = a.N, NP = padded_rows(N);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
@@ -311,12 +347,13 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
     const int kblk = L - bh * nkb;     // ascending: most queries first under the mask
     const int kb0 = kblk * BK;
     const size_t head = (size_t)bh * N * D;
-    const T* __restrict__ Qh = (const T*)a.q + head;
     const T* __restrict__ Kh = (const T*)a.k + head;
     const T* __restrict__ Vh = (const T*)a.v + head;
-    const T* __restrict__ Gh = (const T*)a.dO + head;
-    const float* __restrict__ lse_h = a.lse + (size_t)bh * N;
-    const float* __restrict__ dl_h = a.delta + (size_t)bh * N;
+    const unsigned head_bytes = (unsigned)N * ROWB;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const T*)a.q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc((const T*)a.dO + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.ws + (size_t)bh * NP, (unsigned)N * 4);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.ws + ((size_t)a.BH + bh) * NP, (unsigned)N * 4);
 
     const int kw0 = kb0 + 32 * w;       // this wave's first key
     const int key = kw0 + l32;          // this lane's key
@@ -340,40 +377,36 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
     const int t0 = CAUSAL ? kb0 / BQT : 0;
     const int ntiles = (N + BQT - 1) / BQT;
 
-    const int g_col = tid % GR, g_row = tid / GR;
-    i32x4 qreg[LOADS], greg[LOADS];
-    float lreg = 0.f, dreg = 0.f;
-    auto gload = [&](int i0) {
+    unsigned src_off[LOADS];
+    tile_sources<D, LOADS>(src_off, w, lane);
+    auto issue = [&](auto stg, int t) {
+        char* st = smem + decltype(stg)::value * STAGE;
+        const unsigned base = (unsigned)t * TILE;
 #pragma unroll
         for (int p = 0; p < LOADS; ++p) {
-            const int row = i0 + g_row + p * RPP;
-            i32x4 qx = {0, 0, 0, 0}, gx = {0, 0, 0, 0};
-            if (row < N) {
-                qx = *(const i32x4*)(Qh + (size_t)row * D + g_col * 8);
-                gx = *(const i32x4*)(Gh + (size_t)row * D + g_col * 8);
-            }
-            qreg[p] = qx;
-            greg[p] = gx;
+            dma16(qrs, st + (p * 4 + w) * 1024, base + src_off[p]);
+            dma16(grs, st + TILE + (p * 4 + w) * 1024, base + src_off[p]);
         }
-        if (tid < BQT) {
-            const int row = i0 + tid;
-            // rows past the end get lse = +inf, so their P is exactly 0
-            lreg = row < N ? lse_h[row] * kLog2e : INFINITY;
-            dreg = row < N ? dl_h[row] : 0.f;
+        // the tile's lse2 and D values: 64 floats each, 16 lanes of wave 0
+        if (w == 0 && lane < BQT / 4) {
+            const unsigned fo = (unsigned)(t * BQT + 4 * lane) * 4;
+            dma16(lrs, st + 2 * TILE, fo);
+            dma16(drs, st + 2 * TILE + BQT * 4, fo);
         }
     };
-    auto sstore = [&]() {
+
+    // Q and dO rows as A operands (16-byte reads) and through transposing reads
+    int roff[DK];
 #pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            const int row = g_row + p * RPP;
-            *(i32x4*)(sQ + t_off<D>(row, g_col)) = qreg[p];
-            *(i32x4*)(sG + t_off<D>(row, g_col)) = greg[p];
-        }
-        if (tid < BQT) {
-            sL[tid] = lreg;
-            sD[tid] = dreg;
-        }
-    };
+    for (int kk = 0; kk < DK; ++kk) roff[kk] = t_off<D>(l32, 2 * kk + h);
+    int toff[2][DB];
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+        const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+        const int r0 = 4 * h + (s16 >> 2);
+        toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
+        toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+    }
 
     const float c = a.c;
     f32x16 dk[DB], dv[DB];
@@ -385,89 +418,95 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
             dv[cb][r] = 0.f;
         }
 
-    if (t0 < ntiles) {
-        gload(t0 * BQT);
-        sstore();
-    }
-    __syncthreads();
+    // One 32-query block of a staged tile.  MASK: the block straddles the
+    // causal diagonal of this wave's keys.
+    auto block = [&](auto stg, auto mask, int qb, int i0) {
+        constexpr int STG = decltype(stg)::value;
+        constexpr bool MASK = decltype(mask)::value;
+        const char* sQ = smem + STG * STAGE;
+        const char* sG = sQ + TILE;
+        const float* sL = (const float*)(sQ + 2 * TILE);
+        const float* sD = sL + BQT;
+        const int qo = 32 * qb * ROWB;
+        f32x16 s, dp;
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            const i32x4 qx = *(const i32x4*)(sQ + roff[kk] + qo);
+            s = Elem<T>::mma(bit_cast<v8>(qx), bit_cast<v8>(kf[kk]), kk == 0 ? f32x16{} : s);
+        }
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            const i32x4 gx = *(const i32x4*)(sG + roff[kk] + qo);
+            dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vf[kk]), kk == 0 ? f32x16{} : dp);
+        }
+        // rows of this block held by the lane: 32qb + 8(r/4) + 4h + r%4
+        f32x16 p;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int li = 32 * qb + 8 * rr + 4 * h;
+            const f32x4 l4 = *(const f32x4*)(sL + li);
+            const f32x4 d4 = *(const f32x4*)(sD + li);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rr + e;
+                float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
+                if (MASK) pv = (key <= i0 + li + e) ? pv : 0.f;
+                p[r] = pv;
+                s[r] = pv * (dp[r] - d4[e]);   // dS
+            }
+        }
+        const v8 pb0 = pack8<T>(p, 0), pb1 = pack8<T>(p, 1);
+        const v8 db0 = pack8<T>(s, 0), db1 = pack8<T>(s, 1);
+        v8 dl0 = db0, dl1 = db1;
+        if (SPLIT) {
+            dl0 = pack8_lo<T>(s, 0, db0);
+            dl1 = pack8_lo<T>(s, 1, db1);
+        }
+        // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles)
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int ro = (32 * qb + 16 * q) * ROWB;
+                const v8 gt = join8<v8>(lds_read_tr16(sG, toff[0][cb] + ro),
+                                        lds_read_tr16(sG, toff[1][cb] + ro));
+                dv[cb] = Elem<T>::mma(gt, q ? pb1 : pb0, dv[cb]);
+                const v8 qt = join8<v8>(lds_read_tr16(sQ, toff[0][cb] + ro),
+                                        lds_read_tr16(sQ, toff[1][cb] + ro));
+                dk[cb] = Elem<T>::mma(qt, q ? db1 : db0, dk[cb]);
+                if (SPLIT) dk[cb] = Elem<T>::mma(qt, q ? dl1 : dl0, dk[cb]);
+            }
+        }
+    };
 
-    for (int t = t0; t < ntiles; ++t) {
+    auto step = [&](auto stg, int t) {
+        constexpr int STG = decltype(stg)::value;
+        if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
         const int i0 = t * BQT;
-        if (t + 1 < ntiles) gload(i0 + BQT);
-
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int ib = i0 + 32 * qb;    // first query of this 32-row block
-            // skip blocks with no query at or after any of this wave's keys
-            const bool active = ib < N && (!CAUSAL || ib + 31 >= kw0);
-            if (!active) continue;
-            f32x16 s, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[r] = 0.f;
-                dp[r] = 0.f;
-            }
-            const int qrow_l = 32 * qb + l32;
-#pragma unroll
-            for (int kk = 0; kk < DK; ++kk) {
-                const i32x4 qx = *(const i32x4*)(sQ + t_off<D>(qrow_l, 2 * kk + h));
-                s = Elem<T>::mma(bit_cast<v8>(qx), bit_cast<v8>(kf[kk]), s);
-            }
-#pragma unroll
-            for (int kk = 0; kk < DK; ++kk) {
-                const i32x4 gx = *(const i32x4*)(sG + t_off<D>(qrow_l, 2 * kk + h));
-                dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vf[kk]), dp);
-            }
-            // rows of this block held by the lane: 32qb + 8(r/4) + 4h + r%4
-            const bool need_mask = CAUSAL && ib < kw0 + 31;
-            f32x16 p;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int li = 32 * qb + 8 * rr + 4 * h;
-                const f32x4 l4 = *(const f32x4*)(sL + li);
-                const f32x4 d4 = *(const f32x4*)(sD + li);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rr + e;
-                    float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
-                    if (need_mask) pv = (key <= i0 + li + e) ? pv : 0.f;
-                    p[r] = pv;
-                    s[r] = pv * (dp[r] - d4[e]);   // dS
-                }
-            }
-            constexpr bool SPLIT = SplitDS<T>::value;
-            const v8 pb0 = pack8<T>(p, 0), pb1 = pack8<T>(p, 1);
-            const v8 db0 = pack8<T>(s, 0), db1 = pack8<T>(s, 1);
-            v8 dl0 = db0, dl1 = db1;
-            if (SPLIT) {
-                dl0 = pack8_lo<T>(s, 0, db0);
-                dl1 = pack8_lo<T>(s, 1, db1);
-            }
-            // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles)
-#pragma unroll
-            for (int cb = 0; cb < DB; ++cb) {
-                const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-                const int gcol = col >> 3, within = (col & 7) * 2;
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int row = 32 * qb + 16 * q + 4 * h + (s16 >> 2);
-                    const i16x4 glo = lds_read_tr16(sG, t_off<D>(row, gcol) + within);
-                    const i16x4 ghi = lds_read_tr16(sG, t_off<D>(row + 8, gcol) + within);
-                    dv[cb] = Elem<T>::mma(join8<v8>(glo, ghi), q ? pb1 : pb0, dv[cb]);
-                    const i16x4 qlo = lds_read_tr16(sQ, t_off<D>(row, gcol) + within);
-                    const i16x4 qhi = lds_read_tr16(sQ, t_off<D>(row + 8, gcol) + within);
-                    const v8 qt = join8<v8>(qlo, qhi);
-                    dk[cb] = Elem<T>::mma(qt, q ? db1 : db0, dk[cb]);
-                    if (SPLIT) dk[cb] = Elem<T>::mma(qt, q ? dl1 : dl0, dk[cb]);
-                }
-            }
+            const int ib = i0 + 32 * qb;   // first query of the block
+            if (ib >= N) continue;
+            if (CAUSAL && ib + 31 < kw0) continue;          // every query before every key
+            if (CAUSAL && ib < kw0 + 31)
+                block(stg, std::true_type{}, qb, i0);
+            else
+                block(stg, std::false_type{}, qb, i0);
         }
-        if (t + 1 < ntiles) {
-            __syncthreads();
-            sstore();
-            __syncthreads();
-        }
+        wait_vmem();
+        __syncthreads();
+    };
+
+    if (t0 < ntiles) issue(IC<0>{}, t0);
+    wait_vmem();
+    __syncthreads();
+    int t = t0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(IC<0>{}, t);
+        step(IC<1>{}, t + 1);
     }
+    if (t < ntiles) step(IC<0>{}, t);
+
     if (live) {
         store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale, h);
         store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, 1.f, h);
@@ -495,8 +534,7 @@ hipError_t launch_t(const BwdArgs& a, int d, int causal, hipStream_t stream) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N) {
-    const size_t bytes = size_t(BH) * size_t(N) * sizeof(float);
-    return (bytes + 255) & ~size_t(255);
+    return size_t(2) * size_t(BH) * size_t(padded_rows(int(N))) * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream) {

@@ -35,7 +35,8 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;   // workspace: D_i = dO_i . o_i, [B*H*N]
+    float* ws;      // workspace: per head, D_i = dO_i . o_i then lse_i log2(e),
+                    // each padded to NP = round_up(N, 64) floats: [2][B*H][NP]
     int N;
     int BH;
     float c;        // |scale| * log2(e)

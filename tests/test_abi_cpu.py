@@ -92,8 +92,9 @@ def test_fwd_empty_is_noop(kw):
 
 
 def test_workspace_size():
-    assert attn.attn_bwd_workspace_size(2, 3, 100, 128, 1) == 2560   # 600 floats -> 256-multiple
-    assert attn.attn_bwd_workspace_size(8, 16, 2048, 128, 1) == 8 * 16 * 2048 * 4
+    # two fp32 values per row (D and lse * log2 e), rows padded to 64 per head
+    assert attn.attn_bwd_workspace_size(2, 3, 100, 128, 1) == 2 * 6 * 128 * 4
+    assert attn.attn_bwd_workspace_size(8, 16, 2048, 128, 1) == 2 * 8 * 16 * 2048 * 4
     assert attn.attn_bwd_workspace_size(0, 3, 100, 128, 1) == 0
     assert attn.attn_bwd_workspace_size(1, 1, 100, 96, 1) == 0
     assert attn.attn_bwd_workspace_size(1, 1, 100, 64, 7) == 0
@@ -101,7 +102,7 @@ def test_workspace_size():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dO=0), E_NULL), (dict(lse=0), E_NULL), (dict(dq=0), E_NULL), (dict(dv=0), E_NULL),
-    (dict(ws=0), E_WS), (dict(wsb=2559), E_WS),
+    (dict(ws=0), E_WS), (dict(wsb=6143), E_WS),
     (dict(d=32), E_HD), (dict(dtype=5), E_DT), (dict(N=-1), E_SHAPE),
     (dict(ws=P[9] + 4), E_ALIGN), (dict(dk=P[7] + 8), E_ALIGN),
     (dict(scale=float("-inf")), E_SCALE), (dict(causal=3), E_CAUSAL),
