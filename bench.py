@@ -8,9 +8,23 @@ d=128, bf16, causal, 1% of K rows x8), inputs resident in HBM.
 
 Prints ONE JSON line: TFLOP/s of the step (credited FLOPs: forward
 4*B*H*N^2*d/2 under the causal mask, backward 2.5x that), with a per-phase
-breakdown, the roofline of the dominant kernel measured live with HIP events
-on the launch stream, a sampled parity check against the fp64 oracle, and
-the oracle itself timed on the host cores on a bounded sample.
+and per-kernel breakdown, the roofline of the dominant kernel measured live
+with HIP events on the launch stream, a sampled parity check against the
+fp64 oracle, and the oracle itself timed on the host cores on a bounded
+sample.
+
+Each kernel has its own entry point (attn_fwd, attn_bwd_dq, attn_bwd_dkdv;
+attn_bwd is the last two in order), so the events bracket one kernel each.
+A kernel's algorithmic FLOPs are those of the products its algorithm
+performs per (batch, head), halved under the causal mask: the forward
+4 N^2 d (S, P.V); the dq kernel 6 N^2 d (S and dP recomputed, dS.K); the
+dk/dv kernel 8 N^2 d (S and dP recomputed, P^T.dO, dS^T.Q).
+
+Counter support: --copy-calibration adds a plain copy of known size
+(torch.neg over 512 MiB) before the warm-up, and --traffic FETCH_DIR
+WRITE_DIR turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+such a command into profiles/traffic.json: HBM bytes per launch of each
+kernel, each counter scaled by the copy's known bytes over its reading.
 """
 import argparse
 import hashlib
@@ -57,7 +71,59 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of each oracle sample")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 512 MiB copy (read + write) first, for counter scaling")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output dirs")
     return ap.parse_args()
+
+
+KERNELS = ("fwd_kernel", "dq_kernel", "dkdv_kernel")
+COPY_BYTES = 512 << 20
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, workload):
+    """Per-launch HBM bytes of each kernel from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), scaled by copy-bytes / counter-reading of the copy."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        for r in _pmc_rows(d):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = next((k for k in KERNELS if k in name), "copy" if "neg" in name else None)
+            if key:
+                per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        if "copy" not in per:
+            raise SystemExit(f"no copy-calibration dispatch found in {d}")
+        factor = COPY_BYTES / (sum(per["copy"]) / len(per["copy"]))
+        for k in KERNELS:
+            if k in per:
+                e = res.setdefault(k, {})
+                e[counter.lower() + "_raw_bytes"] = sum(per[k]) / len(per[k])
+                e[counter.lower() + "_factor"] = factor
+                e[counter.lower() + "_bytes"] = factor * sum(per[k]) / len(per[k])
+    for k, e in res.items():
+        e["bytes"] = e.get("fetch_size_bytes", 0.0) + e.get("write_size_bytes", 0.0)
+        e["source_hash"] = source_hash()
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = {}
+    if os.path.exists(path):
+        rec = json.load(open(path))
+    rec[workload] = res
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec[workload], indent=1))
 
 
 def cpu_baseline(w, t, scale, budget_s):
@@ -133,6 +199,9 @@ def sampled_parity(w, t, o, lse, scale):
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(every (batch, head) is independent; see the sharding notes). "
@@ -159,85 +228,116 @@ def main():
     sp = stream.cuda_stream
     causal = int(w.causal)
 
+    nbytes_ws = ws.numel()
+
     def fwd():
         st = attn.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                            B, H, N, d, scale, causal, code, code, sp)
         if st:
             raise attn.AttnError(st, "attn_fwd")
 
-    def bwd():
-        st = attn.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
-                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                           ws.data_ptr(), ws.numel(), B, H, N, d, scale, causal, code, code, sp)
+    def bwd_dq():
+        st = attn.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              dO.data_ptr(), lse.data_ptr(), dq.data_ptr(), ws.data_ptr(),
+                              nbytes_ws, B, H, N, d, scale, causal, code, code, sp)
         if st:
-            raise attn.AttnError(st, "attn_bwd")
+            raise attn.AttnError(st, "attn_bwd_dq")
 
-    f_fwd = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
-    f_bwd = 2.5 * f_fwd
-    phases = {"step": (fwd, bwd), "fwd": (fwd,), "bwd": (bwd,)}[args.phase]
+    def bwd_dkdv():
+        st = attn.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(),
+                                dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes_ws, B, H, N,
+                                d, scale, causal, code, code, sp)
+        if st:
+            raise attn.AttnError(st, "attn_bwd_dkdv")
+
+    half = 0.5 if w.causal else 1.0
+    unit = B * H * N * N * d * half
+    f_fwd = 4.0 * unit
+    f_bwd = 2.5 * f_fwd                      # credited: five N^2 d products
+    algo = {"fwd_kernel": 4.0 * unit, "dq_kernel": 6.0 * unit, "dkdv_kernel": 8.0 * unit}
+    calls = {"step": [("fwd_kernel", fwd), ("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)],
+             "fwd": [("fwd_kernel", fwd)],
+             "bwd": [("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)]}[args.phase]
     if args.phase == "bwd":
         fwd()
     flops_step = {"step": f_fwd + f_bwd, "fwd": f_fwd, "bwd": f_bwd}[args.phase]
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
-        for p in phases:
-            p()
+        for _, fn in calls:
+            fn()
     torch.cuda.synchronize()
 
-    # timed region: events around every call on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+    # timed region: an event after every call, all on the launch stream
+    nc = len(calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nc + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for j, p in enumerate(phases):
-            p()
-            ev[s][j + 1].record(stream)
+    for st_ in range(args.steps):
+        ev[st_][0].record(stream)
+        for j_, (_, fn) in enumerate(calls):
+            fn()
+            ev[st_][j_ + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    per = np.array([[ev[s][j].elapsed_time(ev[s][j + 1]) for j in range(len(phases))]
-                    for s in range(args.steps)])  # ms
+    per = np.array([[ev[s_][j_].elapsed_time(ev[s_][j_ + 1]) for j_ in range(nc)]
+                    for s_ in range(args.steps)])  # ms
     ms_step = wall * 1e3 / args.steps
     value = flops_step / (ms_step * 1e-3) / 1e12
 
-    names = {"step": ["fwd", "bwd"], "fwd": ["fwd"], "bwd": ["bwd"]}[args.phase]
-    phase_flops = {"fwd": f_fwd, "bwd": f_bwd}
-    breakdown = {}
-    for j, nm in enumerate(names):
-        mean_ms = float(per[:, j].mean())
-        breakdown[nm] = {"ms_mean": mean_ms, "ms_min": float(per[:, j].min()),
-                         "tflops": phase_flops[nm] / (mean_ms * 1e-3) / 1e12,
-                         "frac_of_peak": phase_flops[nm] / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    kernels = {}
+    for j_, (nm, _) in enumerate(calls):
+        m = float(per[:, j_].mean())
+        kernels[nm] = {"ms_mean": m, "ms_min": float(per[:, j_].min()),
+                       "algorithmic_tflop": algo[nm] / 1e12,
+                       "tflops": algo[nm] / (m * 1e-3) / 1e12,
+                       "frac_of_peak": algo[nm] / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    phases = {}
+    if "fwd_kernel" in kernels:
+        m = kernels["fwd_kernel"]["ms_mean"]
+        phases["fwd"] = {"ms_mean": m, "tflops": f_fwd / (m * 1e-3) / 1e12,
+                         "frac_of_peak": f_fwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    if "dq_kernel" in kernels:
+        m = kernels["dq_kernel"]["ms_mean"] + kernels["dkdv_kernel"]["ms_mean"]
+        phases["bwd"] = {"ms_mean": m, "tflops": f_bwd / (m * 1e-3) / 1e12,
+                         "frac_of_peak": f_bwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "flops": "credited 2.5x forward"}
 
-    # roofline of the forward kernel (one launch per attn_fwd call)
-    dom = "fwd" if "fwd" in breakdown else "bwd"
-    dom_ms = breakdown[dom]["ms_mean"]
-    dom_flops = phase_flops[dom]
+    # roofline of the dominant kernel (longest mean launch)
+    dom = max(kernels, key=lambda k_: kernels[k_]["ms_mean"])
     traffic = None
     tp = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tp):
         try:
-            rec = json.load(open(tp))
-            entry = rec.get(w.name, {}).get(dom)
+            entry = json.load(open(tp)).get(w.name, {}).get(dom)
             if entry and entry.get("source_hash") == source_hash():
                 traffic = entry.get("bytes")
         except (ValueError, OSError):
             traffic = None
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": {"fwd": "fwd_kernel", "bwd": "dq_kernel+dkdv_kernel"}[dom],
-                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
+    achieved = kernels[dom]["tflops"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "flops_per_launch": algo[dom], "launch_ms": kernels[dom]["ms_mean"]}
+    names = [nm for nm, _ in calls]
 
     out = {
         "metric": "attention fwd/bwd TFLOP/s at 1 GPU + % of bf16 MFMA peak",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.describe()}; step = {'+'.join(names)}",
+        "config": {"workload": f"{w.name}: {w.describe()}; step = {' + '.join(names)}",
                    "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
                    "causal": w.causal, "parallelism": "none (1 GPU)"},
         "frac_of_peak": value / PEAK_BF16_TFLOPS,
-        "phases": breakdown,
+        "phases": phases,
+        "kernels": kernels,
         "roofline": roofline,
         "kernel_source_hash": source_hash(),
     }

@@ -6,8 +6,9 @@ computation runs in the library's HIP kernels.  torch supplies device
 memory and the current stream.
 
 Low level (same names and argument order as the C ABI, raw integers and
-device pointers):  :func:`attn_fwd`, :func:`attn_bwd`,
-:func:`attn_bwd_workspace_size`, :func:`attn_status_str`.
+device pointers):  :func:`attn_fwd`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
+:func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`,
+:func:`attn_status_str`.
 
 Tensor level:  :func:`forward` and :func:`backward`.
 """
@@ -21,7 +22,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_status_str",
+    "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
+    "attn_status_str",
     "forward", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
 ]
 
@@ -65,6 +67,10 @@ def _load():
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_bwd.restype = i32
     lib.attn_bwd.argtypes = [vp] * 10 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_bwd_dq.restype = i32
+    lib.attn_bwd_dq.argtypes = [vp] * 8 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_bwd_dkdv.restype = i32
+    lib.attn_bwd_dkdv.argtypes = [vp] * 7 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -89,6 +95,20 @@ def attn_bwd(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, dk: int
              scale: float, causal: int, dtype: int, out_dtype: int, stream: int) -> int:
     return _load().attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes,
                             B, H, N, d, scale, causal, dtype, out_dtype, stream)
+
+
+def attn_bwd_dq(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, workspace: int,
+                workspace_bytes: int, B: int, H: int, N: int, d: int, scale: float, causal: int,
+                dtype: int, out_dtype: int, stream: int) -> int:
+    return _load().attn_bwd_dq(q, k, v, o, dO, lse, dq, workspace, workspace_bytes, B, H, N, d,
+                               scale, causal, dtype, out_dtype, stream)
+
+
+def attn_bwd_dkdv(q: int, k: int, v: int, dO: int, dk: int, dv: int, workspace: int,
+                  workspace_bytes: int, B: int, H: int, N: int, d: int, scale: float,
+                  causal: int, dtype: int, out_dtype: int, stream: int) -> int:
+    return _load().attn_bwd_dkdv(q, k, v, dO, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                                 scale, causal, dtype, out_dtype, stream)
 
 
 def attn_status_str(status: int) -> str:

@@ -113,31 +113,59 @@ size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int d
     return attn::bwd_workspace_bytes(B * H, N);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-             const float* lse, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-             int causal, int dtype, int out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by attn_bwd (which = 3), attn_bwd_dq (1) and attn_bwd_dkdv (2).
+int bwd_common(int which, const void* q, const void* k, const void* v, const void* o,
+               const void* dO, const float* lse, void* dq, void* dk, void* dv, const void* ws,
+               size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+               int causal, int dtype, int out_dtype, void* stream) {
     bool empty = false;
     int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
     if (st != ATTN_OK || empty) return st;
-    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
-    const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv};
+    const bool want_dq = which & 1, want_dkdv = which & 2;
+    if (!q || !k || !v || !dO) return ATTN_ERR_NULL;
+    if (want_dq && (!o || !lse || !dq)) return ATTN_ERR_NULL;
+    if (want_dkdv && (!dk || !dv)) return ATTN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, dO, want_dq ? o : q, want_dq ? (const void*)lse : q,
+                          want_dq ? dq : q, want_dkdv ? dk : q, want_dkdv ? dv : q};
     for (const void* p : ptrs)
         if (!aligned16(p)) return ATTN_ERR_ALIGN;
     const int64_t BH = B * H;
     const size_t need = attn::bwd_workspace_bytes(BH, N);
-    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    if (!ws || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(ws)) return ATTN_ERR_ALIGN;
+    if (BH > 0x7fffffff / ((N + 63) / 64)) return ATTN_ERR_SHAPE;
+
+    // outputs may overlap neither the inputs nor each other
     const size_t tbytes = size_t(BH * N * d) * 2;
     const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
-    const Range outs[4] = {range(dq, obytes), range(dk, obytes), range(dv, obytes),
-                           range(workspace, need)};
-    const Range ins[6] = {range(q, tbytes), range(k, tbytes), range(v, tbytes),
-                          range(o, obytes), range(dO, tbytes), range(lse, size_t(BH * N) * 4)};
-    for (int i = 0; i < 4; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
+    Range outs[4];
+    int no = 0;
+    Range ins[7];
+    int ni = 0;
+    ins[ni++] = range(q, tbytes);
+    ins[ni++] = range(k, tbytes);
+    ins[ni++] = range(v, tbytes);
+    ins[ni++] = range(dO, tbytes);
+    if (want_dq) {
+        ins[ni++] = range(o, obytes);
+        ins[ni++] = range(lse, size_t(BH * N) * 4);
+        outs[no++] = range(dq, obytes);
+        outs[no++] = range(ws, need);           // written by the dq half
+    } else {
+        ins[ni++] = range(ws, need);            // read by the dk/dv half
+    }
+    if (want_dkdv) {
+        outs[no++] = range(dk, obytes);
+        outs[no++] = range(dv, obytes);
+    }
+    for (int i = 0; i < no; ++i) {
+        for (int r = 0; r < ni; ++r)
+            if (overlap(outs[i], ins[r])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < no; ++j)
             if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
     }
 
@@ -151,16 +179,43 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.ws = static_cast<float*>(workspace);
+    a.ws = static_cast<float*>(const_cast<void*>(ws));
     a.N = int(N);
-    if (BH > 0x7fffffff / ((N + 63) / 64)) return ATTN_ERR_SHAPE;
     a.BH = int(BH);
     a.c = fabsf(scale) * kLog2e;
     a.scale = scale;
     a.negate = scale < 0.f;
-    hipError_t e = attn::launch_bwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
+    hipError_t e = attn::launch_bwd(a, which, dtype, out_dtype == ATTN_F32, int(d), causal,
                                     (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+             int causal, int dtype, int out_dtype, void* stream) {
+    return bwd_common(3, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                      scale, causal, dtype, out_dtype, stream);
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* workspace, size_t workspace_bytes, int64_t B,
+                int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+                int out_dtype, void* stream) {
+    return bwd_common(1, q, k, v, o, dO, lse, dq, nullptr, nullptr, workspace, workspace_bytes, B,
+                      H, N, d, scale, causal, dtype, out_dtype, stream);
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk,
+                  void* dv, const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                  int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
+                  void* stream) {
+    return bwd_common(2, q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace,
+                      workspace_bytes, B, H, N, d, scale, causal, dtype, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -514,21 +514,28 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
 }
 
 template <typename T, typename TO, int D, bool CAUSAL>
-hipError_t launch(const BwdArgs& a, hipStream_t stream) {
-    const int nqb = (a.N + BQ - 1) / BQ;
-    const int nkb = (a.N + BK - 1) / BK;
-    const int tq = a.BH * nqb, tk = a.BH * nkb;
-    hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL>), dim3(tk), dim3(NT), 0, stream, a, nkb, tk);
-    return hipGetLastError();
+hipError_t launch(const BwdArgs& a, int which, hipStream_t stream) {
+    if (which & 1) {
+        const int nqb = (a.N + BQ - 1) / BQ;
+        const int tq = a.BH * nqb;
+        hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (which & 2) {
+        const int nkb = (a.N + BK - 1) / BK;
+        const int tk = a.BH * nkb;
+        hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL>), dim3(tk), dim3(NT), 0, stream, a, nkb, tk);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 template <typename T, typename TO>
-hipError_t launch_t(const BwdArgs& a, int d, int causal, hipStream_t stream) {
-    if (d == 64) return causal ? launch<T, TO, 64, true>(a, stream) : launch<T, TO, 64, false>(a, stream);
-    return causal ? launch<T, TO, 128, true>(a, stream) : launch<T, TO, 128, false>(a, stream);
+hipError_t launch_t(const BwdArgs& a, int which, int d, int causal, hipStream_t stream) {
+    if (d == 64)
+        return causal ? launch<T, TO, 64, true>(a, which, stream) : launch<T, TO, 64, false>(a, which, stream);
+    return causal ? launch<T, TO, 128, true>(a, which, stream) : launch<T, TO, 128, false>(a, which, stream);
 }
 
 }  // namespace
@@ -537,12 +544,13 @@ size_t bwd_workspace_bytes(int64_t BH, int64_t N) {
     return size_t(2) * size_t(BH) * size_t(padded_rows(int(N))) * sizeof(float);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, int which, int dtype, bool out_f32, int d, int causal,
+                      hipStream_t stream) {
     if (dtype == 1)
-        return out_f32 ? launch_t<__bf16, float>(a, d, causal, stream)
-                       : launch_t<__bf16, __bf16>(a, d, causal, stream);
-    return out_f32 ? launch_t<_Float16, float>(a, d, causal, stream)
-                   : launch_t<_Float16, _Float16>(a, d, causal, stream);
+        return out_f32 ? launch_t<__bf16, float>(a, which, d, causal, stream)
+                       : launch_t<__bf16, __bf16>(a, which, d, causal, stream);
+    return out_f32 ? launch_t<_Float16, float>(a, which, d, causal, stream)
+                   : launch_t<_Float16, _Float16>(a, which, d, causal, stream);
 }
 
 }  // namespace attn

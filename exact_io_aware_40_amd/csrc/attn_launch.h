@@ -45,6 +45,8 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N);
-hipError_t launch_bwd(const BwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
+// which: 1 = dq kernel only, 2 = dk/dv kernel only, 3 = both in order
+hipError_t launch_bwd(const BwdArgs& a, int which, int dtype, bool out_f32, int d, int causal,
+                      hipStream_t stream);
 
 }  // namespace attn

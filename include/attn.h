@@ -133,6 +133,29 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, int out_dtype, void* stream);
 
+/*
+ * attn_bwd_dq, attn_bwd_dkdv -- the two halves of attn_bwd, callable on
+ * their own.  attn_bwd is exactly attn_bwd_dq followed by attn_bwd_dkdv on
+ * the same stream with the same arguments.
+ *
+ * attn_bwd_dq computes dq and fills `workspace` with two values per query
+ * row (D_i = dO_i . o_i and lse_i log2(e)); it reads q, k, v, o, dO, lse and
+ * writes dq and the workspace.  attn_bwd_dkdv computes dk and dv; it reads
+ * q, k, v, dO and a workspace filled by attn_bwd_dq for the same inputs,
+ * sizes and flags (enqueued earlier on the same stream, or otherwise
+ * complete), and writes dk and dv.  It does not read o or lse.  Argument
+ * meanings, layouts and validation are those of attn_bwd; pointers a call
+ * does not use may be NULL.
+ */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* workspace, size_t workspace_bytes,
+                int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                int dtype, int out_dtype, void* stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                  void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                  int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                  int dtype, int out_dtype, void* stream);
+
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);
 

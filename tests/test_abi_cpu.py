@@ -30,8 +30,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
-                                    "attn_status_str"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
+                                    "attn_bwd_workspace_size", "attn_fwd", "attn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -116,3 +116,50 @@ def test_bwd_rejects(kw, code):
 
 def test_bwd_empty_is_noop():
     assert bwd(B=0, ws=0, wsb=0) == OK
+
+
+def bwd_dq(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], ws=P[9], wsb=1 << 20,
+             B=2, H=3, N=100, d=128, scale=0.1, causal=1, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_bwd_dq(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"], a["ws"],
+                            a["wsb"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                            a["dtype"], od, a["stream"])
+
+
+def bwd_dkdv(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], dO=P[4], dk=P[7], dv=P[8], ws=P[9], wsb=1 << 20,
+             B=2, H=3, N=100, d=128, scale=0.1, causal=1, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_bwd_dkdv(a["q"], a["k"], a["v"], a["dO"], a["dk"], a["dv"], a["ws"],
+                              a["wsb"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                              a["dtype"], od, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=0), E_NULL), (dict(lse=0), E_NULL), (dict(dq=0), E_NULL), (dict(q=0), E_NULL),
+    (dict(ws=0), E_WS), (dict(wsb=6143), E_WS), (dict(d=80), E_HD), (dict(dtype=3), E_DT),
+    (dict(dq=P[9] + 4096), E_ALIAS),           # dq over the workspace it also writes
+    (dict(ws=P[3]), E_ALIAS), (dict(dq=P[5]), E_ALIAS), (dict(causal=5), E_CAUSAL),
+])
+def test_bwd_dq_rejects(kw, code):
+    assert bwd_dq(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=0), E_NULL), (dict(dv=0), E_NULL), (dict(dO=0), E_NULL),
+    (dict(ws=0), E_WS), (dict(wsb=100), E_WS), (dict(dk=P[7] + 2), E_ALIGN),
+    (dict(dk=P[9]), E_ALIAS),                  # dk over the workspace it reads
+    (dict(dv=P[7] + 64), E_ALIAS), (dict(dv=P[1]), E_ALIAS), (dict(scale=float("nan")), E_SCALE),
+])
+def test_bwd_dkdv_rejects(kw, code):
+    assert bwd_dkdv(**kw) == code
+
+
+def test_split_backward_ignores_unused_pointers():
+    """Each half validates only what it uses: o, lse may be NULL for the
+    dk/dv half, and an empty problem does nothing."""
+    assert bwd_dkdv(B=0) == OK and bwd_dq(N=0) == OK
+    assert bwd_dkdv(d=96) == E_HD      # still validated before anything else

@@ -100,6 +100,31 @@ def test_gradient_invariants():
     assert sk <= bk and sv <= bv, (sk, bk, sv, bv)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_calls_match_attn_bwd(causal):
+    """attn_bwd_dq then attn_bwd_dkdv give exactly what attn_bwd gives."""
+    dt = torch.bfloat16
+    q, k, v, dO = (randn((1, 3, 300, 128), dt, 350 + i).to(DEV) for i in range(4))
+    announce(f"split backward causal={causal}")
+    o, lse = attn.forward(q, k, v, causal=causal)
+    dq, dk, dv = attn.backward(q, k, v, o, lse, dO, causal=causal)
+    B, H, N, d = q.shape
+    code = attn.ATTN_BF16
+    nbytes = attn.attn_bwd_workspace_size(B, H, N, d, code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    dq2, dk2, dv2 = (torch.full_like(q, float("nan")) for _ in range(3))
+    sp = torch.cuda.current_stream().cuda_stream
+    sc = 1 / math.sqrt(d)
+    assert attn.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
+                            lse.data_ptr(), dq2.data_ptr(), ws.data_ptr(), nbytes, B, H, N, d, sc,
+                            int(causal), code, code, sp) == 0
+    assert attn.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(),
+                              dk2.data_ptr(), dv2.data_ptr(), ws.data_ptr(), nbytes, B, H, N, d,
+                              sc, int(causal), code, code, sp) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
 def test_repeatable_bitwise():
     q, k, v, dO = (randn((1, 4, 700, 128), torch.bfloat16, 340 + i) for i in range(4))
     announce("bwd repeatability")
