@@ -4,6 +4,7 @@
 // (and testable) without a GPU.
 #include "attn.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -13,6 +14,13 @@ namespace {
 
 constexpr int64_t kMaxHeadElems = int64_t(1) << 30;  // N * d per head
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Exponent units of the kernels: |scale| log2(e), raised to the smallest
+// normal float when it is smaller (a zero scale in particular).  For any
+// finite score s, s * FLT_MIN rounds 2^(s c - m c) to exactly 1, so the
+// weights of a zero scale come out uniform as they should, while a masked
+// score (-inf) still gives -inf * c = -inf and weight 0.
+float exponent_unit(float scale) { return fmaxf(fabsf(scale) * kLog2e, FLT_MIN); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -100,7 +108,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     const int64_t total = BH * a.nqb;
     if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
     a.total = int(total);
-    a.c = fabsf(scale) * kLog2e;
+    a.c = exponent_unit(scale);
     a.negate = scale < 0.f;
     hipError_t e = attn::launch_fwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
                                     (hipStream_t)stream);
@@ -182,7 +190,7 @@ int bwd_common(int which, const void* q, const void* k, const void* v, const voi
     a.ws = static_cast<float*>(const_cast<void*>(ws));
     a.N = int(N);
     a.BH = int(BH);
-    a.c = fabsf(scale) * kLog2e;
+    a.c = exponent_unit(scale);
     a.scale = scale;
     a.negate = scale < 0.f;
     hipError_t e = attn::launch_bwd(a, which, dtype, out_dtype == ATTN_F32, int(d), causal,

@@ -38,8 +38,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer resource over `bytes` bytes at `base`: loads past the end return 0.
+// base and bytes must be the same for the whole wave; they are moved to
+// scalar registers explicitly so that every load using the resource is a
+// single instruction (a resource the compiler believes may differ between
+// lanes costs a loop per load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+    const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+    void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes, read at

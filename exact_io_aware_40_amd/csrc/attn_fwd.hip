@@ -58,10 +58,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     constexpr int DB = D / 32;             // 32-wide output column blocks
 
     // [stage][K | V][tile]
-    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
 
     const int N = a.N;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
 
@@ -91,9 +92,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
 
-    // Copy p of this thread fills LDS slot (p*4 + w)*64 + lane of the tile:
-    // tile row `row`, physical granule pg, which holds logical granule
-    // pg ^ key(row) of that row (the t_off placement).
+    // K and V tiles have separate double buffers: K runs one tile ahead of V,
+    // because the products S = K Q^T for tile t+1 are issued while tile t's
+    // exponents and P.V products run.  Copy p of this thread fills LDS slot
+    // (p*4 + w)*64 + lane of a tile: row `row`, physical granule pg, which
+    // holds logical granule pg ^ key(row) of that row (the t_off placement).
     unsigned src_off[LOADS];
 #pragma unroll
     for (int p = 0; p < LOADS; ++p) {
@@ -101,18 +104,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         const int row = slot / GR, pg = slot % GR;
         src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
     }
-    auto issue = [&](auto stg, int t) {
-        char* st = smem + decltype(stg)::value * 2 * TILE;
+    // smem: K slot 0, K slot 1, V slot 0, V slot 1.  Copies of tiles past
+    // the end of the sequence read zeros and are never consumed.
+    auto issue = [&](auto which, auto slot, int t) {
+        char* st = smem + (decltype(which)::value * 2 + decltype(slot)::value) * TILE;
+        const __amdgpu_buffer_rsrc_t rs = decltype(which)::value ? vrs : krs;
         const unsigned base = (unsigned)t * TILE;
 #pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            dma16(krs, st + (p * 4 + w) * 1024, base + src_off[p]);
-            dma16(vrs, st + TILE + (p * 4 + w) * 1024, base + src_off[p]);
-        }
+        for (int p = 0; p < LOADS; ++p) dma16(rs, st + (p * 4 + w) * 1024, base + src_off[p]);
     };
 
     // Loop-invariant LDS offsets of this lane's operand reads; the block,
-    // half-tile and stage parts are added as immediates (the swizzle key
+    // half-tile and slot parts are added as immediates (the swizzle key
     // depends on the row modulo 16 only).
     int koff[DK];
 #pragma unroll
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         voff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
     }
 
-    const float c = a.c;
+    const float c = a.c;   // > 0 (the host maps a zero scale to the smallest normal unit)
     f32x16 oacc[DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
@@ -138,75 +141,68 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     // one exactly as used) and the fp32 sum of P (it gives lse)
     float l_run = 0.f, lf_run = 0.f;
 
-    // One K/V tile for this wave's 32 rows.  MASK: causal diagonal or the
-    // ragged last tile; otherwise every key of the tile is visible.
-    auto tile = [&](auto stg, auto mask, int j0) {
-        constexpr int STG = decltype(stg)::value;
-        constexpr bool MASK = decltype(mask)::value;
-        const char* sK = smem + STG * 2 * TILE;
-        const char* sV = sK + TILE;
-
-        int nb = KB;  // 32-key blocks holding any key visible to this wave
-        if (MASK) {
-            if (CAUSAL) {
-                const int lim = qlo + 31 - j0;
-                nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
-            }
-            nb = min(nb, (N - j0 + 31) / 32);
-        }
-
-        // S^T = K Q^T
-        f32x16 s[KB];
+    // S^T = K Q^T for a whole tile (every 32-key block; blocks a wave cannot
+    // see are masked to -inf afterwards and then contribute exactly zero).
+    auto scores = [&](auto kslot, f32x16 (&s)[KB]) {
+        const char* sK = smem + decltype(kslot)::value * TILE;
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            if (MASK && b >= nb) continue;
+        for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
                 const i32x4 kx = *(const i32x4*)(sK + koff[kk] + 32 * b * ROWB);
-                const f32x16 acc = kk == 0 ? f32x16{} : s[b];
-                s[b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), acc);
+                s[b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s[b]);
             }
-        }
-        if (MASK) {
+    };
+
+    // Mask tile j0's scores if needed, then move the row's reference when
+    // its maximum rose by more than kTau binades; rescale l and O by the
+    // factor (O already holds every earlier tile's P.V).
+    auto rowmax_update = [&](f32x16 (&s)[KB], int j0) {
+        const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
+        if (need_mask) [[unlikely]] {
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                if (b >= nb) continue;
+            for (int b = 0; b < KB; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
                     const bool ok = key < N && (!CAUSAL || key <= qrow);
                     s[b][r] = ok ? s[b][r] : -INFINITY;
                 }
-            }
         }
-
-        // row maximum of the tile; move the reference only past kTau
         float mt = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            if (MASK && b >= nb) continue;
+        for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[b][r], s[b][r + 1]));
-        }
-        mt = max32(mt);
-        const float tc = (mt == -INFINITY) ? -INFINITY : mt * c;
+        const float tc = max32(mt) * c;
         const bool upd = tc > mc_run + kTau;
         const float mc = upd ? tc : mc_run;
         const float alpha = upd ? fast_exp2(mc_run - mc) : 1.f;
         mc_run = mc;
+        l_run *= alpha;
+        lf_run *= alpha;
+        if (__ballot(upd) != 0) [[unlikely]] {
+#pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        }
+    };
 
-        // P = 2^(S c - mc), packed to the operand type
-        v8 pb[KB][2];
+    // P = 2^(S c - mc) for a tile whose reference is settled, packed to the
+    // operand type, and O^T += V^T P^T.  B operand chunk (b, q) holds, at
+    // k = 8h + e, the probability of key 32b + 16q + 8(e/4) + 4h + e%4; the
+    // transposing reads fetch V at exactly those keys.
+    auto exp_pv = [&](auto vslot, f32x16 (&s)[KB]) {
+        const char* sV = smem + (2 + decltype(vslot)::value) * TILE;
+        const float mc = mc_run;
         float lsum = 0.f, lfsum = 0.f;
+        v8 pb[KB][2];
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-            if (MASK && b >= nb) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float e = fmaf(s[b][r], c, -mc);
-                // a masked score's exponent is -inf even when c == 0
-                if (MASK) e = (s[b][r] == -INFINITY) ? -INFINITY : e;
-                s[b][r] = fast_exp2(e);
+                s[b][r] = fast_exp2(fmaf(s[b][r], c, -mc));
                 lfsum += s[b][r];
             }
 #pragma unroll
@@ -219,23 +215,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
                 lsum = Elem<T>::sum8(pb[b][q], lsum);
             }
         }
-        l_run = alpha * l_run + lsum;
-        lf_run = alpha * lf_run + lfsum;
-        if (__ballot(upd) != 0) [[unlikely]] {
+        l_run += lsum;
+        lf_run += lfsum;
 #pragma unroll
-            for (int cb = 0; cb < DB; ++cb)
+        for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        }
-
-        // O^T += V^T P^T.  B operand chunk (b, q) holds, at k = 8h + e, the
-        // probability of key 32b + 16q + 8(e/4) + 4h + e%4; the transposing
-        // reads fetch V at exactly those keys.
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb) {
-#pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                if (MASK && b >= nb) continue;
+            for (int b = 0; b < KB; ++b)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const int roff = (32 * b + 16 * q) * ROWB;
@@ -243,34 +228,39 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
                     const i16x4 hi = lds_read_tr16(sV, voff[1][cb] + roff);
                     oacc[cb] = Elem<T>::mma(join8<v8>(lo, hi), pb[b][q], oacc[cb]);
                 }
-            }
-        }
     };
 
-    // One pipeline step: start the copy of tile t+1 into the other stage,
-    // consume tile t, then wait for the copy and for every wave.
-    auto step = [&](auto stg, int t) {
-        constexpr int STG = decltype(stg)::value;
-        if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
-        const int j0 = t * BC;
-        const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
-        if (need_mask)
-            tile(stg, std::true_type{}, j0);
-        else
-            tile(stg, std::false_type{}, j0);
+    // Iteration t: K(t+2) and V(t+1) copies start; S for tile t+1 (its K
+    // arrived one iteration ago) is issued while tile t's exponents and
+    // P.V products run; then tile t+1's mask, row maximum and reference.
+    // Invariant at the top: tile t's scores are in `cur`, K(t+1) and V(t)
+    // are in LDS, and no wave still reads K(t)'s slot.
+    auto step = [&](auto par, int t, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
+        constexpr int P = decltype(par)::value;   // t % 2
+        issue(IC<0>{}, IC<P>{}, t + 2);
+        issue(IC<1>{}, IC<1 - P>{}, t + 1);
+        scores(IC<1 - P>{}, nxt);
+        exp_pv(IC<P>{}, cur);
+        if (t + 1 < ntiles) rowmax_update(nxt, (t + 1) * BC);
         wait_vmem();
         __syncthreads();
     };
 
-    issue(IC<0>{}, 0);
+    f32x16 sA[KB], sB[KB];
+    issue(IC<0>{}, IC<0>{}, 0);
+    issue(IC<1>{}, IC<0>{}, 0);
+    issue(IC<0>{}, IC<1>{}, 1);
     wait_vmem();
     __syncthreads();
+    scores(IC<0>{}, sA);
+    rowmax_update(sA, 0);
+    __syncthreads();   // every wave is done with K(0)'s slot
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
-        step(IC<0>{}, t);
-        step(IC<1>{}, t + 1);
+        step(IC<0>{}, t, sA, sB);
+        step(IC<1>{}, t + 1, sB, sA);
     }
-    if (t < ntiles) step(IC<0>{}, t);
+    if (t < ntiles) step(IC<0>{}, t, sA, sB);
 
     // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
     const float l_tot = sum32(l_run);
