@@ -31,6 +31,7 @@ constexpr int NT = 256;         // 4 waves
 constexpr int BQ = 128;         // dq_kernel: query rows per workgroup
 constexpr int BKT = 64;         // dq_kernel: keys per K/V tile
 constexpr int BK = 128;         // dkdv_kernel: keys per workgroup
+constexpr int NTK = 512;        // dkdv_kernel: 8 waves
 constexpr int BQT = 64;         // dkdv_kernel: queries per Q/dO tile
 constexpr int PADR = 64;        // workspace rows per head are padded to this
 constexpr float kLog2e = 1.4426950408889634f;
@@ -323,22 +324,34 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
 }
 
 // --------------------------------------------------------------------------
-// dkdv_kernel: dK, dV for 128 keys (32 per wave); Q/dO tiles stream past.
+// dkdv_kernel: dK, dV for 128 keys; Q/dO tiles of 64 queries stream past.
 //   S = Q K^T, dP = dO V^T (queries x keys), P = 2^(S c - lse2),
 //   dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
+// Eight waves, two per SIMD: wave (kg, qh) owns keys 32 kg .. 32 kg + 31 of
+// the block and query rows 32 qh .. 32 qh + 31 of every tile.  The block's
+// K and V rows sit in LDS for the whole kernel; the two halves' partial dK
+// and dV are added through LDS at the end.
 // --------------------------------------------------------------------------
 template <typename T, typename TO, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total) {
+__global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int total) {
     typedef typename Elem<T>::v8 v8;
-    constexpr int ROWB = D * 2, TILE = BQT * ROWB, LOADS = TILE / (NT * 16);
-    constexpr int QB = BQT / 32, DK = D / 16, DB = D / 32;
-    constexpr int STAGE = 2 * TILE + 2 * BQT * 4;   // Q tile, dO tile, lse2, D
+    constexpr int ROWB = D * 2;
+    constexpr int TILE = BQT * ROWB;               // one Q or dO tile
+    constexpr int KVB = BK * ROWB;                 // the K or V block
+    constexpr int TLOADS = TILE / (NTK * 16), KLOADS = KVB / (NTK * 16);
+    constexpr int DK = D / 16, DB = D / 32;
+    constexpr int STAGE = 2 * TILE + 2 * BQT * 4;  // Q tile, dO tile, lse2, D
+    constexpr int SMEM = 2 * KVB + 2 * STAGE;
     constexpr bool SPLIT = SplitDS<T>::value;
+    static_assert(4 * 2 * DB * 16 * 64 * 4 <= SMEM, "reduction area must fit in LDS");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    // [K block][V block][stage 0][stage 1]
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int N = a.N, NP = padded_rows(N);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = w & 3, qh = w >> 2;
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
 
@@ -347,45 +360,50 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
     const int kblk = L - bh * nkb;     // ascending: most queries first under the mask
     const int kb0 = kblk * BK;
     const size_t head = (size_t)bh * N * D;
-    const T* __restrict__ Kh = (const T*)a.k + head;
-    const T* __restrict__ Vh = (const T*)a.v + head;
     const unsigned head_bytes = (unsigned)N * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const T*)a.q + head, head_bytes);
     const __amdgpu_buffer_rsrc_t grs = make_rsrc((const T*)a.dO + head, head_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.ws + (size_t)bh * NP, (unsigned)N * 4);
     const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.ws + ((size_t)a.BH + bh) * NP, (unsigned)N * 4);
 
-    const int kw0 = kb0 + 32 * w;       // this wave's first key
+    const int kw0 = kb0 + 32 * kg;      // this wave's first key
     const int key = kw0 + l32;          // this lane's key
-    const bool live = key < N;
 
-    // K^T and V^T fragments of this lane's key (B operands)
-    i32x4 kf[DK], vf[DK];
+    // LDS slot s of a [rows][D] region holds row s / (D/8), physical granule
+    // s % (D/8): the 16-byte piece at logical granule pg ^ key(row).
+    auto src_of = [&](int slot) {
+        const int row = slot / (D / 8), pg = slot % (D / 8);
+        return (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
+    };
+    char* sKb = smem;
+    char* sVb = smem + KVB;
+    {
+        // the block's K and V rows (rows past the end read as zeros; negated K
+        // when scale < 0 is applied to the S product below)
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-        i32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-        if (live) {
-            const size_t off = (size_t)key * D + 16 * kk + 8 * h;
-            x = *(const i32x4*)(Kh + off);
-            y = *(const i32x4*)(Vh + off);
+        for (int p = 0; p < KLOADS; ++p) {
+            const int slot = (p * 8 + w) * 64 + lane;
+            const unsigned off = (unsigned)kb0 * ROWB + src_of(slot);
+            dma16(krs, sKb + (p * 8 + w) * 1024, off);
+            dma16(vrs, sVb + (p * 8 + w) * 1024, off);
         }
-        if (a.negate) x ^= (int)0x80008000;
-        kf[kk] = x;
-        vf[kk] = y;
     }
 
     const int t0 = CAUSAL ? kb0 / BQT : 0;
     const int ntiles = (N + BQT - 1) / BQT;
 
-    unsigned src_off[LOADS];
-    tile_sources<D, LOADS>(src_off, w, lane);
+    unsigned tsrc[TLOADS];
+#pragma unroll
+    for (int p = 0; p < TLOADS; ++p) tsrc[p] = src_of((p * 8 + w) * 64 + lane);
     auto issue = [&](auto stg, int t) {
-        char* st = smem + decltype(stg)::value * STAGE;
+        char* st = smem + 2 * KVB + decltype(stg)::value * STAGE;
         const unsigned base = (unsigned)t * TILE;
 #pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            dma16(qrs, st + (p * 4 + w) * 1024, base + src_off[p]);
-            dma16(grs, st + TILE + (p * 4 + w) * 1024, base + src_off[p]);
+        for (int p = 0; p < TLOADS; ++p) {
+            dma16(qrs, st + (p * 8 + w) * 1024, base + tsrc[p]);
+            dma16(grs, st + TILE + (p * 8 + w) * 1024, base + tsrc[p]);
         }
         // the tile's lse2 and D values: 64 floats each, 16 lanes of wave 0
         if (w == 0 && lane < BQT / 4) {
@@ -395,7 +413,9 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
         }
     };
 
-    // Q and dO rows as A operands (16-byte reads) and through transposing reads
+    // Operand offsets: rows l32 at granule 2kk + h (16-byte reads; the
+    // wave's K/V rows and Q/dO rows add a multiple of 32 rows), and the
+    // transposing reads of Q/dO rows 32 qh + 16 q + 4 h + s16/4 (+ 8).
     int roff[DK];
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) roff[kk] = t_off<D>(l32, 2 * kk + h);
@@ -407,8 +427,23 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
         toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
         toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
     }
+    // fold this wave's row offsets into the lane offsets once, so that every
+    // read below is a register plus a compile-time immediate
+    const int kvo = 32 * kg * ROWB, qo = 32 * qh * ROWB;
+    int qaddr[DK], kaddr[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) {
+        qaddr[kk] = roff[kk] + qo;
+        kaddr[kk] = roff[kk] + kvo;
+    }
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+        toff[0][cb] += qo;
+        toff[1][cb] += qo;
+    }
 
     const float c = a.c;
+    const int kneg = a.negate ? (int)0x80008000 : 0;   // scale < 0: S from -K and |scale|
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
@@ -418,39 +453,40 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
             dv[cb][r] = 0.f;
         }
 
-    // One 32-query block of a staged tile.  MASK: the block straddles the
-    // causal diagonal of this wave's keys.
-    auto block = [&](auto stg, auto mask, int qb, int i0) {
+    // This wave's 32 queries of a staged tile.  masked: the block straddles
+    // the causal diagonal of this wave's keys (one code path for both keeps
+    // the register footprint of a single copy).
+    auto block = [&](auto stg, bool masked, int i0) {
         constexpr int STG = decltype(stg)::value;
-        constexpr bool MASK = decltype(mask)::value;
-        const char* sQ = smem + STG * STAGE;
+        const char* sQ = smem + 2 * KVB + STG * STAGE;
         const char* sG = sQ + TILE;
         const float* sL = (const float*)(sQ + 2 * TILE);
         const float* sD = sL + BQT;
-        const int qo = 32 * qb * ROWB;
         f32x16 s, dp;
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) {
-            const i32x4 qx = *(const i32x4*)(sQ + roff[kk] + qo);
-            s = Elem<T>::mma(bit_cast<v8>(qx), bit_cast<v8>(kf[kk]), kk == 0 ? f32x16{} : s);
+            const i32x4 qx = *(const i32x4*)(sQ + qaddr[kk]);
+            const i32x4 kx = *(const i32x4*)(sKb + kaddr[kk]) ^ kneg;
+            s = Elem<T>::mma(bit_cast<v8>(qx), bit_cast<v8>(kx), kk == 0 ? f32x16{} : s);
         }
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) {
-            const i32x4 gx = *(const i32x4*)(sG + roff[kk] + qo);
-            dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vf[kk]), kk == 0 ? f32x16{} : dp);
+            const i32x4 gx = *(const i32x4*)(sG + qaddr[kk]);
+            const i32x4 vx = *(const i32x4*)(sVb + kaddr[kk]);
+            dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vx), kk == 0 ? f32x16{} : dp);
         }
-        // rows of this block held by the lane: 32qb + 8(r/4) + 4h + r%4
+        // rows of this block held by the lane: 32 qh + 8(r/4) + 4h + r%4
         f32x16 p;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int li = 32 * qb + 8 * rr + 4 * h;
+            const int li = 32 * qh + 8 * rr + 4 * h;
             const f32x4 l4 = *(const f32x4*)(sL + li);
             const f32x4 d4 = *(const f32x4*)(sD + li);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rr + e;
                 float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
-                if (MASK) pv = (key <= i0 + li + e) ? pv : 0.f;
+                pv = (!masked || key <= i0 + li + e) ? pv : 0.f;
                 p[r] = pv;
                 s[r] = pv * (dp[r] - d4[e]);   // dS
             }
@@ -467,7 +503,7 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
         for (int cb = 0; cb < DB; ++cb) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int ro = (32 * qb + 16 * q) * ROWB;
+                const int ro = 16 * q * ROWB;
                 const v8 gt = join8<v8>(lds_read_tr16(sG, toff[0][cb] + ro),
                                         lds_read_tr16(sG, toff[1][cb] + ro));
                 dv[cb] = Elem<T>::mma(gt, q ? pb1 : pb0, dv[cb]);
@@ -483,16 +519,9 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
         constexpr int STG = decltype(stg)::value;
         if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
         const int i0 = t * BQT;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int ib = i0 + 32 * qb;   // first query of the block
-            if (ib >= N) continue;
-            if (CAUSAL && ib + 31 < kw0) continue;          // every query before every key
-            if (CAUSAL && ib < kw0 + 31)
-                block(stg, std::true_type{}, qb, i0);
-            else
-                block(stg, std::false_type{}, qb, i0);
-        }
+        const int ib = i0 + 32 * qh;        // first query of this wave's rows
+        const bool skip = ib >= N || (CAUSAL && ib + 31 < kw0);   // every query before every key
+        if (!skip) block(stg, CAUSAL && ib < kw0 + 31, i0);
         wait_vmem();
         __syncthreads();
     };
@@ -507,7 +536,32 @@ __global__ __launch_bounds__(NT) void dkdv_kernel(BwdArgs a, int nkb, int total)
     }
     if (t < ntiles) step(IC<0>{}, t);
 
-    if (live) {
+    // the two query halves of each key group: qh = 1 hands its partial sums
+    // to qh = 0 through LDS ([kg][accumulator quad][lane] of 16 bytes)
+    f32x4* red = (f32x4*)smem + kg * (2 * DB * 4) * 64;
+    if (qh == 1) {
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                red[((cb * 4 + g) * 2 + 0) * 64 + lane] = {dk[cb][4 * g], dk[cb][4 * g + 1], dk[cb][4 * g + 2], dk[cb][4 * g + 3]};
+                red[((cb * 4 + g) * 2 + 1) * 64 + lane] = {dv[cb][4 * g], dv[cb][4 * g + 1], dv[cb][4 * g + 2], dv[cb][4 * g + 3]};
+            }
+    }
+    __syncthreads();
+    if (qh == 0 && key < N) {
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 xk = red[((cb * 4 + g) * 2 + 0) * 64 + lane];
+                const f32x4 xv = red[((cb * 4 + g) * 2 + 1) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dk[cb][4 * g + e] += xk[e];
+                    dv[cb][4 * g + e] += xv[e];
+                }
+            }
         store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale, h);
         store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, 1.f, h);
     }
@@ -525,7 +579,7 @@ hipError_t launch(const BwdArgs& a, int which, hipStream_t stream) {
     if (which & 2) {
         const int nkb = (a.N + BK - 1) / BK;
         const int tk = a.BH * nkb;
-        hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL>), dim3(tk), dim3(NT), 0, stream, a, nkb, tk);
+        hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL>), dim3(tk), dim3(NTK), 0, stream, a, nkb, tk);
         return hipGetLastError();
     }
     return hipSuccess;
