@@ -190,7 +190,9 @@ int bwd_common(int which, const void* q, const void* k, const void* v, const voi
     a.ws = static_cast<float*>(const_cast<void*>(ws));
     a.N = int(N);
     a.BH = int(BH);
-    a.c = exponent_unit(scale);
+    // the backward tracks no maximum, so it takes the exponent unit with the
+    // scale's sign and uses q and k as they are
+    a.c = scale < 0.f ? -exponent_unit(scale) : exponent_unit(scale);
     a.scale = scale;
     a.negate = scale < 0.f;
     hipError_t e = attn::launch_bwd(a, which, dtype, out_dtype == ATTN_F32, int(d), causal,

@@ -188,7 +188,6 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
             g = *(const i32x4*)(Gh + off);
             dpart += RowDot<T, TO>::run(Gh, Oh, off);
         }
-        if (a.negate) x ^= (int)0x80008000;
         qf[kk] = x;
         gf[kk] = g;
     }
@@ -340,12 +339,15 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     constexpr int KVB = BK * ROWB;                 // the K or V block
     constexpr int TLOADS = TILE / (NTK * 16), KLOADS = KVB / (NTK * 16);
     constexpr int DK = D / 16, DB = D / 32;
-    constexpr int STAGE = 2 * TILE + 2 * BQT * 4;  // Q tile, dO tile, lse2, D
-    constexpr int SMEM = 2 * KVB + 2 * STAGE;
+    constexpr int STAGE = 2 * TILE;                // Q tile, dO tile
+    constexpr int KOFF = 2 * STAGE;                // K block, then V block
+    constexpr int LOFF = KOFF + 2 * KVB;           // per stage: lse2[64], D[64]
+    constexpr int SMEM = LOFF + 2 * 2 * BQT * 4;
     constexpr bool SPLIT = SplitDS<T>::value;
     static_assert(4 * 2 * DB * 16 * 64 * 4 <= SMEM, "reduction area must fit in LDS");
+    static_assert(2 * STAGE <= 65536, "stage reads use 16-bit immediate offsets");
 
-    // [K block][V block][stage 0][stage 1]
+    // [stage 0: Q | dO][stage 1: Q | dO][K block][V block][lse2 | D per stage]
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int N = a.N, NP = padded_rows(N);
@@ -377,18 +379,13 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         const int row = slot / (D / 8), pg = slot % (D / 8);
         return (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
     };
-    char* sKb = smem;
-    char* sVb = smem + KVB;
-    {
-        // the block's K and V rows (rows past the end read as zeros; negated K
-        // when scale < 0 is applied to the S product below)
+    // the block's K and V rows (rows past the end read as zeros)
 #pragma unroll
-        for (int p = 0; p < KLOADS; ++p) {
-            const int slot = (p * 8 + w) * 64 + lane;
-            const unsigned off = (unsigned)kb0 * ROWB + src_of(slot);
-            dma16(krs, sKb + (p * 8 + w) * 1024, off);
-            dma16(vrs, sVb + (p * 8 + w) * 1024, off);
-        }
+    for (int p = 0; p < KLOADS; ++p) {
+        const int slot = (p * 8 + w) * 64 + lane;
+        const unsigned off = (unsigned)kb0 * ROWB + src_of(slot);
+        dma16(krs, smem + KOFF + (p * 8 + w) * 1024, off);
+        dma16(vrs, smem + KOFF + KVB + (p * 8 + w) * 1024, off);
     }
 
     const int t0 = CAUSAL ? kb0 / BQT : 0;
@@ -398,7 +395,8 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
 #pragma unroll
     for (int p = 0; p < TLOADS; ++p) tsrc[p] = src_of((p * 8 + w) * 64 + lane);
     auto issue = [&](auto stg, int t) {
-        char* st = smem + 2 * KVB + decltype(stg)::value * STAGE;
+        constexpr int STG = decltype(stg)::value;
+        char* st = smem + STG * STAGE;
         const unsigned base = (unsigned)t * TILE;
 #pragma unroll
         for (int p = 0; p < TLOADS; ++p) {
@@ -408,42 +406,31 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         // the tile's lse2 and D values: 64 floats each, 16 lanes of wave 0
         if (w == 0 && lane < BQT / 4) {
             const unsigned fo = (unsigned)(t * BQT + 4 * lane) * 4;
-            dma16(lrs, st + 2 * TILE, fo);
-            dma16(drs, st + 2 * TILE + BQT * 4, fo);
+            dma16(lrs, smem + LOFF + STG * 2 * BQT * 4, fo);
+            dma16(drs, smem + LOFF + STG * 2 * BQT * 4 + BQT * 4, fo);
         }
     };
 
-    // Operand offsets: rows l32 at granule 2kk + h (16-byte reads; the
-    // wave's K/V rows and Q/dO rows add a multiple of 32 rows), and the
-    // transposing reads of Q/dO rows 32 qh + 16 q + 4 h + s16/4 (+ 8).
-    int roff[DK];
+    // Per-lane LDS offsets; every read below adds only a compile-time
+    // immediate (stage, tensor, half tile) below 64 KiB.
+    int qaddr[DK], kaddr[DK];         // rows l32 (+ this wave's 32 rows) at granule 2kk + h
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) roff[kk] = t_off<D>(l32, 2 * kk + h);
-    int toff[2][DB];
+    for (int kk = 0; kk < DK; ++kk) {
+        const int o = t_off<D>(l32, 2 * kk + h);
+        qaddr[kk] = o + 32 * qh * ROWB;
+        kaddr[kk] = o + 32 * kg * ROWB + KOFF;
+    }
+    int toff[2][DB];                  // transposing reads: rows 32qh + 4h + s16/4 (+8)
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) {
         const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
         const int r0 = 4 * h + (s16 >> 2);
-        toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
-        toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+        toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
+        toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
     }
-    // fold this wave's row offsets into the lane offsets once, so that every
-    // read below is a register plus a compile-time immediate
-    const int kvo = 32 * kg * ROWB, qo = 32 * qh * ROWB;
-    int qaddr[DK], kaddr[DK];
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-        qaddr[kk] = roff[kk] + qo;
-        kaddr[kk] = roff[kk] + kvo;
-    }
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-        toff[0][cb] += qo;
-        toff[1][cb] += qo;
-    }
+    const int laddr = LOFF + (32 * qh + 4 * h) * 4;   // lse2 / D of this lane's rows
 
-    const float c = a.c;
-    const int kneg = a.negate ? (int)0x80008000 : 0;   // scale < 0: S from -K and |scale|
+    const float c = a.c;   // signed exponent unit: no maximum is tracked here
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb)
@@ -453,40 +440,38 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
             dv[cb][r] = 0.f;
         }
 
-    // This wave's 32 queries of a staged tile.  masked: the block straddles
-    // the causal diagonal of this wave's keys (one code path for both keeps
-    // the register footprint of a single copy).
-    auto block = [&](auto stg, bool masked, int i0) {
+    // This wave's 32 queries of a staged tile.  MASK: the block straddles
+    // the causal diagonal of this wave's keys (only the first two tiles of a
+    // key block can; they run before the main loop).
+    auto block = [&](auto stg, auto mask, int i0) {
         constexpr int STG = decltype(stg)::value;
-        const char* sQ = smem + 2 * KVB + STG * STAGE;
+        constexpr bool MASK = decltype(mask)::value;
+        const char* sQ = smem + STG * STAGE;
         const char* sG = sQ + TILE;
-        const float* sL = (const float*)(sQ + 2 * TILE);
-        const float* sD = sL + BQT;
         f32x16 s, dp;
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) {
             const i32x4 qx = *(const i32x4*)(sQ + qaddr[kk]);
-            const i32x4 kx = *(const i32x4*)(sKb + kaddr[kk]) ^ kneg;
+            const i32x4 kx = *(const i32x4*)(smem + kaddr[kk]);
             s = Elem<T>::mma(bit_cast<v8>(qx), bit_cast<v8>(kx), kk == 0 ? f32x16{} : s);
         }
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk) {
             const i32x4 gx = *(const i32x4*)(sG + qaddr[kk]);
-            const i32x4 vx = *(const i32x4*)(sVb + kaddr[kk]);
+            const i32x4 vx = *(const i32x4*)(smem + KVB + kaddr[kk]);
             dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vx), kk == 0 ? f32x16{} : dp);
         }
         // rows of this block held by the lane: 32 qh + 8(r/4) + 4h + r%4
         f32x16 p;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int li = 32 * qh + 8 * rr + 4 * h;
-            const f32x4 l4 = *(const f32x4*)(sL + li);
-            const f32x4 d4 = *(const f32x4*)(sD + li);
+            const f32x4 l4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + 32 * rr);
+            const f32x4 d4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rr + e;
                 float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
-                pv = (!masked || key <= i0 + li + e) ? pv : 0.f;
+                if (MASK) pv = (key <= i0 + 32 * qh + 8 * rr + 4 * h + e) ? pv : 0.f;
                 p[r] = pv;
                 s[r] = pv * (dp[r] - d4[e]);   // dS
             }
@@ -515,13 +500,13 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         }
     };
 
-    auto step = [&](auto stg, int t) {
+    auto step = [&](auto stg, auto mask, int t) {
         constexpr int STG = decltype(stg)::value;
         if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
         const int i0 = t * BQT;
         const int ib = i0 + 32 * qh;        // first query of this wave's rows
         const bool skip = ib >= N || (CAUSAL && ib + 31 < kw0);   // every query before every key
-        if (!skip) block(stg, CAUSAL && ib < kw0 + 31, i0);
+        if (!skip) block(stg, mask, i0);
         wait_vmem();
         __syncthreads();
     };
@@ -530,11 +515,16 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     wait_vmem();
     __syncthreads();
     int t = t0;
-    for (; t + 1 < ntiles; t += 2) {
-        step(IC<0>{}, t);
-        step(IC<1>{}, t + 1);
+    if (CAUSAL) {
+        // the key block spans queries kb0 .. kb0 + 127: tiles t0 and t0 + 1
+        if (t < ntiles) step(IC<0>{}, std::true_type{}, t++);
+        if (t < ntiles) step(IC<1>{}, std::true_type{}, t++);
     }
-    if (t < ntiles) step(IC<0>{}, t);
+    for (; t + 1 < ntiles; t += 2) {
+        step(IC<0>{}, std::false_type{}, t);
+        step(IC<1>{}, std::false_type{}, t + 1);
+    }
+    if (t < ntiles) step(IC<0>{}, std::false_type{}, t);
 
     // the two query halves of each key group: qh = 1 hands its partial sums
     // to qh = 0 through LDS ([kg][accumulator quad][lane] of 16 bytes)

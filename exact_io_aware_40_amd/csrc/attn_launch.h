@@ -39,9 +39,9 @@ struct BwdArgs {
                     // each padded to NP = round_up(N, 64) floats: [2][B*H][NP]
     int N;
     int BH;
-    float c;        // |scale| * log2(e)
+    float c;        // scale * log2(e) with its sign (magnitude at least FLT_MIN)
     float scale;    // the caller's scale (gradient factor)
-    int negate;
+    int negate;     // unused by the backward kernels
 };
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N);
