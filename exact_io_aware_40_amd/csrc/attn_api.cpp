@@ -105,7 +105,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.N = int(N);
     const int br = attn::fwd_block_rows();
     a.nqb = int((N + br - 1) / br);
-    const int64_t total = BH * a.nqb;
+    // causal: one workgroup per pair of query blocks (a heavy and a light one)
+    const int64_t total = BH * (causal ? (a.nqb + 1) / 2 : a.nqb);
     if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
     a.total = int(total);
     a.c = exponent_unit(scale);

@@ -51,6 +51,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                              0x00020000);
 }
 
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's 16 bytes, read at
 // byte offset `voff` of the buffer, land at lds_base + 16 l (lds_base must be
 // the same for the whole wave).  Completion is tracked by vmcnt.
@@ -58,9 +63,42 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds_base,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_base, 16, voff, 0, 0, 0);
 }
 
+// The same copy written as inline assembly.  The compiler then knows of no
+// copy into LDS in flight, so it does not make LDS reads wait for it (it
+// cannot tell which LDS bytes a copy writes, and before a transposing read it
+// would wait for every outstanding copy); the caller orders the copies
+// against the reads with wait_vmem_upto and barriers.  lds_base is an LDS
+// byte address, the same for the whole wave.  M0 is written here; nothing
+// else in the kernels that use this relies on it.
+__device__ __forceinline__ void dma16_async(__amdgpu_buffer_rsrc_t rs, unsigned lds_base, unsigned voff) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(lds_base), "v"(voff), "s"(rs)
+                     : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // Wait until this wave's outstanding vector-memory operations (including
 // direct-to-LDS copies) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order); expcnt and lgkmcnt are left alone.
+template <int N> __device__ __forceinline__ void wait_vmem_upto() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that does not wait for this wave's own memory operations
+// (copies still in flight stay in flight); the empty asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
 
 // Per-element-type pieces: operand vector types, the 32x32x16 product, and
 // round-to-nearest-even conversion of four floats.
@@ -76,6 +114,16 @@ template <> struct Elem<__bf16> {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ v4 cvt4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+    // two floats rounded to nearest even and packed into one dword
+    static __device__ __forceinline__ unsigned cvt2(float a, float b) {
+        const f32x2 x = {a, b};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
+    }
+    // acc + both elements of a packed pair (fp32 accumulation)
+    static __device__ __forceinline__ float sum2(unsigned pr, float acc) {
+        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), one, acc, false);
+    }
     // acc + x[0] + ... + x[7] of an 8-element operand (fp32 accumulation)
     static __device__ __forceinline__ float sum8(v8 x, float acc) {
         const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
@@ -95,6 +143,14 @@ template <> struct Elem<_Float16> {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ v4 cvt4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+    static __device__ __forceinline__ unsigned cvt2(float a, float b) {
+        const f32x2 x = {a, b};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(x, f16x2));
+    }
+    static __device__ __forceinline__ float sum2(unsigned pr, float acc) {
+        const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), one, acc, false);
+    }
     static __device__ __forceinline__ float sum8(v8 x, float acc) {
         const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
@@ -136,6 +192,42 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // 8-byte transposing LDS read at byte address `addr` of the LDS window.
 __device__ __forceinline__ i16x4 lds_read_tr16(const char* base, int addr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + addr));
+}
+
+// LDS reads written as inline assembly, for loops that also have
+// direct-to-LDS copies in flight: the compiler cannot tell that a
+// transposing read does not touch the copies' destination and would wait for
+// every outstanding copy before it.  The compiler does not count these reads
+// either, so their results may be used only after lds_wait_upto<n>(), with n
+// the number of LDS reads issued after them.  `addr` is a byte address in
+// LDS, `off` a constant below 65536 (it must fold to one after inlining).
+__device__ __forceinline__ i32x4 lds_read_b128_asm(unsigned addr, int off) {
+    i32x4 r;
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
+    return r;
+}
+__device__ __forceinline__ i32x2 lds_read_tr16_asm(unsigned addr, int off) {
+    i32x2 r;
+    __asm__ volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
+    return r;
+}
+// Wait until at most N LDS operations of this wave are outstanding; the six
+// registers passed are the results this makes safe to use (they are tied to
+// the wait so that no use is scheduled above it).
+template <int N>
+__device__ __forceinline__ void lds_wait_upto(i32x4& a, i32x4& b, i32x2& c, i32x2& d, i32x2& e,
+                                              i32x2& f) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+    __asm__ volatile("s_waitcnt lgkmcnt(%6)"
+                     : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f)
+                     : "i"(N));
+}
+
+// The same wait for three results (one 16-byte and two 8-byte reads).
+template <int N>
+__device__ __forceinline__ void lds_wait_upto(i32x4& a, i32x2& b, i32x2& c) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+    __asm__ volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "i"(N));
 }
 
 // Two 4-element pieces -> one 8-element operand.

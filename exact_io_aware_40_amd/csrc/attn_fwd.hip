@@ -1,25 +1,23 @@
 // attn_fwd.hip -- fused attention forward for gfx950.
 //
-// One workgroup owns one block of BR = 128 query rows of one (batch, head);
-// each of its four waves owns 32 of those rows for the whole kernel and
-// writes their output once ("FlashAttention" explainer, Step 3 "Tiling":
-// one Q block stays on chip while K/V tiles stream past, and each block's
-// output is written once).  K/V tiles of BC = 64 keys go straight from
-// global memory into one of two LDS stages (16-byte direct-to-LDS copies,
-// coalesced, zero-filled past the end of the sequence by the buffer bounds
-// check): tile t+1 is in flight while tile t is consumed, with one barrier
-// per tile.  Two workgroups share a CU, so one wave's softmax can overlap
-// another's matrix products.
+// One workgroup owns BR = 128 query rows of one (batch, head) -- under causal
+// masking a pair of such blocks, one after the other -- and streams the K/V
+// tiles those rows can see through LDS ("FlashAttention" explainer, Step 3
+// "Tiling": a Q block stays on chip while K/V tiles stream past, and each
+// block's output is written once).  Each of its four waves owns 32 of the
+// rows for the whole block; two workgroups share a CU, so every SIMD runs
+// two waves.  A tile holds 8 KiB of keys (32 keys at d = 128, 64 at d = 64).
 //
-// Per tile and wave (the pages' online softmax: "13% more FLOPs, 5.7x
-// faster", sections "Softmax is the anti-tiling operation" and
-// "FlashAttention's move: rescale the output, too"; explainer Step 4):
+// Per tile and wave (the pages' online softmax: sections "Softmax is the
+// anti-tiling operation" and "FlashAttention's move: rescale the output,
+// too"; explainer Step 4):
 //   S^T = K Q^T         on the matrix cores (keys x queries, fp32)
-//   mask                causal and ragged-tail tiles only
+//   mask                causal, ragged-tail and out-of-range tiles only
 //   m_t = rowmax S               lanes own query rows; one cross-lane step
 //   reference mc: the scaled running maximum, moved to m_t c only when
-//                 that exceeds it by more than kTau binades (the first
-//                 tile always moves it); alpha = 2^(mc_old - mc_new)
+//                 that exceeds it by more than kTau binades (32 for bf16
+//                 operands, 15 for fp16; the first tile always moves it);
+//                 alpha = 2^(mc_old - mc_new)
 //   P = 2^(S c - mc),  c = |scale| log2(e);  l = alpha l + rowsum P
 //   O^T = alpha O^T + V^T P^T    V^T read from the row-major tile with
 //                                transposing LDS reads
@@ -27,9 +25,22 @@
 // Any reference point gives the same O and lse (2^(x - m) = 2^(x - m')
 // 2^(m' - m), the identity behind the pages' rescale); keeping it within
 // kTau binades of the true maximum bounds P by 2^kTau, so nothing overflows,
-// and lets most tiles skip the rescale of the accumulator.
+// and lets almost every tile skip the rescale of the accumulator.
 // S and P exist only in registers; nothing of size N x N touches memory.
+//
+// Schedule.  Iteration t of a wave issues, interleaved: the softmax of tile
+// t (vector ALU), cut into pieces; the products for S of tile t+1 and for
+// P.V of tile t-1 (matrix cores), whose LDS operands are read four steps
+// ahead; and the direct-to-LDS copies of K(t+3) and V(t+1) into rings of
+// four buffers.  The copies and the operand reads are written as inline
+// assembly so that neither waits for the other (they never touch the same
+// buffer), with explicit waits where the data is consumed.  Every wave
+// walks every tile of its block: tiles past a wave's diagonal are masked
+// entirely and contribute exactly zero.
+#include <float.h>
+
 #include <type_traits>
+#include <utility>
 
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -37,28 +48,70 @@
 namespace attn {
 namespace {
 
-constexpr int BR = 128;   // query rows per workgroup
-constexpr int BC = 64;    // keys per K/V tile
-constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int QB = 1;             // 32-row query blocks per wave
+constexpr int NW = 4;             // waves per workgroup
+constexpr int BR = 32 * QB * NW;  // query rows per workgroup
+constexpr int NT = 64 * NW;       // threads per workgroup
+constexpr int OCC = 2;            // workgroups per CU
+// keys per K/V tile: 8 KiB tiles
+template <int D> constexpr int bc() { return 8192 / (2 * D); }
+// LDS buffers for K tiles, and as many for V tiles, within a workgroup's
+// share of the 160 KiB (an even count)
+constexpr int RING = ((160 * 1024 / OCC) / (2 * 8192)) & ~1;
+
 // The exponent's reference point moves only when a row's maximum rises by
-// more than kTau binades, so P <= 2^kTau and most tiles skip the rescale.
-constexpr float kTau = 8.f;
+// more than kTau binades, so P <= 2^kTau and most tiles skip the rescale of
+// the accumulator.  The bound keeps P representable in the operand type
+// (fp16 holds up to 65504 < 2^16) and far below fp32's range for O and l.
+template <typename T> constexpr float kTau = 32.f;
+template <> constexpr float kTau<_Float16> = 15.f;
 
 template <int V> using IC = std::integral_constant<int, V>;
 
+// f(IC<0>), f(IC<1>), ... while f returns true.
+template <typename F, int... I>
+__device__ __forceinline__ bool for_ring(F& f, std::integer_sequence<int, I...>) {
+    return (f(IC<I>{}) && ...);
+}
+
+// lds_wait_upto<3 K> for a K in 0..KMAX known only after unrolling.
+template <int KMAX> struct WaitSel3 {
+    static __device__ __forceinline__ void run(int k, i32x4& a, i32x2& b, i32x2& c) {
+        if (k >= KMAX) lds_wait_upto<3 * KMAX>(a, b, c);
+        else WaitSel3<KMAX - 1>::run(k, a, b, c);
+    }
+};
+template <> struct WaitSel3<0> {
+    static __device__ __forceinline__ void run(int, i32x4& a, i32x2& b, i32x2& c) { lds_wait_upto<0>(a, b, c); }
+};
+
+// An empty use of a register value: it must be computed at this point of
+// the program (the compiler would otherwise sink work past later branches).
+template <typename V> __device__ __forceinline__ void materialize(const V& x) {
+    __asm__ volatile("" ::"v"(x));
+}
+
 template <typename T, typename TO, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     typedef typename Elem<T>::v8 v8;
+    constexpr int BC = bc<D>();
+    static_assert(RING >= 4, "the pipeline needs four buffers per tensor");
+    constexpr int KLEAD = RING - 1;   // iteration t starts the copy of K(t + KLEAD) ...
+    constexpr int VLEAD = RING - 3;   // ... and of V(t + VLEAD)
     constexpr int ROWB = D * 2;            // bytes per tile row
     constexpr int GR = D / 8;              // 16-byte granules per row
     constexpr int TILE = BC * ROWB;        // bytes of one K (or V) tile
-    constexpr int LOADS = TILE / (NT * 16);  // copies per thread per tile and tensor
+    constexpr int LOADS = TILE / (NT * 16);  // 16-byte loads per thread per tile and tensor
+    static_assert(LOADS * NT * 16 == TILE, "a tile splits evenly over the workgroup");
     constexpr int KB = BC / 32;            // 32-key blocks per tile
     constexpr int DK = D / 16;             // k-steps of the S product
     constexpr int DB = D / 32;             // 32-wide output column blocks
+    constexpr int NF = KB * DK;            // K fragments per tile (and as many V fragments)
+    static_assert(NF == DB * KB * 2, "");
+    constexpr int NMM = 2 * QB * NF;       // products per iteration
 
-    // [stage][K | V][tile]
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+    // K ring (RING tiles), then V ring (RING tiles)
+    __shared__ __attribute__((aligned(1024))) char smem[2 * RING * TILE];
 
     const int N = a.N;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -66,218 +119,349 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
 
+    // Work: one query block of one (batch, head); under causal masking the
+    // pair of blocks nqb-1-p and p of one head, one after the other, so that
+    // every workgroup streams about as many tiles as any other (heavy and
+    // light blocks together) and the grid has no tail of heavy blocks.
     const int L = xcd_remap(blockIdx.x, a.total);
-    const int bh = L / a.nqb;
-    int qb = L - bh * a.nqb;
-    if (CAUSAL) qb = a.nqb - 1 - qb;  // heaviest query blocks first
-    const int q0 = qb * BR;
-    const size_t head = (size_t)bh * N * D;
-    const T* __restrict__ Qh = (const T*)a.q + head;
-    const unsigned head_bytes = (unsigned)N * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
-
-    // This lane's query row and its Q fragment (B operand of S^T = K Q^T).
-    const int qlo = q0 + 32 * w;
-    const int qrow = qlo + l32;
-    i32x4 qf[DK];
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-        i32x4 x = {0, 0, 0, 0};
-        if (qrow < N) x = *(const i32x4*)(Qh + (size_t)qrow * D + 16 * kk + 8 * h);
-        if (a.negate) x ^= (int)0x80008000;   // scale < 0: use -Q and |scale|
-        qf[kk] = x;
+    int bh, qb_items[2], nitems = 1;
+    if (CAUSAL) {
+        const int npairs = (a.nqb + 1) >> 1;
+        bh = L / npairs;
+        const int p = L - bh * npairs;
+        qb_items[0] = a.nqb - 1 - p;
+        qb_items[1] = p;
+        nitems = p != a.nqb - 1 - p ? 2 : 1;
+    } else {
+        bh = L / a.nqb;
+        qb_items[0] = L - bh * a.nqb;
     }
+    for (int item = 0; item < nitems; ++item) {
+        const int qb = qb_items[item];
+        const int q0 = qb * BR;
+        const size_t head = (size_t)bh * N * D;
+        const T* __restrict__ Qh = (const T*)a.q + head;
+        const unsigned head_bytes = (unsigned)N * ROWB;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
 
-    const int kend = CAUSAL ? min(N, q0 + BR) : N;
-    const int ntiles = (kend + BC - 1) / BC;
-
-    // K and V tiles have separate double buffers: K runs one tile ahead of V,
-    // because the products S = K Q^T for tile t+1 are issued while tile t's
-    // exponents and P.V products run.  Copy p of this thread fills LDS slot
-    // (p*4 + w)*64 + lane of a tile: row `row`, physical granule pg, which
-    // holds logical granule pg ^ key(row) of that row (the t_off placement).
-    unsigned src_off[LOADS];
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-        const int slot = (p * 4 + w) * 64 + lane;
-        const int row = slot / GR, pg = slot % GR;
-        src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
-    }
-    // smem: K slot 0, K slot 1, V slot 0, V slot 1.  Copies of tiles past
-    // the end of the sequence read zeros and are never consumed.
-    auto issue = [&](auto which, auto slot, int t) {
-        char* st = smem + (decltype(which)::value * 2 + decltype(slot)::value) * TILE;
-        const __amdgpu_buffer_rsrc_t rs = decltype(which)::value ? vrs : krs;
-        const unsigned base = (unsigned)t * TILE;
-#pragma unroll
-        for (int p = 0; p < LOADS; ++p) dma16(rs, st + (p * 4 + w) * 1024, base + src_off[p]);
-    };
-
-    // Loop-invariant LDS offsets of this lane's operand reads; the block,
-    // half-tile and slot parts are added as immediates (the swizzle key
-    // depends on the row modulo 16 only).
-    int koff[DK];
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) koff[kk] = t_off<D>(l32, 2 * kk + h);
-    int voff[2][DB];
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-        const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-        const int r0 = 4 * h + (s16 >> 2);
-        voff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
-        voff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
-    }
-
-    const float c = a.c;   // > 0 (the host maps a zero scale to the smallest normal unit)
-    f32x16 oacc[DB];
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    float mc_run = -INFINITY;   // exponent reference (scaled units) of this row
-    // this lane's share of the row's normaliser, twice: the sum of P as
-    // rounded for the P.V product (it normalises O, so O's weights sum to
-    // one exactly as used) and the fp32 sum of P (it gives lse)
-    float l_run = 0.f, lf_run = 0.f;
-
-    // S^T = K Q^T for a whole tile (every 32-key block; blocks a wave cannot
-    // see are masked to -inf afterwards and then contribute exactly zero).
-    auto scores = [&](auto kslot, f32x16 (&s)[KB]) {
-        const char* sK = smem + decltype(kslot)::value * TILE;
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
+        // This lane's query rows and their Q fragments (B operands of S^T = K Q^T).
+        const int qlo = q0 + 32 * QB * w;
+        int qrow[QB];
+        i32x4 qf[QB][DK];
+    #pragma unroll
+        for (int r = 0; r < QB; ++r) {
+            qrow[r] = qlo + 32 * r + l32;
+    #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                const i32x4 kx = *(const i32x4*)(sK + koff[kk] + 32 * b * ROWB);
-                s[b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s[b]);
-            }
-    };
-
-    // Mask tile j0's scores if needed, then move the row's reference when
-    // its maximum rose by more than kTau binades; rescale l and O by the
-    // factor (O already holds every earlier tile's P.V).
-    auto rowmax_update = [&](f32x16 (&s)[KB], int j0) {
-        const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
-        if (need_mask) [[unlikely]] {
-#pragma unroll
-            for (int b = 0; b < KB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool ok = key < N && (!CAUSAL || key <= qrow);
-                    s[b][r] = ok ? s[b][r] : -INFINITY;
-                }
-        }
-        float mt = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[b][r], s[b][r + 1]));
-        const float tc = max32(mt) * c;
-        const bool upd = tc > mc_run + kTau;
-        const float mc = upd ? tc : mc_run;
-        const float alpha = upd ? fast_exp2(mc_run - mc) : 1.f;
-        mc_run = mc;
-        l_run *= alpha;
-        lf_run *= alpha;
-        if (__ballot(upd) != 0) [[unlikely]] {
-#pragma unroll
-            for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        }
-    };
-
-    // P = 2^(S c - mc) for a tile whose reference is settled, packed to the
-    // operand type, and O^T += V^T P^T.  B operand chunk (b, q) holds, at
-    // k = 8h + e, the probability of key 32b + 16q + 8(e/4) + 4h + e%4; the
-    // transposing reads fetch V at exactly those keys.
-    auto exp_pv = [&](auto vslot, f32x16 (&s)[KB]) {
-        const char* sV = smem + (2 + decltype(vslot)::value) * TILE;
-        const float mc = mc_run;
-        float lsum = 0.f, lfsum = 0.f;
-        v8 pb[KB][2];
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[b][r] = fast_exp2(fmaf(s[b][r], c, -mc));
-                lfsum += s[b][r];
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const f32x4 lo = {s[b][8 * q + 0], s[b][8 * q + 1], s[b][8 * q + 2], s[b][8 * q + 3]};
-                const f32x4 hi = {s[b][8 * q + 4], s[b][8 * q + 5], s[b][8 * q + 6], s[b][8 * q + 7]};
-                const auto l4 = Elem<T>::cvt4(lo);
-                const auto h4 = Elem<T>::cvt4(hi);
-                pb[b][q] = __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
-                lsum = Elem<T>::sum8(pb[b][q], lsum);
+                i32x4 x = {0, 0, 0, 0};
+                if (qrow[r] < N) x = *(const i32x4*)(Qh + (size_t)qrow[r] * D + 16 * kk + 8 * h);
+                if (a.negate) x ^= (int)0x80008000;   // scale < 0: use -Q and |scale|
+                    qf[r][kk] = x;
             }
         }
-        l_run += lsum;
-        lf_run += lfsum;
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-            for (int b = 0; b < KB; ++b)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int roff = (32 * b + 16 * q) * ROWB;
-                    const i16x4 lo = lds_read_tr16(sV, voff[0][cb] + roff);
-                    const i16x4 hi = lds_read_tr16(sV, voff[1][cb] + roff);
-                    oacc[cb] = Elem<T>::mma(join8<v8>(lo, hi), pb[b][q], oacc[cb]);
-                }
-    };
 
-    // Iteration t: K(t+2) and V(t+1) copies start; S for tile t+1 (its K
-    // arrived one iteration ago) is issued while tile t's exponents and
-    // P.V products run; then tile t+1's mask, row maximum and reference.
-    // Invariant at the top: tile t's scores are in `cur`, K(t+1) and V(t)
-    // are in LDS, and no wave still reads K(t)'s slot.
-    auto step = [&](auto par, int t, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
-        constexpr int P = decltype(par)::value;   // t % 2
-        issue(IC<0>{}, IC<P>{}, t + 2);
-        issue(IC<1>{}, IC<1 - P>{}, t + 1);
-        scores(IC<1 - P>{}, nxt);
-        exp_pv(IC<P>{}, cur);
-        if (t + 1 < ntiles) rowmax_update(nxt, (t + 1) * BC);
-        wait_vmem();
-        __syncthreads();
-    };
+        const int kend = CAUSAL ? min(N, q0 + BR) : N;
+        const int ntiles = (kend + BC - 1) / BC;   // tiles the workgroup streams
 
-    f32x16 sA[KB], sB[KB];
-    issue(IC<0>{}, IC<0>{}, 0);
-    issue(IC<1>{}, IC<0>{}, 0);
-    issue(IC<0>{}, IC<1>{}, 1);
-    wait_vmem();
-    __syncthreads();
-    scores(IC<0>{}, sA);
-    rowmax_update(sA, 0);
-    __syncthreads();   // every wave is done with K(0)'s slot
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-        step(IC<0>{}, t, sA, sB);
-        step(IC<1>{}, t + 1, sB, sA);
-    }
-    if (t < ntiles) step(IC<0>{}, t, sA, sB);
-
-    // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
-    const float l_tot = sum32(l_run);
-    const float lf_tot = sum32(lf_run);
-    const float inv = fast_rcp(l_tot);
-    if (qrow < N) {
-        TO* __restrict__ orow = (TO*)a.o + head + (size_t)qrow * D;
-#pragma unroll
+        // Copy p of this thread fills LDS slot (p*4 + w)*64 + lane of a tile:
+        // row `row`, physical granule pg, which holds logical granule
+        // pg ^ key(row) of that row (the t_off placement).
+        unsigned src_off[LOADS];
+    #pragma unroll
+        for (int p = 0; p < LOADS; ++p) {
+            const int slot = (p * NW + w) * 64 + lane;
+            const int row = slot / GR, pg = slot % GR;
+            src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
+        }
+        // Copies of tiles past the end of the streamed range start past the end
+        // of the buffer: they read zeros and cost no memory traffic.
+        const unsigned sbase = lds_addr(smem) + w * 1024;
+        auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int t, int buf) __attribute__((always_inline)) {
+            const unsigned base = t < ntiles ? (unsigned)t * TILE : head_bytes;
+    #pragma unroll
+            for (int p = 0; p < LOADS; ++p) dma16_async(rs, sbase + buf * TILE + p * NW * 1024, base + src_off[p]);
+        };
+        // Loop-invariant LDS addresses of this lane's operand reads (those of V
+        // include the V ring's base); the block, half-tile and buffer parts are
+        // added as immediates (the swizzle key depends on the row modulo 16 only).
+        int koff[DK];
+    #pragma unroll
+        for (int kk = 0; kk < DK; ++kk) koff[kk] = t_off<D>(l32, 2 * kk + h);
+        int voff[2][DB];
+    #pragma unroll
         for (int cb = 0; cb < DB; ++cb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 x = {oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv,
-                           oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv};
-                store4<TO>(orow + 32 * cb + 8 * g + 4 * h, x);
+            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+            const int r0 = 4 * h + (s16 >> 2);
+            voff[0][cb] = RING * TILE + t_off<D>(r0, col >> 3) + (col & 7) * 2;
+            voff[1][cb] = RING * TILE + t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+        }
+
+        const float c = a.c;   // > 0 (the host maps a zero scale to the smallest normal unit)
+        f32x16 oacc[QB][DB];
+    #pragma unroll
+        for (int r = 0; r < QB; ++r)
+    #pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[r][cb][e] = 0.f;
+        // per row: exponent reference (scaled units), and this lane's share of
+        // the row's normaliser twice: the sum of P as rounded for the P.V product
+        // (it normalises O, so O's weights sum to one exactly as used) and the
+        // fp32 sum of P (it gives lse)
+        float mc_run[QB], l_run[QB], lf_run[QB];
+        // (the reference starts at the lowest finite value: the first tile, whose
+        // key 0 every row sees, always moves it, with alpha = 0)
+    #pragma unroll
+        for (int r = 0; r < QB; ++r) mc_run[r] = -FLT_MAX, l_run[r] = 0.f, lf_run[r] = 0.f;
+
+        typedef f32x16 Scores[QB][KB];   // S^T of one tile, per row block and 32-key block
+        typedef v8 Probs[QB][KB][2];     // P of one tile packed as B operands
+
+        // S^T = K Q^T for the tile in K buffer kb_, row blocks accumulated from
+        // each K fragment in turn.
+        auto s_frag = [&](int kbuf, int i, Scores& sn) __attribute__((always_inline)) {
+            const int b = i % KB, kk = i / KB;
+            const i32x4 kx = *(const i32x4*)(smem + kbuf * TILE + koff[kk] + 32 * b * ROWB);
+    #pragma unroll
+            for (int r = 0; r < QB; ++r)
+                sn[r][b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[r][kk]), kk == 0 ? f32x16{} : sn[r][b]);
+        };
+        // Scores of keys a row may not see (causal, past the end of the
+        // sequence, or past the workgroup's range) become -inf.
+        auto apply_mask = [&](Scores& sc, int j0) __attribute__((always_inline)) {
+    #pragma unroll
+            for (int r = 0; r < QB; ++r)
+    #pragma unroll
+                for (int b = 0; b < KB; ++b)
+    #pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = j0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3);
+                        const bool ok = key < N && (!CAUSAL || key <= qrow[r]);
+                        sc[r][b][e] = ok ? sc[r][b][e] : -INFINITY;
+                    }
+        };
+
+        Scores sA, sB;
+        Probs pA, pB;
+    #pragma unroll
+        for (int r = 0; r < QB; ++r)
+    #pragma unroll
+            for (int b = 0; b < KB; ++b)
+    #pragma unroll
+                for (int q = 0; q < 2; ++q) pA[r][b][q] = v8{};
+
+        // An iteration runs in NF steps; step k reads K fragment k and V
+        // fragment k and issues 2 QB products: per row block, one of S (for the
+        // next tile) and one of P.V (for the previous tile).  Fragments are read
+        // DIST steps ahead by inline assembly and waited for explicitly.  The
+        // softmax of the current tile is cut into pieces, placed between the
+        // products; scheduling fences keep every piece in its slot.
+        constexpr int DIST = QB == 1 ? 4 : 3;
+        struct Frag {
+            i32x4 k;
+            i32x2 v0, v1;
+        };
+        const unsigned lbase = lds_addr(smem);
+        unsigned kaddr[DK];
+    #pragma unroll
+        for (int kk = 0; kk < DK; ++kk) kaddr[kk] = lbase + koff[kk];
+        unsigned vaddr[2][DB];
+    #pragma unroll
+        for (int cb = 0; cb < DB; ++cb) vaddr[0][cb] = lbase + voff[0][cb], vaddr[1][cb] = lbase + voff[1][cb];
+        auto load_frag = [&](int kbuf, int vbuf, int k, Frag& f) __attribute__((always_inline)) {
+            const int b = k % KB, kk = k / KB;
+            f.k = lds_read_b128_asm(kaddr[kk], kbuf * TILE + 32 * b * ROWB);
+            const int cb = k % DB, jj = k / DB, bv = jj >> 1, q = jj & 1;
+            const int roff = vbuf * TILE + (32 * bv + 16 * q) * ROWB;
+            f.v0 = lds_read_tr16_asm(vaddr[0][cb], roff);
+            f.v1 = lds_read_tr16_asm(vaddr[1][cb], roff);
+        };
+        // product m of step k: row block r = m / 2, S for even m, P.V for odd m.
+        // B operand chunk (b, q) of P holds, at k = 8h + e, the probability of
+        // key 32b + 16q + 8(e/4) + 4h + e%4; the transposing reads fetch V at
+        // exactly those keys.
+        auto product = [&](int k, int m, const Frag& f, Scores& sn, const Probs& pp) __attribute__((always_inline)) {
+            const int r = m >> 1;
+            if ((m & 1) == 0) {
+                const int b = k % KB, kk = k / KB;
+                sn[r][b] = Elem<T>::mma(bit_cast<v8>(f.k), bit_cast<v8>(qf[r][kk]), kk == 0 ? f32x16{} : sn[r][b]);
+            } else {
+                const int cb = k % DB, jj = k / DB, bv = jj >> 1, q = jj & 1;
+                const i32x4 vx = __builtin_shufflevector(f.v0, f.v1, 0, 1, 2, 3);
+                oacc[r][cb] = Elem<T>::mma(bit_cast<v8>(vx), pp[r][bv][q], oacc[r][cb]);
+            }
+        };
+
+        // Softmax of one tile, as pieces p = 0 .. NP-1 (row block p % QB):
+        // row maximum over 8 scores (2 KB pieces); the reference, alpha and the
+        // flag for the rescale of O (1); two probabilities, their fp32 sum, their
+        // packed pair and its sum as rounded (8 KB pieces); the row's running
+        // sums (1).  The reference moves when the row maximum rose by more than
+        // kTau binades; alpha is the factor for the older accumulation (1 when
+        // it stays).
+        constexpr int NP_ROW = 10 * KB + 2;
+        constexpr int NP = QB * NP_ROW;
+        float st_mt[QB], st_alpha[QB], st_ls[QB], st_lfs[QB];
+        unsigned pw[QB][KB][2][4];
+        auto piece = [&](int p, Scores& sc, bool& upd_any) __attribute__((always_inline)) {
+            const int r = p % QB, sx = p / QB;
+            if (sx < 2 * KB) {
+                const int b = sx >> 1, e0 = 8 * (sx & 1);
+                float m = (sx == 0) ? fmaxf(sc[r][b][e0], sc[r][b][e0 + 1])
+                                    : fmaxf(st_mt[r], fmaxf(sc[r][b][e0], sc[r][b][e0 + 1]));
+    #pragma unroll
+                for (int e = 2; e < 8; e += 2) m = fmaxf(m, fmaxf(sc[r][b][e0 + e], sc[r][b][e0 + e + 1]));
+                st_mt[r] = m;
+            } else if (sx == 2 * KB) {
+                const float tc = max32(st_mt[r]) * c;
+                const bool upd = tc > mc_run[r] + kTau<T>;
+                const float mc = upd ? tc : mc_run[r];
+                st_alpha[r] = fast_exp2(mc_run[r] - mc);   // 1 when the reference stays
+                // O needs the factor only once it holds something: before the
+                // first tile it is zero (and alpha is 0)
+                upd_any |= upd && mc_run[r] != -FLT_MAX;
+                mc_run[r] = mc;
+                st_ls[r] = 0.f;
+                st_lfs[r] = 0.f;
+            } else if (sx < 10 * KB + 1) {
+                const int q = sx - 2 * KB - 1, b = q / 8, e = 2 * (q % 8);
+                const float x0 = fast_exp2(fmaf(sc[r][b][e], c, -mc_run[r]));
+                const float x1 = fast_exp2(fmaf(sc[r][b][e + 1], c, -mc_run[r]));
+                st_lfs[r] += x0;
+                st_lfs[r] += x1;
+                const unsigned pr = Elem<T>::cvt2(x0, x1);
+                st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
+                pw[r][b][e / 8][(e % 8) / 2] = pr;
+            } else {
+                l_run[r] = l_run[r] * st_alpha[r] + st_ls[r];
+                lf_run[r] = lf_run[r] * st_alpha[r] + st_lfs[r];
+            }
+        };
+
+        // Iteration t (t = 0 .. ntiles): copies of K(t+KLEAD) and V(t+VLEAD)
+        // start, into K buffer (t-1)%RING and V buffer (t-3)%RING, which last
+        // held K(t-1) and V(t-3), read in iteration t-2 at the latest; softmax of
+        // tile t (scores in sc, P to pc), S of tile t+1 (to sn, K buffer
+        // (t+1)%RING), P.V of tile t-1 (P in pp, V buffer (t-1)%RING; for t = 0
+        // both are zero); then this wave waits for its copies of K(t+2) and V(t),
+        // started in iteration t+2-KLEAD, and a barrier makes every wave's copies
+        // visible to iteration t+1, which reads them.  Tile ntiles is all masked
+        // and its P is zero.
+        constexpr int INFLIGHT = (KLEAD - 2) * 2 * LOADS;   // copies younger than those waited for
+        static_assert(KLEAD - 2 == VLEAD, "K and V copies of one iteration are waited for together");
+        static_assert(INFLIGHT < 64, "vmcnt is six bits");
+        auto iter = [&](auto J, int t, Scores& sc, Scores& sn, Probs& pp, Probs& pc) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;   // t % RING
+            const int j0 = t * BC;
+            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
+            float alpha[QB];
+            bool upd_any;
+            issue(krs, t + KLEAD, (j + KLEAD) % RING);
+            issue(vrs, t + VLEAD, RING + (j + VLEAD) % RING);
+            if (need_mask) [[unlikely]] apply_mask(sc, j0);
+            upd_any = false;
+            {
+                constexpr int kbuf = (j + 1) % RING, vbuf = (j + RING - 1) % RING;
+                constexpr int NS = 2 * QB;   // products per step
+                Frag f[DIST + 1];
+    #pragma unroll
+                for (int k = 0; k < DIST; ++k) load_frag(kbuf, vbuf, k, f[k]);
+    #pragma unroll
+                for (int k = 0; k < NF; ++k) {
+                    Frag& cur = f[k % (DIST + 1)];
+                    const int later = min(DIST - 1, NF - 1 - k);   // steps read after this one
+                    WaitSel3<DIST - 1>::run(later, cur.k, cur.v0, cur.v1);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int m = 0; m < NS; ++m) {
+                        const int slot = k * NS + m;
+                        product(k, m, cur, sn, pp);
+                        if (m == 0 && k + DIST < NF) load_frag(kbuf, vbuf, k + DIST, f[(k + DIST) % (DIST + 1)]);
+    #pragma unroll
+                        for (int p = slot * NP / NMM; p < (slot + 1) * NP / NMM; ++p) piece(p, sc, upd_any);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+    #pragma unroll
+            for (int r = 0; r < QB; ++r) {
+                alpha[r] = st_alpha[r];
+    #pragma unroll
+                for (int b = 0; b < KB; ++b)
+    #pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const i32x4 x = {(int)pw[r][b][q][0], (int)pw[r][b][q][1], (int)pw[r][b][q][2], (int)pw[r][b][q][3]};
+                        pc[r][b][q] = bit_cast<v8>(x);
+                        materialize(pc[r][b][q]);
+                    }
+            }
+            if (__ballot(upd_any) != 0) [[unlikely]] {
+    #pragma unroll
+                for (int r = 0; r < QB; ++r)
+    #pragma unroll
+                    for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+                        for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha[r];
+            }
+            wait_vmem_upto<INFLIGHT>();
+            barrier_only();
+        };
+
+        // Prologue: copies of K(0), K(1), then K(t+KLEAD) and V(t+VLEAD) in the
+        // order iterations t = -VLEAD .. -1 would start them; V buffer RING-1
+        // (read as "tile -1" with P = 0) cleared so that it holds finite values;
+        // S of tile 0.
+        issue(krs, 0, 0);
+        issue(krs, 1, 1);
+    #pragma unroll
+        for (int t = -VLEAD; t < 0; ++t) {
+            issue(krs, t + KLEAD, t + KLEAD);
+            issue(vrs, t + VLEAD, RING + t + VLEAD);
+        }
+    #pragma unroll
+        for (int p = 0; p < LOADS; ++p)
+            *(i32x4*)(smem + (2 * RING - 1) * TILE + (p * NW + w) * 1024 + 16 * lane) = i32x4{0, 0, 0, 0};
+        wait_vmem_upto<INFLIGHT>();   // Q, K(0) and K(1)
+        __syncthreads();
+    #pragma unroll
+        for (int i = 0; i < NF; ++i) s_frag(0, i, sA);
+
+        // iterations in groups of RING (buffer indices are constants); scores and
+        // probabilities alternate between the A and B sets
+        int t = 0;
+        auto one = [&](auto J) __attribute__((always_inline)) {
+            if constexpr (decltype(J)::value % 2 == 0) iter(J, t, sA, sB, pA, pB);
+            else iter(J, t, sB, sA, pB, pA);
+            return ++t <= ntiles;
+        };
+        while (for_ring(one, std::make_integer_sequence<int, RING>{})) {
+        }
+        wait_vmem();   // no copy may still be writing LDS when the workgroup ends
+
+        // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
+    #pragma unroll
+        for (int r = 0; r < QB; ++r) {
+            const float l_tot = sum32(l_run[r]);
+            const float lf_tot = sum32(lf_run[r]);
+            const float inv = fast_rcp(l_tot);
+            if (qrow[r] < N) {
+                TO* __restrict__ orow = (TO*)a.o + head + (size_t)qrow[r] * D;
+    #pragma unroll
+                for (int cb = 0; cb < DB; ++cb) {
+    #pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) {
+                        f32x4 x = {oacc[r][cb][4 * gg] * inv, oacc[r][cb][4 * gg + 1] * inv,
+                                   oacc[r][cb][4 * gg + 2] * inv, oacc[r][cb][4 * gg + 3] * inv};
+                        store4<TO>(orow + 32 * cb + 8 * gg + 4 * h, x);
+                    }
+                }
+                if (h == 0) a.lse[(size_t)bh * N + qrow[r]] = (mc_run[r] + fast_log2(lf_tot)) * 0.69314718055994531f;
             }
         }
-        if (h == 0) a.lse[(size_t)bh * N + qrow] = (mc_run + fast_log2(lf_tot)) * 0.69314718055994531f;
+        // the next item reuses the LDS buffers (this wave's copies have
+        // drained; the barrier waits for every other wave's reads)
+        if (item + 1 < nitems) __syncthreads();
     }
 }
 

@@ -17,7 +17,7 @@ struct FwdArgs {
     float* lse;
     int N;        // sequence length
     int nqb;      // query blocks per (batch, head)
-    int total;    // workgroups = B * H * nqb
+    int total;    // workgroups: B * H * nqb, or B * H * ceil(nqb / 2) under causal masking
     float c;      // |scale| * log2(e): exponent units of the kernel
     int negate;   // scale < 0: the kernel multiplies Q by -1 (exact)
 };
