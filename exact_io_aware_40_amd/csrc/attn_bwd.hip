@@ -208,8 +208,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
         const unsigned base = (unsigned)t * TILE;
 #pragma unroll
         for (int p = 0; p < LOADS; ++p) {
-            dma16(krs, st + (p * 4 + w) * 1024, base + src_off[p]);
-            dma16(vrs, st + TILE + (p * 4 + w) * 1024, base + src_off[p]);
+            dma16_async(krs, lds_addr(st + (p * 4 + w) * 1024), base + src_off[p]);
+            dma16_async(vrs, lds_addr(st + TILE + (p * 4 + w) * 1024), base + src_off[p]);
         }
     };
 
@@ -384,8 +384,8 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     for (int p = 0; p < KLOADS; ++p) {
         const int slot = (p * 8 + w) * 64 + lane;
         const unsigned off = (unsigned)kb0 * ROWB + src_of(slot);
-        dma16(krs, smem + KOFF + (p * 8 + w) * 1024, off);
-        dma16(vrs, smem + KOFF + KVB + (p * 8 + w) * 1024, off);
+        dma16_async(krs, lds_addr(smem + KOFF + (p * 8 + w) * 1024), off);
+        dma16_async(vrs, lds_addr(smem + KOFF + KVB + (p * 8 + w) * 1024), off);
     }
 
     const int t0 = CAUSAL ? kb0 / BQT : 0;
@@ -400,14 +400,14 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         const unsigned base = (unsigned)t * TILE;
 #pragma unroll
         for (int p = 0; p < TLOADS; ++p) {
-            dma16(qrs, st + (p * 8 + w) * 1024, base + tsrc[p]);
-            dma16(grs, st + TILE + (p * 8 + w) * 1024, base + tsrc[p]);
+            dma16_async(qrs, lds_addr(st + (p * 8 + w) * 1024), base + tsrc[p]);
+            dma16_async(grs, lds_addr(st + TILE + (p * 8 + w) * 1024), base + tsrc[p]);
         }
         // the tile's lse2 and D values: 64 floats each, 16 lanes of wave 0
         if (w == 0 && lane < BQT / 4) {
             const unsigned fo = (unsigned)(t * BQT + 4 * lane) * 4;
-            dma16(lrs, smem + LOFF + STG * 2 * BQT * 4, fo);
-            dma16(drs, smem + LOFF + STG * 2 * BQT * 4 + BQT * 4, fo);
+            dma16_async(lrs, lds_addr(smem + LOFF + STG * 2 * BQT * 4), fo);
+            dma16_async(drs, lds_addr(smem + LOFF + STG * 2 * BQT * 4 + BQT * 4), fo);
         }
     };
 

@@ -75,7 +75,7 @@ __device__ __forceinline__ void dma16_async(__amdgpu_buffer_rsrc_t rs, unsigned 
 #pragma clang diagnostic ignored "-Winline-asm"
     __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :
-                     : "s"(lds_base), "v"(voff), "s"(rs)
+                     : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rs)
                      : "memory", "m0");
 #pragma clang diagnostic pop
 }
