@@ -445,8 +445,12 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             const float l_tot = sum32(l_run[r]);
             const float lf_tot = sum32(lf_run[r]);
             const float inv = fast_rcp(l_tot);
-            if (qrow[r] < N) {
-                TO* __restrict__ orow = (TO*)a.o + head + (size_t)qrow[r] * D;
+            // (the row index passes through an empty asm statement so that
+            // its 64-bit offset is formed here, not kept live through the loop)
+            int qr = qrow[r];
+            __asm__ volatile("" : "+v"(qr));
+            if (qr < N) {
+                TO* __restrict__ orow = (TO*)a.o + head + (size_t)qr * D;
     #pragma unroll
                 for (int cb = 0; cb < DB; ++cb) {
     #pragma unroll
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                         store4<TO>(orow + 32 * cb + 8 * gg + 4 * h, x);
                     }
                 }
-                if (h == 0) a.lse[(size_t)bh * N + qrow[r]] = (mc_run[r] + fast_log2(lf_tot)) * 0.69314718055994531f;
+                if (h == 0) a.lse[(size_t)bh * N + qr] = (mc_run[r] + fast_log2(lf_tot)) * 0.69314718055994531f;
             }
         }
         // the next item reuses the LDS buffers (this wave's copies have

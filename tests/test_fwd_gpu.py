@@ -63,6 +63,16 @@ def test_several_tiles_and_blocks(dtype, causal):
     run_and_compare(q, k, v, causal, 1 / math.sqrt(128), "multi-block")
 
 
+@pytest.mark.parametrize("N", [640, 641, 1024])
+def test_causal_block_pairs(N):
+    """Causal workgroups take a heavy and a light query block of one head:
+    an odd number of blocks leaves the middle one alone (640, 641), an even
+    number pairs them all (1024); several heads and batches check the mapping
+    from workgroup to (batch, head, pair)."""
+    q, k, v = (randn((2, 3, N, 64), torch.bfloat16, 130 + i) for i in range(3))
+    run_and_compare(q, k, v, True, 1 / math.sqrt(64), f"pairs N={N}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.9])
 def test_zero_negative_and_large_scale(scale):
     q, k, v = (randn((1, 2, 200, 64), torch.float16, 60 + i) for i in range(3))
