@@ -6,11 +6,11 @@ computation runs in the library's HIP kernels.  torch supplies device
 memory and the current stream.
 
 Low level (same names and argument order as the C ABI, raw integers and
-device pointers):  :func:`attn_fwd`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
-:func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`,
-:func:`attn_status_str`.
+device pointers):  :func:`attn_fwd`, :func:`attn_fwd_split`,
+:func:`attn_fwd_split_workspace_size`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
+:func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`, :func:`attn_status_str`.
 
-Tensor level:  :func:`forward` and :func:`backward`.
+Tensor level:  :func:`forward`, :func:`forward_split` and :func:`backward`.
 """
 from __future__ import annotations
 
@@ -22,9 +22,10 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
+    "attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_size",
+    "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
     "attn_status_str",
-    "forward", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
+    "forward", "forward_split", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
 ]
 
 ATTN_F16 = 0
@@ -63,6 +64,10 @@ def _load():
                              ctypes.c_size_t)
     lib.attn_fwd.restype = i32
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_fwd_split_workspace_size.restype = sz
+    lib.attn_fwd_split_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_fwd_split.restype = i32
+    lib.attn_fwd_split.argtypes = [vp] * 6 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, i32, vp]
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_bwd.restype = i32
@@ -84,6 +89,17 @@ def _load():
 def attn_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
              scale: float, causal: int, dtype: int, out_dtype: int, stream: int) -> int:
     return _load().attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, out_dtype, stream)
+
+
+def attn_fwd_split_workspace_size(B: int, H: int, N: int, d: int, nsplit: int) -> int:
+    return _load().attn_fwd_split_workspace_size(B, H, N, d, nsplit)
+
+
+def attn_fwd_split(q: int, k: int, v: int, o: int, lse: int, workspace: int, workspace_bytes: int,
+                   B: int, H: int, N: int, d: int, scale: float, causal: int, dtype: int,
+                   out_dtype: int, nsplit: int, stream: int) -> int:
+    return _load().attn_fwd_split(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                                  causal, dtype, out_dtype, nsplit, stream)
 
 
 def attn_bwd_workspace_size(B: int, H: int, N: int, d: int, dtype: int) -> int:
@@ -176,6 +192,39 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
                   _stream(q))
     if st != 0:
         raise AttnError(st, "attn_fwd")
+    return o, lse
+
+
+def forward_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                  scale: Optional[float] = None, nsplit: int = 2,
+                  out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact attention forward with each query block's K/V split into nsplit
+    chunks and the partial results merged (attn_fwd_split).  Arguments and
+    results as for :func:`forward`; workspace, if given, is a uint8 CUDA
+    tensor of at least attn_fwd_split_workspace_size(...) bytes."""
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"dtype must be float16 or bfloat16, got {q.dtype}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    od = _out_dtype(q, out_dtype)
+    o = torch.empty(q.shape, dtype=od, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = attn_fwd_split_workspace_size(B, H, N, d, int(nsplit))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                        B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
+                        _OUT_CODE[od], int(nsplit), _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_split")
     return o, lse
 
 

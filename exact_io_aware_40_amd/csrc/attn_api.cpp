@@ -74,6 +74,7 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale must be finite";
         case ATTN_ERR_CAUSAL: return "ATTN_ERR_CAUSAL: causal must be 0 or 1";
         case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: an output overlaps an input or another output";
+        case ATTN_ERR_SPLIT: return "ATTN_ERR_SPLIT: nsplit must be in 1 .. ATTN_MAX_SPLIT";
         default: return "unknown attn status";
     }
 }
@@ -111,8 +112,69 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.total = int(total);
     a.c = exponent_unit(scale);
     a.negate = scale < 0.f;
+    a.nsplit = 0;
+    a.split_o = 0;
+    a.split_lse = 0;
     hipError_t e = attn::launch_fwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
                                     (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_fwd_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int nsplit) {
+    bool empty = false;
+    if (check_common(B, H, N, d, 1.0f, 0, ATTN_BF16, ATTN_BF16, &empty) != ATTN_OK || empty) return 0;
+    if (nsplit < 1 || nsplit > ATTN_MAX_SPLIT) return 0;
+    return attn::fwd_split_workspace_bytes(B * H, N, d, nsplit);
+}
+
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                   int causal, int dtype, int out_dtype, int nsplit, void* stream) {
+    bool empty = false;
+    int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
+    if (st != ATTN_OK) return st;
+    if (nsplit < 1 || nsplit > ATTN_MAX_SPLIT) return ATTN_ERR_SPLIT;
+    if (empty) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const size_t need = attn::fwd_split_workspace_bytes(BH, N, d, nsplit);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    const size_t tbytes = size_t(BH * N * d) * 2;
+    const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
+    const Range ro = range(o, obytes), rl = range(lse, size_t(BH * N) * 4), rw = range(workspace, need);
+    const Range in[3] = {range(q, tbytes), range(k, tbytes), range(v, tbytes)};
+    for (const Range& r : in)
+        if (overlap(ro, r) || overlap(rl, r) || overlap(rw, r)) return ATTN_ERR_ALIAS;
+    if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw)) return ATTN_ERR_ALIAS;
+
+    attn::FwdArgs a;
+    const size_t split_o = size_t(BH * N * d), split_lse = size_t(BH * N);
+    float* ws_o = static_cast<float*>(workspace);
+    float* ws_lse = ws_o + size_t(nsplit) * split_o;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = ws_o;
+    a.lse = ws_lse;
+    a.N = int(N);
+    const int br = attn::fwd_block_rows();
+    a.nqb = int((N + br - 1) / br);
+    const int64_t total = BH * a.nqb * nsplit;
+    if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
+    a.total = int(total);
+    a.c = exponent_unit(scale);
+    a.negate = scale < 0.f;
+    a.nsplit = nsplit;
+    a.split_o = split_o;
+    a.split_lse = split_lse;
+    // the partials are fp32 whatever the output type; the merge rounds once
+    hipError_t e = attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
+    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+    e = attn::launch_fwd_merge(ws_o, ws_lse, o, lse, BH * N, nsplit, split_o, split_lse, int(d), dtype,
+                               out_dtype == ATTN_F32, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -124,8 +124,17 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     // every workgroup streams about as many tiles as any other (heavy and
     // light blocks together) and the grid has no tail of heavy blocks.
     const int L = xcd_remap(blockIdx.x, a.total);
-    int bh, qb_items[2], nitems = 1;
-    if (CAUSAL) {
+    int bh, qb_items[2], nitems = 1, split = 0;
+    if (a.nsplit > 0) {
+        // split K/V: one query block and one chunk of its tiles (heaviest
+        // causal blocks first); the partial results are merged afterwards
+        const int per = a.nqb * a.nsplit;
+        bh = L / per;
+        const int rem = L - bh * per;
+        const int qbi = rem / a.nsplit;
+        split = rem - qbi * a.nsplit;
+        qb_items[0] = CAUSAL ? a.nqb - 1 - qbi : qbi;
+    } else if (CAUSAL) {
         const int npairs = (a.nqb + 1) >> 1;
         bh = L / npairs;
         const int p = L - bh * npairs;
@@ -157,12 +166,22 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 i32x4 x = {0, 0, 0, 0};
                 if (qrow[r] < N) x = *(const i32x4*)(Qh + (size_t)qrow[r] * D + 16 * kk + 8 * h);
                 if (a.negate) x ^= (int)0x80008000;   // scale < 0: use -Q and |scale|
-                    qf[r][kk] = x;
+                qf[r][kk] = x;
             }
         }
 
         const int kend = CAUSAL ? min(N, q0 + BR) : N;
-        const int ntiles = (kend + BC - 1) / BC;   // tiles the workgroup streams
+        const int ntiles = (kend + BC - 1) / BC;   // tiles the block's rows can see
+        // The tiles of this work item, tb .. te-1: all of the block's, or one
+        // chunk of them under split K/V (possibly none); keys from klim on are
+        // masked.
+        int tb = 0, te = ntiles;
+        if (a.nsplit > 0) {
+            const int chunk = (ntiles + a.nsplit - 1) / a.nsplit;
+            tb = min(ntiles, split * chunk);
+            te = min(ntiles, tb + chunk);
+        }
+        const int klim = min(kend, te * BC);
 
         // Copy p of this thread fills LDS slot (p*4 + w)*64 + lane of a tile:
         // row `row`, physical granule pg, which holds logical granule
@@ -178,7 +197,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // of the buffer: they read zeros and cost no memory traffic.
         const unsigned sbase = lds_addr(smem) + w * 1024;
         auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int t, int buf) __attribute__((always_inline)) {
-            const unsigned base = t < ntiles ? (unsigned)t * TILE : head_bytes;
+            const unsigned base = t < te ? (unsigned)t * TILE : head_bytes;
     #pragma unroll
             for (int p = 0; p < LOADS; ++p) dma16_async(rs, sbase + buf * TILE + p * NW * 1024, base + src_off[p]);
         };
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = j0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3);
-                        const bool ok = key < N && (!CAUSAL || key <= qrow[r]);
+                        const bool ok = key < klim && (!CAUSAL || key <= qrow[r]);
                         sc[r][b][e] = ok ? sc[r][b][e] : -INFINITY;
                     }
         };
@@ -339,26 +358,27 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             }
         };
 
-        // Iteration t (t = 0 .. ntiles): copies of K(t+KLEAD) and V(t+VLEAD)
+        // Iteration t (t = 0 .. te-tb; tile numbers below are relative to tb):
+        // copies of K(t+KLEAD) and V(t+VLEAD)
         // start, into K buffer (t-1)%RING and V buffer (t-3)%RING, which last
         // held K(t-1) and V(t-3), read in iteration t-2 at the latest; softmax of
         // tile t (scores in sc, P to pc), S of tile t+1 (to sn, K buffer
         // (t+1)%RING), P.V of tile t-1 (P in pp, V buffer (t-1)%RING; for t = 0
         // both are zero); then this wave waits for its copies of K(t+2) and V(t),
         // started in iteration t+2-KLEAD, and a barrier makes every wave's copies
-        // visible to iteration t+1, which reads them.  Tile ntiles is all masked
+        // visible to iteration t+1, which reads them.  Tile te-tb is all masked
         // and its P is zero.
         constexpr int INFLIGHT = (KLEAD - 2) * 2 * LOADS;   // copies younger than those waited for
         static_assert(KLEAD - 2 == VLEAD, "K and V copies of one iteration are waited for together");
         static_assert(INFLIGHT < 64, "vmcnt is six bits");
         auto iter = [&](auto J, int t, Scores& sc, Scores& sn, Probs& pp, Probs& pc) __attribute__((always_inline)) {
             constexpr int j = decltype(J)::value;   // t % RING
-            const int j0 = t * BC;
-            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qlo);
+            const int j0 = (tb + t) * BC;
+            const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo);
             float alpha[QB];
             bool upd_any;
-            issue(krs, t + KLEAD, (j + KLEAD) % RING);
-            issue(vrs, t + VLEAD, RING + (j + VLEAD) % RING);
+            issue(krs, tb + t + KLEAD, (j + KLEAD) % RING);
+            issue(vrs, tb + t + VLEAD, RING + (j + VLEAD) % RING);
             if (need_mask) [[unlikely]] apply_mask(sc, j0);
             upd_any = false;
             {
@@ -412,12 +432,12 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // order iterations t = -VLEAD .. -1 would start them; V buffer RING-1
         // (read as "tile -1" with P = 0) cleared so that it holds finite values;
         // S of tile 0.
-        issue(krs, 0, 0);
-        issue(krs, 1, 1);
+        issue(krs, tb, 0);
+        issue(krs, tb + 1, 1);
     #pragma unroll
         for (int t = -VLEAD; t < 0; ++t) {
-            issue(krs, t + KLEAD, t + KLEAD);
-            issue(vrs, t + VLEAD, RING + t + VLEAD);
+            issue(krs, tb + t + KLEAD, t + KLEAD);
+            issue(vrs, tb + t + VLEAD, RING + t + VLEAD);
         }
     #pragma unroll
         for (int p = 0; p < LOADS; ++p)
@@ -433,7 +453,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         auto one = [&](auto J) __attribute__((always_inline)) {
             if constexpr (decltype(J)::value % 2 == 0) iter(J, t, sA, sB, pA, pB);
             else iter(J, t, sB, sA, pB, pA);
-            return ++t <= ntiles;
+            return ++t <= te - tb;
         };
         while (for_ring(one, std::make_integer_sequence<int, RING>{})) {
         }
@@ -444,13 +464,15 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < QB; ++r) {
             const float l_tot = sum32(l_run[r]);
             const float lf_tot = sum32(lf_run[r]);
-            const float inv = fast_rcp(l_tot);
+            // a row that sees no key of its chunk (split K/V only) gets O = 0 and
+            // lse = -inf, which weigh nothing in the merge
+            const float inv = l_tot > 0.f ? fast_rcp(l_tot) : 0.f;
             // (the row index passes through an empty asm statement so that
             // its 64-bit offset is formed here, not kept live through the loop)
             int qr = qrow[r];
             __asm__ volatile("" : "+v"(qr));
             if (qr < N) {
-                TO* __restrict__ orow = (TO*)a.o + head + (size_t)qr * D;
+                TO* __restrict__ orow = (TO*)a.o + (size_t)split * a.split_o + head + (size_t)qr * D;
     #pragma unroll
                 for (int cb = 0; cb < DB; ++cb) {
     #pragma unroll
@@ -460,13 +482,54 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                         store4<TO>(orow + 32 * cb + 8 * gg + 4 * h, x);
                     }
                 }
-                if (h == 0) a.lse[(size_t)bh * N + qr] = (mc_run[r] + fast_log2(lf_tot)) * 0.69314718055994531f;
+                if (h == 0)
+                    a.lse[(size_t)split * a.split_lse + (size_t)bh * N + qr] =
+                        lf_tot > 0.f ? (mc_run[r] + fast_log2(lf_tot)) * 0.69314718055994531f : -INFINITY;
             }
         }
         // the next item reuses the LDS buffers (this wave's copies have
         // drained; the barrier waits for every other wave's reads)
         if (item + 1 < nitems) __syncthreads();
     }
+}
+
+// Merge of split K/V partials, one thread per 4 columns of a row: the
+// pages' rescale rule for combining two partial softmaxes ("FlashAttention's
+// move: rescale the output, too"; explainer "Common questions" on
+// Flash-Decoding) in logsumexp form, over all chunks at once:
+//   lse = log sum_s e^(lse_s),  O = sum_s e^(lse_s - lse) O_s,
+// with each O_s already normalised by its own chunk's sum.  A chunk whose
+// row saw no key has lse_s = -inf and weight 0.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws_o,
+                                                    const float* __restrict__ ws_lse,
+                                                    TO* __restrict__ o, float* __restrict__ lse,
+                                                    int64_t rows, int nsplit, size_t split_o,
+                                                    size_t split_lse) {
+    constexpr int G = D / 4;   // 4-column groups per row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / G;
+    const int cg = (int)(gid - row * G);
+    if (row >= rows) return;
+    float m = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ws_lse[sp * split_lse + row]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float wgt = expf(ws_lse[sp * split_lse + row] - m);
+            const f32x4 x = *(const f32x4*)(ws_o + sp * split_o + row * D + 4 * cg);
+            wsum += wgt;
+            acc[0] += wgt * x[0];
+            acc[1] += wgt * x[1];
+            acc[2] += wgt * x[2];
+            acc[3] += wgt * x[3];
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const f32x4 y = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    store4<TO>(o + row * D + 4 * cg, y);
+    if (cg == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
 template <typename T, typename TO, int D, bool CAUSAL>
@@ -484,6 +547,33 @@ hipError_t launch_t(const FwdArgs& a, int d, int causal, hipStream_t stream) {
 }  // namespace
 
 int fwd_block_rows() { return BR; }
+
+size_t fwd_split_workspace_bytes(int64_t BH, int64_t N, int64_t d, int nsplit) {
+    return (size_t)nsplit * (size_t)BH * (size_t)N * (size_t)(d + 1) * 4;
+}
+
+template <typename TO, int D>
+hipError_t launch_merge_t(const float* ws_o, const float* ws_lse, void* o, float* lse, int64_t rows,
+                          int nsplit, size_t split_o, size_t split_lse, hipStream_t stream) {
+    const int64_t threads = rows * (D / 4);
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL((merge_kernel<TO, D>), dim3(grid), dim3(256), 0, stream, ws_o, ws_lse, (TO*)o,
+                       lse, rows, nsplit, split_o, split_lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_merge(const float* ws_o, const float* ws_lse, void* o, float* lse, int64_t rows,
+                            int nsplit, size_t split_o, size_t split_lse, int d, int dtype, bool out_f32,
+                            hipStream_t stream) {
+    if (out_f32)
+        return d == 64 ? launch_merge_t<float, 64>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream)
+                       : launch_merge_t<float, 128>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream);
+    if (dtype == 1)
+        return d == 64 ? launch_merge_t<__bf16, 64>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream)
+                       : launch_merge_t<__bf16, 128>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream);
+    return d == 64 ? launch_merge_t<_Float16, 64>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream)
+                   : launch_merge_t<_Float16, 128>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream);
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream) {
     if (dtype == 1)

@@ -20,10 +20,21 @@ struct FwdArgs {
     int total;    // workgroups: B * H * nqb, or B * H * ceil(nqb / 2) under causal masking
     float c;      // |scale| * log2(e): exponent units of the kernel
     int negate;   // scale < 0: the kernel multiplies Q by -1 (exact)
+    int nsplit;   // 0: whole query blocks; > 0: each block's K/V tiles in nsplit chunks,
+                  // partial results (fp32 O, lse) to o / lse at chunk strides below
+    size_t split_o;    // elements between the partial outputs of consecutive chunks
+    size_t split_lse;  // elements between their partial lse
 };
 
 int fwd_block_rows();
 hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
+
+// Split K/V: workspace bytes for nsplit chunks (fp32 partial O and lse), and
+// the merge of the partials into o (dtype, or fp32) and lse.
+size_t fwd_split_workspace_bytes(int64_t BH, int64_t N, int64_t d, int nsplit);
+hipError_t launch_fwd_merge(const float* ws_o, const float* ws_lse, void* o, float* lse, int64_t rows,
+                            int nsplit, size_t split_o, size_t split_lse, int d, int dtype, bool out_f32,
+                            hipStream_t stream);
 
 struct BwdArgs {
     const void* q;

@@ -70,8 +70,12 @@ enum attn_status {
     ATTN_ERR_LAUNCH = -7,    /* the HIP runtime rejected a kernel launch */
     ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite */
     ATTN_ERR_CAUSAL = -9,    /* causal is neither 0 nor 1 */
-    ATTN_ERR_ALIAS = -10     /* an output overlaps an input or another output */
+    ATTN_ERR_ALIAS = -10,    /* an output overlaps an input or another output */
+    ATTN_ERR_SPLIT = -11     /* nsplit outside 1 .. ATTN_MAX_SPLIT */
 };
+
+/* Largest number of K/V chunks attn_fwd_split accepts. */
+#define ATTN_MAX_SPLIT 64
 
 /*
  * attn_fwd -- forward pass.
@@ -96,6 +100,42 @@ enum attn_status {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, int out_dtype, void* stream);
+
+/*
+ * attn_fwd_split_workspace_size -- bytes of device workspace attn_fwd_split
+ * needs: nsplit partial outputs and partial lse, fp32,
+ * nsplit * B * H * N * (d + 1) * 4.  Returns 0 when there is nothing to do
+ * and for invalid arguments (attn_fwd_split validates them).
+ */
+size_t attn_fwd_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int nsplit);
+
+/*
+ * attn_fwd_split -- the forward pass with each query block's K/V tiles split
+ * into nsplit chunks processed by separate workgroups (Flash-Decoding:
+ * explainer "Common questions"), for shapes whose query blocks alone do not
+ * fill the GPU.  Each chunk c yields, for every row, its own softmax over
+ * the chunk's keys: a partial output O_c (normalised by the chunk's sum) and
+ * a partial lse_c (-inf when the row sees no key of the chunk).  A second
+ * kernel merges them with the rescale rule of the online softmax ("FlashAttention's
+ * move: rescale the output, too") in logsumexp form:
+ *     lse = log sum_c exp(lse_c),   o = sum_c exp(lse_c - lse) O_c.
+ * The result is the same o and lse as attn_fwd up to rounding.
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, causal, dtype, out_dtype, stream :
+ *             as for attn_fwd
+ *   workspace, workspace_bytes : caller-owned device memory of at least
+ *             attn_fwd_split_workspace_size(B, H, N, d, nsplit) bytes,
+ *             16-byte aligned, overlapping no input or output; its contents
+ *             on entry do not matter and on return are unspecified
+ *   nsplit  : number of chunks, 1 .. ATTN_MAX_SPLIT (chunks past a query
+ *             block's last tile are empty)
+ * Returns ATTN_OK or a negative attn_status (ATTN_ERR_SPLIT for nsplit out
+ * of range, ATTN_ERR_WORKSPACE for a missing or short workspace).
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                   int64_t d, float scale, int causal, int dtype, int out_dtype, int nsplit,
+                   void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 # status codes as declared in the header
-OK, E_NULL, E_SHAPE, E_HD, E_DT, E_ALIGN, E_WS, E_LAUNCH, E_SCALE, E_CAUSAL, E_ALIAS = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+OK, E_NULL, E_SHAPE, E_HD, E_DT, E_ALIGN, E_WS, E_LAUNCH, E_SCALE, E_CAUSAL, E_ALIAS, E_SPLIT = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11)
 
 # fake, 16-byte aligned, far-apart addresses (validation only)
 P = [0x10000000 * (i + 1) for i in range(12)]
@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                    "attn_bwd_workspace_size", "attn_fwd", "attn_status_str"]
+                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_split",
+                                    "attn_fwd_split_workspace_size", "attn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for code in (OK, E_NULL, E_SHAPE, E_HD, E_DT, E_ALIGN, E_WS, E_LAUNCH, E_SCALE, E_CAUSAL,
-                 E_ALIAS):
+                 E_ALIAS, E_SPLIT):
         s = attn.attn_status_str(code)
         assert s.startswith("ATTN_")
     assert "unknown" in attn.attn_status_str(12345)
@@ -55,6 +56,19 @@ def fwd(**kw):
     od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
     return attn.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
                          a["d"], a["scale"], a["causal"], a["dtype"], od, a["stream"])
+
+
+def fwd_split(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], wsb=None, B=2, H=3, N=100,
+             d=128, scale=0.1, causal=0, dtype=1, out_dtype=None, nsplit=4, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    wsb = a["wsb"]
+    if wsb is None:
+        wsb = attn.attn_fwd_split_workspace_size(a["B"], a["H"], a["N"], a["d"], a["nsplit"])
+    return attn.attn_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], wsb, a["B"],
+                               a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], od,
+                               a["nsplit"], a["stream"])
 
 
 def bwd(**kw):
@@ -163,3 +177,29 @@ def test_split_backward_ignores_unused_pointers():
     dk/dv half, and an empty problem does nothing."""
     assert bwd_dkdv(B=0) == OK and bwd_dq(N=0) == OK
     assert bwd_dkdv(d=96) == E_HD      # still validated before anything else
+
+
+def test_split_workspace_size():
+    # nsplit partial outputs and lse, fp32: nsplit * B*H*N * (d + 1) * 4 bytes
+    assert attn.attn_fwd_split_workspace_size(2, 3, 100, 128, 4) == 4 * 6 * 100 * 129 * 4
+    assert attn.attn_fwd_split_workspace_size(1, 1, 1, 64, 1) == 65 * 4
+    assert attn.attn_fwd_split_workspace_size(0, 3, 100, 128, 4) == 0
+    assert attn.attn_fwd_split_workspace_size(2, 3, 100, 96, 4) == 0
+    assert attn.attn_fwd_split_workspace_size(2, 3, 100, 128, 0) == 0
+    assert attn.attn_fwd_split_workspace_size(2, 3, 100, 128, 65) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nsplit=0), E_SPLIT), (dict(nsplit=65), E_SPLIT), (dict(nsplit=-3), E_SPLIT),
+    (dict(ws=0), E_WS), (dict(wsb=100), E_WS), (dict(ws=P[5] + 8), E_ALIGN),
+    (dict(ws=P[0]), E_ALIAS), (dict(ws=P[3]), E_ALIAS), (dict(lse=P[5]), E_ALIAS),
+    (dict(o=0), E_NULL), (dict(d=80), E_HD), (dict(causal=2), E_CAUSAL),
+    (dict(scale=float("nan")), E_SCALE), (dict(dtype=7), E_DT), (dict(q=P[0] + 2), E_ALIGN),
+])
+def test_fwd_split_rejects(kw, code):
+    assert fwd_split(**kw) == code
+
+
+def test_fwd_split_empty_is_noop():
+    assert fwd_split(B=0) == OK
+    assert fwd_split(N=0, ws=0, wsb=0) == OK

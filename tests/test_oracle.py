@@ -316,3 +316,28 @@ def test_backward_matches_brute_and_autograd(causal):
     out.backward(torch.from_numpy(dO))
     for a, tt in ((dq, t[0]), (dk, t[1]), (dv, t[2])):
         assert np.abs(a - tt.grad.numpy()).max() <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bounds", [[0, 37], [0, 5, 5, 37], [0, 1, 2, 3, 37], [0, 16, 20, 36, 37],
+                                    [0, 0, 37, 37]])
+def test_split_merge_equals_definition(causal, bounds):
+    """Softmax per chunk of the keys, merged by the rescale rule in logsumexp
+    form, gives the full softmax: for any chunking, including empty chunks
+    and (causal) rows that see no key of a chunk."""
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((2, 37, 8)) for _ in range(3))
+    o_ref, lse_ref, _ = brute.fwd(q, k, v, 0.3, causal)
+    o, lse = brute.split_merge(q, k, v, 0.3, causal, bounds)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-12, rtol=0)
+
+
+def test_split_merge_dropped_chunk_is_detected():
+    """The check above is sharp: leaving one chunk out of the merge (a plausible
+    mistake) changes O and lse."""
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((1, 20, 4)) for _ in range(3))
+    o_ref, lse_ref, _ = brute.fwd(q, k, v, 0.5, False)
+    o, lse = brute.split_merge(q, k, v, 0.5, False, [0, 10])   # keys 10..19 missing
+    assert np.abs(lse - lse_ref).max() > 1e-3 and np.abs(o - o_ref).max() > 1e-3
