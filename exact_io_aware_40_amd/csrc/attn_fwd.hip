@@ -123,8 +123,11 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     // pair of blocks nqb-1-p and p of one head, one after the other, so that
     // every workgroup streams about as many tiles as any other (heavy and
     // light blocks together) and the grid has no tail of heavy blocks.
+    // (the divisions by run-time counts are vector code; their results are
+    // the same in every lane and are moved to scalar registers, so that they
+    // and everything derived from them take no vector registers in the loop)
     const int L = xcd_remap(blockIdx.x, a.total);
-    int bh, qb_items[2], nitems = 1, split = 0;
+    int bh, qb_first, qb_second = 0, nitems = 1, split = 0;
     if (a.nsplit > 0) {
         // split K/V: one query block and one chunk of its tiles (heaviest
         // causal blocks first); the partial results are merged afterwards
@@ -133,20 +136,25 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         const int rem = L - bh * per;
         const int qbi = rem / a.nsplit;
         split = rem - qbi * a.nsplit;
-        qb_items[0] = CAUSAL ? a.nqb - 1 - qbi : qbi;
+        qb_first = CAUSAL ? a.nqb - 1 - qbi : qbi;
     } else if (CAUSAL) {
         const int npairs = (a.nqb + 1) >> 1;
         bh = L / npairs;
         const int p = L - bh * npairs;
-        qb_items[0] = a.nqb - 1 - p;
-        qb_items[1] = p;
+        qb_first = a.nqb - 1 - p;
+        qb_second = p;
         nitems = p != a.nqb - 1 - p ? 2 : 1;
     } else {
         bh = L / a.nqb;
-        qb_items[0] = L - bh * a.nqb;
+        qb_first = L - bh * a.nqb;
     }
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    qb_first = __builtin_amdgcn_readfirstlane(qb_first);
+    qb_second = __builtin_amdgcn_readfirstlane(qb_second);
+    nitems = __builtin_amdgcn_readfirstlane(nitems);
+    split = __builtin_amdgcn_readfirstlane(split);
     for (int item = 0; item < nitems; ++item) {
-        const int qb = qb_items[item];
+        const int qb = item == 0 ? qb_first : qb_second;
         const int q0 = qb * BR;
         const size_t head = (size_t)bh * N * D;
         const T* __restrict__ Qh = (const T*)a.q + head;
@@ -178,8 +186,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         int tb = 0, te = ntiles;
         if (a.nsplit > 0) {
             const int chunk = (ntiles + a.nsplit - 1) / a.nsplit;
-            tb = min(ntiles, split * chunk);
-            te = min(ntiles, tb + chunk);
+            tb = __builtin_amdgcn_readfirstlane(min(ntiles, split * chunk));
+            te = __builtin_amdgcn_readfirstlane(min(ntiles, tb + chunk));
         }
         const int klim = min(kend, te * BC);
 
