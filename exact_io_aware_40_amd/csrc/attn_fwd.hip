@@ -256,17 +256,21 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         };
         // Scores of keys a row may not see (causal, past the end of the
         // sequence, or past the workgroup's range) become -inf.
+        // Element e of block b holds key j0 + 4h + (32b + 8(e/4) + e%4), which is
+        // visible when that key is below klim and (causal) at most the row: one
+        // comparison of the constant part against a per-lane limit.
         auto apply_mask = [&](Scores& sc, int j0) __attribute__((always_inline)) {
     #pragma unroll
-            for (int r = 0; r < QB; ++r)
+            for (int r = 0; r < QB; ++r) {
+                const int lim = (CAUSAL ? min(klim - 1, qrow[r]) : klim - 1) - j0 - 4 * h;
     #pragma unroll
                 for (int b = 0; b < KB; ++b)
     #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int key = j0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3);
-                        const bool ok = key < klim && (!CAUSAL || key <= qrow[r]);
-                        sc[r][b][e] = ok ? sc[r][b][e] : -INFINITY;
+                        const int kc = 32 * b + 8 * (e >> 2) + (e & 3);
+                        sc[r][b][e] = kc <= lim ? sc[r][b][e] : -INFINITY;
                     }
+            }
         };
 
         Scores sA, sB;
@@ -321,48 +325,56 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         };
 
         // Softmax of one tile, as pieces p = 0 .. NP-1 (row block p % QB):
-        // row maximum over 8 scores (2 KB pieces); the reference, alpha and the
-        // flag for the rescale of O (1); two probabilities, their fp32 sum, their
-        // packed pair and its sum as rounded (8 KB pieces); the row's running
-        // sums (1).  The reference moves when the row maximum rose by more than
-        // kTau binades; alpha is the factor for the older accumulation (1 when
-        // it stays).
-        constexpr int NP_ROW = 10 * KB + 2;
+        // row maximum over 8 scores (2 KB pieces); the reference and the wave's
+        // rescale flags (1); two probabilities, their fp32 sum, their packed
+        // pair and its sum as rounded (8 KB pieces).  The reference moves when
+        // the row maximum rose by more than kTau binades; the factor for the
+        // older accumulation, 2^(old - new), is formed only in the rare branch
+        // that rescales O and the sums (also after the first tile, whose move
+        // from the lowest finite value gives the factor 0 for an O and sums
+        // that are still zero).
+        constexpr int NP_ROW = 10 * KB + 1;
         constexpr int NP = QB * NP_ROW;
-        float st_mt[QB], st_alpha[QB], st_ls[QB], st_lfs[QB];
+        float st_mt[QB], st_mold[QB], st_ls[QB], st_lfs[QB];
         unsigned pw[QB][KB][2][4];
-        auto piece = [&](int p, Scores& sc, bool& upd_any) __attribute__((always_inline)) {
+        auto piece = [&](int p, Scores& sc, uint64_t& upd_mask) __attribute__((always_inline)) {
             const int r = p % QB, sx = p / QB;
             if (sx < 2 * KB) {
+                // a chain of three-way maxima: 8 instructions per 16 scores
                 const int b = sx >> 1, e0 = 8 * (sx & 1);
-                float m = (sx == 0) ? fmaxf(sc[r][b][e0], sc[r][b][e0 + 1])
-                                    : fmaxf(st_mt[r], fmaxf(sc[r][b][e0], sc[r][b][e0 + 1]));
+                const f32x16& x = sc[r][b];
+                float m;
+                if (sx == 0) {
+                    m = fmaxf(fmaxf(x[e0], x[e0 + 1]), x[e0 + 2]);
+                    m = fmaxf(fmaxf(m, x[e0 + 3]), x[e0 + 4]);
+                    m = fmaxf(fmaxf(m, x[e0 + 5]), x[e0 + 6]);
+                    m = fmaxf(m, x[e0 + 7]);
+                } else {
+                    m = st_mt[r];
     #pragma unroll
-                for (int e = 2; e < 8; e += 2) m = fmaxf(m, fmaxf(sc[r][b][e0 + e], sc[r][b][e0 + e + 1]));
+                    for (int e = 0; e < 8; e += 2) m = fmaxf(fmaxf(m, x[e0 + e]), x[e0 + e + 1]);
+                }
                 st_mt[r] = m;
             } else if (sx == 2 * KB) {
                 const float tc = max32(st_mt[r]) * c;
                 const bool upd = tc > mc_run[r] + kTau<T>;
-                const float mc = upd ? tc : mc_run[r];
-                st_alpha[r] = fast_exp2(mc_run[r] - mc);   // 1 when the reference stays
-                // O needs the factor only once it holds something: before the
-                // first tile it is zero (and alpha is 0)
-                upd_any |= upd && mc_run[r] != -FLT_MAX;
-                mc_run[r] = mc;
-                st_ls[r] = 0.f;
-                st_lfs[r] = 0.f;
-            } else if (sx < 10 * KB + 1) {
+                st_mold[r] = mc_run[r];
+                mc_run[r] = upd ? tc : mc_run[r];
+                upd_mask |= __builtin_amdgcn_ballot_w64(upd);
+            } else {
                 const int q = sx - 2 * KB - 1, b = q / 8, e = 2 * (q % 8);
                 const float x0 = fast_exp2(fmaf(sc[r][b][e], c, -mc_run[r]));
                 const float x1 = fast_exp2(fmaf(sc[r][b][e + 1], c, -mc_run[r]));
-                st_lfs[r] += x0;
-                st_lfs[r] += x1;
                 const unsigned pr = Elem<T>::cvt2(x0, x1);
-                st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
+                if (q == 0) {
+                    st_lfs[r] = x0 + x1;
+                    st_ls[r] = Elem<T>::sum2(pr, 0.f);
+                } else {
+                    st_lfs[r] += x0;
+                    st_lfs[r] += x1;
+                    st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
+                }
                 pw[r][b][e / 8][(e % 8) / 2] = pr;
-            } else {
-                l_run[r] = l_run[r] * st_alpha[r] + st_ls[r];
-                lf_run[r] = lf_run[r] * st_alpha[r] + st_lfs[r];
             }
         };
 
@@ -383,12 +395,10 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             constexpr int j = decltype(J)::value;   // t % RING
             const int j0 = (tb + t) * BC;
             const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo);
-            float alpha[QB];
-            bool upd_any;
+            uint64_t upd_mask = 0;
             issue(krs, tb + t + KLEAD, (j + KLEAD) % RING);
             issue(vrs, tb + t + VLEAD, RING + (j + VLEAD) % RING);
             if (need_mask) [[unlikely]] apply_mask(sc, j0);
-            upd_any = false;
             {
                 constexpr int kbuf = (j + 1) % RING, vbuf = (j + RING - 1) % RING;
                 constexpr int NS = 2 * QB;   // products per step
@@ -407,14 +417,13 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                         product(k, m, cur, sn, pp);
                         if (m == 0 && k + DIST < NF) load_frag(kbuf, vbuf, k + DIST, f[(k + DIST) % (DIST + 1)]);
     #pragma unroll
-                        for (int p = slot * NP / NMM; p < (slot + 1) * NP / NMM; ++p) piece(p, sc, upd_any);
+                        for (int p = slot * NP / NMM; p < (slot + 1) * NP / NMM; ++p) piece(p, sc, upd_mask);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
-                alpha[r] = st_alpha[r];
     #pragma unroll
                 for (int b = 0; b < KB; ++b)
     #pragma unroll
@@ -424,13 +433,22 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                         materialize(pc[r][b][q]);
                     }
             }
-            if (__ballot(upd_any) != 0) [[unlikely]] {
+            if (upd_mask != 0) [[unlikely]] {
     #pragma unroll
-                for (int r = 0; r < QB; ++r)
+                for (int r = 0; r < QB; ++r) {
+                    const float alpha = fast_exp2(st_mold[r] - mc_run[r]);   // 1 for a row that stays
     #pragma unroll
                     for (int cb = 0; cb < DB; ++cb)
     #pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha[r];
+                        for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha;
+                    l_run[r] *= alpha;
+                    lf_run[r] *= alpha;
+                }
+            }
+    #pragma unroll
+            for (int r = 0; r < QB; ++r) {
+                l_run[r] += st_ls[r];
+                lf_run[r] += st_lfs[r];
             }
             wait_vmem_upto<INFLIGHT>();
             barrier_only();
