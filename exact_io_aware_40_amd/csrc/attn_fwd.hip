@@ -159,8 +159,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         const size_t head = (size_t)bh * N * D;
         const T* __restrict__ Qh = (const T*)a.q + head;
         const unsigned head_bytes = (unsigned)N * ROWB;
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
+        const char* const kbase = (const char*)((const T*)a.k + head);
+        const char* const vbase = (const char*)((const T*)a.v + head);
 
         // This lane's query rows and their Q fragments (B operands of S^T = K Q^T).
         const int qlo = q0 + 32 * QB * w;
@@ -201,13 +201,18 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             const int row = slot / GR, pg = slot % GR;
             src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
         }
-        // Copies of tiles past the end of the streamed range start past the end
-        // of the buffer: they read zeros and cost no memory traffic.
+        // The copies of tile t go through a buffer descriptor whose base is the
+        // tile's first byte and whose size is what is left of the head (none
+        // past the end of the streamed range), formed in scalar registers: the
+        // per-lane offsets stay fixed, and rows past the end of the sequence or
+        // of the range read zeros and cost no memory traffic.
         const unsigned sbase = lds_addr(smem) + w * 1024;
-        auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, int t, int buf) __attribute__((always_inline)) {
-            const unsigned base = t < te ? (unsigned)t * TILE : head_bytes;
+        auto issue = [&](const char* base, int t, int buf) __attribute__((always_inline)) {
+            const bool in = t < te;
+            const unsigned off = in ? (unsigned)t * TILE : 0u;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + off, in ? head_bytes - off : 0u);
     #pragma unroll
-            for (int p = 0; p < LOADS; ++p) dma16_async(rs, sbase + buf * TILE + p * NW * 1024, base + src_off[p]);
+            for (int p = 0; p < LOADS; ++p) dma16_async(rs, sbase + buf * TILE + p * NW * 1024, src_off[p]);
         };
         // Loop-invariant LDS addresses of this lane's operand reads (those of V
         // include the V ring's base); the block, half-tile and buffer parts are
@@ -396,8 +401,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             const int j0 = (tb + t) * BC;
             const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo);
             uint64_t upd_mask = 0;
-            issue(krs, tb + t + KLEAD, (j + KLEAD) % RING);
-            issue(vrs, tb + t + VLEAD, RING + (j + VLEAD) % RING);
+            issue(kbase, tb + t + KLEAD, (j + KLEAD) % RING);
+            issue(vbase, tb + t + VLEAD, RING + (j + VLEAD) % RING);
             if (need_mask) [[unlikely]] apply_mask(sc, j0);
             {
                 constexpr int kbuf = (j + 1) % RING, vbuf = (j + RING - 1) % RING;
@@ -458,12 +463,12 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // order iterations t = -VLEAD .. -1 would start them; V buffer RING-1
         // (read as "tile -1" with P = 0) cleared so that it holds finite values;
         // S of tile 0.
-        issue(krs, tb, 0);
-        issue(krs, tb + 1, 1);
+        issue(kbase, tb, 0);
+        issue(kbase, tb + 1, 1);
     #pragma unroll
         for (int t = -VLEAD; t < 0; ++t) {
-            issue(krs, tb + t + KLEAD, t + KLEAD);
-            issue(vrs, tb + t + VLEAD, RING + t + VLEAD);
+            issue(kbase, tb + t + KLEAD, t + KLEAD);
+            issue(vbase, tb + t + VLEAD, RING + t + VLEAD);
         }
     #pragma unroll
         for (int p = 0; p < LOADS; ++p)
