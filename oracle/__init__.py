@@ -9,9 +9,11 @@ Two independent implementations live here:
 
 * ``liboracle.so`` (``attn_oracle.c``, plain C, fp64, OpenMP): the
   definition of attention with a three-pass safe softmax per row, its
-  chain-rule gradient, and the pages' online (chunked) softmax and tiled
-  forward in fp64.  Wrapped by :func:`fwd`, :func:`bwd`,
-  :func:`online_softmax`, :func:`fwd_online`.
+  chain-rule gradient, both optionally with dropout on the probabilities
+  (mask from Philox4x32-10), and the pages' online (chunked) softmax and
+  tiled forward in fp64.  Wrapped by :func:`fwd`, :func:`bwd`,
+  :func:`dropout_keep`, :func:`philox4x32_10`, :func:`online_softmax`,
+  :func:`fwd_online`.
 * :mod:`oracle.brute` (NumPy, fp64): standard attention with the N x N score
   and probability matrices materialised, for tiny inputs.
 
@@ -46,6 +48,20 @@ def _load():
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_bwd.argtypes = [_dp] * 10 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.oracle_fwd_dropout.restype = ctypes.c_int
+    lib.oracle_fwd_dropout.argtypes = [_dp] * 5 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                   ctypes.c_double, ctypes.c_int, ctypes.c_double,
+                                                   ctypes.c_uint64, ctypes.c_uint32, _i64p,
+                                                   ctypes.c_int64, ctypes.c_int]
+    lib.oracle_bwd_dropout.restype = ctypes.c_int
+    lib.oracle_bwd_dropout.argtypes = [_dp] * 10 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                    ctypes.c_double, ctypes.c_int, ctypes.c_double,
+                                                    ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int]
+    lib.oracle_dropout_keep.restype = ctypes.c_int
+    lib.oracle_dropout_keep.argtypes = [ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_philox4x32_10.restype = ctypes.c_int
+    lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p] * 3
     lib.oracle_online_softmax.restype = ctypes.c_int64
     lib.oracle_online_softmax.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
     lib.oracle_fwd_online.restype = ctypes.c_int
@@ -70,12 +86,19 @@ def default_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def fwd(q, k, v, scale, causal=False, rows=None, threads=None):
+def _dropout_args(dropout):
+    p, seed, offset = dropout
+    return float(p), int(seed) & (2**64 - 1), int(offset) & (2**32 - 1)
+
+
+def fwd(q, k, v, scale, causal=False, rows=None, threads=None, dropout=None):
     """Forward definition.  q, k, v: [..., N, d] (leading dims flattened to BH).
 
     rows: optional 1-D int array of flattened row ids (bh * N + i); the result
     then holds only those rows, as (o [n_rows, d], lse [n_rows]).  Without
     rows the result has the input's leading shape: (o [..., N, d], lse [..., N]).
+    dropout: optional (p, seed, offset): dropout on the probabilities with the
+    mask of :func:`dropout_keep`.
     """
     lib = _load()
     q, k, v = _c(q), _c(k), _c(v)
@@ -93,19 +116,25 @@ def fwd(q, k, v, scale, causal=False, rows=None, threads=None):
         o = np.empty((nr, d), np.float64)
         lse = np.empty((nr,), np.float64)
         rp = rows.ctypes.data_as(_i64p)
-    rc = lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, N, d,
-                        float(scale), int(bool(causal)), rp, nr,
-                        int(threads or default_threads()))
+    if dropout is None:
+        rc = lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, N, d,
+                            float(scale), int(bool(causal)), rp, nr,
+                            int(threads or default_threads()))
+    else:
+        rc = lib.oracle_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, N, d,
+                                    float(scale), int(bool(causal)), *_dropout_args(dropout), rp, nr,
+                                    int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError("oracle_fwd failed")
     return o, lse
 
 
-def bwd(q, k, v, dO, scale, causal=False, threads=None, o_in=None):
+def bwd(q, k, v, dO, scale, causal=False, threads=None, o_in=None, dropout=None):
     """Gradients of sum(O * dO).  Returns (o, lse, dq, dk, dv), all fp64.
 
     o_in: optional stored forward output; when given, D_i = dO_i . o_in_i
     (the library's backward contract) instead of sum_j P_ij dP_ij.
+    dropout: optional (p, seed, offset), as for :func:`fwd`.
     """
     lib = _load()
     q, k, v, dO = _c(q), _c(k), _c(v), _c(dO)
@@ -123,13 +152,40 @@ def bwd(q, k, v, dO, scale, causal=False, threads=None, o_in=None):
     dq = np.empty(q.shape, np.float64)
     dk = np.empty(q.shape, np.float64)
     dv = np.empty(q.shape, np.float64)
-    rc = lib.oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO),
-                        _ptr(o_in) if o_in is not None else None, _ptr(o), _ptr(lse), _ptr(dq),
-                        _ptr(dk), _ptr(dv), BH, N, d, float(scale), int(bool(causal)),
-                        int(threads or default_threads()))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(o_in) if o_in is not None else None,
+            _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv))
+    nthr = int(threads or default_threads())
+    if dropout is None:
+        rc = lib.oracle_bwd(*ptrs, BH, N, d, float(scale), int(bool(causal)), nthr)
+    else:
+        rc = lib.oracle_bwd_dropout(*ptrs, BH, N, d, float(scale), int(bool(causal)),
+                                    *_dropout_args(dropout), nthr)
     if rc != 0:
         raise RuntimeError("oracle_bwd failed")
     return o, lse, dq, dk, dv
+
+
+def dropout_keep(p, seed, offset, bh, N):
+    """Keep mask of head bh, [N, N] uint8 (1 kept), before any causal mask."""
+    lib = _load()
+    keep = np.empty((N, N), np.uint8)
+    rc = lib.oracle_dropout_keep(float(p), int(seed) & (2**64 - 1), int(offset) & (2**32 - 1),
+                                 int(bh), int(N), keep.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_dropout_keep failed")
+    return keep
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of one counter (4 words) under one key (2 words)."""
+    lib = _load()
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    if c.size != 4 or k.size != 2 or lib.oracle_philox4x32_10(c.ctypes.data, k.ctypes.data,
+                                                              out.ctypes.data) != 0:
+        raise RuntimeError("oracle_philox4x32_10 failed")
+    return out
 
 
 def online_softmax(x, chunk):

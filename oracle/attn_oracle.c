@@ -45,6 +45,23 @@
  *    serve the pages' worked examples (the 8-score chunked softmax, and the
  *    Step 6 exactness check of tiled against standard attention).
  *
+ *  - oracle_fwd_dropout / oracle_bwd_dropout: the same two computations with
+ *    dropout on the attention probabilities, which the pages fuse into the
+ *    kernel and whose mask the backward regenerates from the PRNG state the
+ *    forward keeps ("13% more FLOPs, 5.7x faster", section "The backward
+ *    pass: recompute instead of read"; explainer Step 3 "Tiling").  The pages
+ *    fix neither the generator nor the mask's layout; the reading taken:
+ *        keep_ij = [R_ij >= t],  t = floor(256 p + 1/2)  (0 <= t <= 255),
+ *        O_i     = sum_j keep_ij (256 / (256 - t)) P_ij v_j,
+ *    lse the statistic of the undropped softmax, and R_ij one byte of
+ *    Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+ *    as easy as 1, 2, 3", SC 2011): with key (seed mod 2^32, seed / 2^32)
+ *    and counter (i, 2 floor(j/32) + floor(j/4) mod 2, bh, offset), R_ij is
+ *    byte (j mod 4) of output word floor((j mod 32) / 8).  The gradient is
+ *    the chain rule through the dropped weights W_ij = keep_ij r P_ij
+ *    (r = 256 / (256 - t)): dV_j = sum_i W_ij dO_i, dP_ij = keep_ij r
+ *    dO_i . v_j, D_i = sum_j P_ij dP_ij (= dO_i . O_i), dS = P (dP - D).
+ *
  * All arithmetic is IEEE double with libm exp/log; loops run in the plain
  * index order of the formulas.  OpenMP only splits independent rows (forward)
  * or independent heads (backward) across threads.
@@ -57,16 +74,86 @@
 #include <omp.h>
 #endif
 
+/* Philox4x32-10 (Salmon et al., SC 2011): ten rounds of two 32x32->64-bit
+ * products, each round mapping (c0, c1, c2, c3) with key (k0, k1) to
+ * (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)), the key
+ * advanced by the Weyl constants between rounds. */
+static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0, c1 = n1, c2 = n2, c3 = n3;
+        k0 += W0, k1 += W1;
+    }
+    out[0] = c0, out[1] = c1, out[2] = c2, out[3] = c3;
+}
+
+int oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out) {
+    if (!ctr || !key || !out) return -1;
+    philox4x32_10(ctr, key, out);
+    return 0;
+}
+
+/* Dropout state: threshold t, keep factor r = 256 / (256 - t), generator key
+ * and counter offset. */
+struct drop {
+    int t;
+    double r;
+    uint64_t seed;
+    uint32_t offset;
+};
+
+static int drop_init(struct drop* dr, double p, uint64_t seed, uint32_t offset) {
+    if (!(p >= 0.0 && p < 1.0)) return -1;
+    const double tt = floor(256.0 * p + 0.5);
+    if (tt > 255.0) return -1;
+    dr->t = (int)tt;
+    dr->r = 256.0 / (256.0 - tt);
+    dr->seed = seed;
+    dr->offset = offset;
+    return 0;
+}
+
+/* keep_ij of head bh (1 kept, 0 dropped) */
+static int drop_keep(const struct drop* dr, int64_t bh, int64_t i, int64_t j) {
+    const uint32_t ctr[4] = {(uint32_t)i, (uint32_t)(2 * (j / 32) + (j / 4) % 2), (uint32_t)bh, dr->offset};
+    const uint32_t key[2] = {(uint32_t)dr->seed, (uint32_t)(dr->seed >> 32)};
+    uint32_t out[4];
+    philox4x32_10(ctr, key, out);
+    const uint32_t byte = (out[(j % 32) / 8] >> (8 * (j % 4))) & 0xFFu;
+    return byte >= (uint32_t)dr->t;
+}
+
+/* The keep mask of one head, N x N bytes (1 kept, 0 dropped); the causal
+ * mask is not applied here. */
+int oracle_dropout_keep(double p, uint64_t seed, uint32_t offset, int64_t bh, int64_t N,
+                        uint8_t* keep) {
+    struct drop dr;
+    if (!keep || N < 0 || bh < 0 || drop_init(&dr, p, seed, offset)) return -1;
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < N; ++j) keep[i * N + j] = (uint8_t)drop_keep(&dr, bh, i, j);
+    return 0;
+}
+
 /* Number of keys row i may attend to: all N, or i+1 under the causal mask. */
 static int64_t keys_for_row(int64_t i, int64_t N, int causal) {
     return causal ? (i + 1) : N;
 }
 
 /* One query row of the forward definition.
- * qi: d values; kh, vh: N x d of this (batch, head); s: scratch of N doubles.
+ * qi: d values; kh, vh: N x d of this (batch, head); s: scratch of N doubles;
+ * dr: dropout state or NULL, bh the head's index (for the dropout mask).
  * Writes oi (d values) and *lse_i. */
 static void fwd_row(const double* qi, const double* kh, const double* vh,
                     int64_t i, int64_t N, int64_t d, double scale, int causal,
+                    const struct drop* dr, int64_t bh,
                     double* s, double* oi, double* lse_i) {
     int64_t nk = keys_for_row(i, N, causal);
     /* scores s_j = scale * q_i . k_j */
@@ -82,10 +169,12 @@ static void fwd_row(const double* qi, const double* kh, const double* vh,
     /* pass 2: normaliser */
     double l = 0.0;
     for (int64_t j = 0; j < nk; ++j) l += exp(s[j] - m);
-    /* pass 3: normalised weights applied to V */
+    /* pass 3: normalised weights (dropped and rescaled under dropout)
+     * applied to V */
     for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
     for (int64_t j = 0; j < nk; ++j) {
         double p = exp(s[j] - m) / l;
+        if (dr) p = drop_keep(dr, bh, i, j) ? dr->r * p : 0.0;
         for (int64_t c = 0; c < d; ++c) oi[c] += p * vh[j * d + c];
     }
     *lse_i = m + log(l);
@@ -101,10 +190,11 @@ static void fwd_row(const double* qi, const double* kh, const double* vh,
  *   threads : OpenMP threads to use (<= 0: library default)
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_fwd(const double* q, const double* k, const double* v,
-               double* o, double* lse,
-               int64_t BH, int64_t N, int64_t d, double scale, int causal,
-               const int64_t* rows, int64_t n_rows, int threads) {
+static int fwd_rows(const double* q, const double* k, const double* v,
+                    double* o, double* lse,
+                    int64_t BH, int64_t N, int64_t d, double scale, int causal,
+                    const struct drop* dr,
+                    const int64_t* rows, int64_t n_rows, int threads) {
     if (!q || !k || !v || !o || !lse || BH < 0 || N < 0 || d <= 0) return -1;
     if (!rows) n_rows = BH * N;
     if (n_rows < 0) return -1;
@@ -129,12 +219,31 @@ int oracle_fwd(const double* q, const double* k, const double* v,
                 int64_t bh = r / N, i = r % N;
                 const double* kh = k + bh * N * d;
                 const double* vh = v + bh * N * d;
-                fwd_row(q + r * d, kh, vh, i, N, d, scale, causal, s, o + t * d, lse + t);
+                fwd_row(q + r * d, kh, vh, i, N, d, scale, causal, dr, bh, s, o + t * d, lse + t);
             }
             free(s);
         }
     }
     return failed ? -1 : 0;
+}
+
+int oracle_fwd(const double* q, const double* k, const double* v,
+               double* o, double* lse,
+               int64_t BH, int64_t N, int64_t d, double scale, int causal,
+               const int64_t* rows, int64_t n_rows, int threads) {
+    return fwd_rows(q, k, v, o, lse, BH, N, d, scale, causal, NULL, rows, n_rows, threads);
+}
+
+/* oracle_fwd_dropout: oracle_fwd with dropout probability p (quantised to
+ * t / 256) and generator state (seed, offset). */
+int oracle_fwd_dropout(const double* q, const double* k, const double* v,
+                       double* o, double* lse,
+                       int64_t BH, int64_t N, int64_t d, double scale, int causal,
+                       double p, uint64_t seed, uint32_t offset,
+                       const int64_t* rows, int64_t n_rows, int threads) {
+    struct drop dr;
+    if (drop_init(&dr, p, seed, offset)) return -1;
+    return fwd_rows(q, k, v, o, lse, BH, N, d, scale, causal, &dr, rows, n_rows, threads);
 }
 
 /*
@@ -148,10 +257,11 @@ int oracle_fwd(const double* q, const double* k, const double* v,
  * accumulate without races.  Row by row: recompute s and the forward
  * statistics, form P, dP, D, dS, then add the row's terms to dQ, dK, dV.
  */
-int oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
-               const double* o_in,
-               double* o, double* lse, double* dq, double* dk, double* dv,
-               int64_t BH, int64_t N, int64_t d, double scale, int causal, int threads) {
+static int bwd_heads(const double* q, const double* k, const double* v, const double* dO,
+                     const double* o_in,
+                     double* o, double* lse, double* dq, double* dk, double* dv,
+                     int64_t BH, int64_t N, int64_t d, double scale, int causal,
+                     const struct drop* dr, int threads) {
     if (!q || !k || !v || !dO || !o || !lse || !dq || !dk || !dv || BH < 0 || N < 0 || d <= 0)
         return -1;
 #ifdef _OPENMP
@@ -165,7 +275,8 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
         double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
         double* p = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
         double* dp = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
-        if (!s || !p || !dp) {
+        double* w = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (!s || !p || !dp || !w) {
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
@@ -186,14 +297,18 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
                     const double* qi = qh + i * d;
                     const double* gi = gh + i * d;
                     /* forward quantities of this row: o_i and lse_i */
-                    fwd_row(qi, kh, vh, i, N, d, scale, causal, s, oh + i * d, lh + i);
-                    /* s was overwritten by fwd_row with the scaled scores; P from lse */
-                    for (int64_t j = 0; j < nk; ++j) p[j] = exp(s[j] - lh[i]);
-                    /* dP_ij = dO_i . v_j */
+                    fwd_row(qi, kh, vh, i, N, d, scale, causal, dr, bh, s, oh + i * d, lh + i);
+                    /* s was overwritten by fwd_row with the scaled scores; P from
+                     * lse, and the weights W applied to V (W = P without dropout) */
+                    for (int64_t j = 0; j < nk; ++j) {
+                        p[j] = exp(s[j] - lh[i]);
+                        w[j] = dr ? (drop_keep(dr, bh, i, j) ? dr->r * p[j] : 0.0) : p[j];
+                    }
+                    /* dP_ij = d(loss)/dP_ij: dO_i . v_j, times keep_ij r under dropout */
                     for (int64_t j = 0; j < nk; ++j) {
                         double acc = 0.0;
                         for (int64_t c = 0; c < d; ++c) acc += gi[c] * vh[j * d + c];
-                        dp[j] = acc;
+                        dp[j] = dr ? (drop_keep(dr, bh, i, j) ? dr->r * acc : 0.0) : acc;
                     }
                     /* D_i = sum_j P_ij dP_ij, or dO_i . o_i for a given stored o */
                     double Di = 0.0;
@@ -210,7 +325,7 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
                         for (int64_t c = 0; c < d; ++c) {
                             dqh[i * d + c] += scale * ds * kh[j * d + c];
                             dkh[j * d + c] += scale * ds * qi[c];
-                            dvh[j * d + c] += p[j] * gi[c];
+                            dvh[j * d + c] += w[j] * gi[c];
                         }
                     }
                 }
@@ -219,8 +334,28 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
         free(s);
         free(p);
         free(dp);
+        free(w);
     }
     return failed ? -1 : 0;
+}
+
+int oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
+               const double* o_in,
+               double* o, double* lse, double* dq, double* dk, double* dv,
+               int64_t BH, int64_t N, int64_t d, double scale, int causal, int threads) {
+    return bwd_heads(q, k, v, dO, o_in, o, lse, dq, dk, dv, BH, N, d, scale, causal, NULL, threads);
+}
+
+/* oracle_bwd_dropout: oracle_bwd through the dropped weights (see the top of
+ * the file); o and lse are the dropout forward's. */
+int oracle_bwd_dropout(const double* q, const double* k, const double* v, const double* dO,
+                       const double* o_in,
+                       double* o, double* lse, double* dq, double* dk, double* dv,
+                       int64_t BH, int64_t N, int64_t d, double scale, int causal,
+                       double p, uint64_t seed, uint32_t offset, int threads) {
+    struct drop dr;
+    if (drop_init(&dr, p, seed, offset)) return -1;
+    return bwd_heads(q, k, v, dO, o_in, o, lse, dq, dk, dv, BH, N, d, scale, causal, &dr, threads);
 }
 
 /*
