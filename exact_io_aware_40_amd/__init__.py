@@ -76,6 +76,12 @@ def _load():
     lib.attn_bwd_dq.argtypes = [vp] * 8 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.attn_bwd_dkdv.restype = i32
     lib.attn_bwd_dkdv.argtypes = [vp] * 7 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.attn_fwd_dropout.restype = i32
+    lib.attn_fwd_dropout.argtypes = [vp] * 5 + [i64, i64, i64, i64, f32, i32, f32, u64, u32, i32, i32, vp]
+    lib.attn_bwd_dropout.restype = i32
+    lib.attn_bwd_dropout.argtypes = [vp] * 10 + [sz, i64, i64, i64, i64, f32, i32, f32, u64, u32, i32,
+                                                 i32, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -127,6 +133,22 @@ def attn_bwd_dkdv(q: int, k: int, v: int, dO: int, dk: int, dv: int, workspace: 
                                  scale, causal, dtype, out_dtype, stream)
 
 
+def attn_fwd_dropout(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+                     scale: float, causal: int, dropout_p: float, seed: int, offset: int, dtype: int,
+                     out_dtype: int, stream: int) -> int:
+    return _load().attn_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed,
+                                    offset, dtype, out_dtype, stream)
+
+
+def attn_bwd_dropout(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, dk: int, dv: int,
+                     workspace: int, workspace_bytes: int, B: int, H: int, N: int, d: int,
+                     scale: float, causal: int, dropout_p: float, seed: int, offset: int,
+                     dtype: int, out_dtype: int, stream: int) -> int:
+    return _load().attn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes,
+                                    B, H, N, d, scale, causal, dropout_p, seed, offset, dtype,
+                                    out_dtype, stream)
+
+
 def attn_status_str(status: int) -> str:
     return _load().attn_status_str(status).decode()
 
@@ -161,12 +183,14 @@ def _out_dtype(q: torch.Tensor, out_dtype) -> torch.dtype:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-            out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+            out_dtype: Optional[torch.dtype] = None,
+            dropout: Optional[Tuple[float, int, int]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact attention forward.  q, k, v: [B, H, N, d] fp16/bf16 on the GPU.
 
     Returns (o [B, H, N, d], lse [B, H, N] float32); o has q's dtype unless
-    out_dtype=torch.float32.  scale defaults to 1/sqrt(d).  The work is
-    enqueued on torch's current stream.
+    out_dtype=torch.float32.  scale defaults to 1/sqrt(d).  dropout, if
+    given, is (p, seed, offset) for attn_fwd_dropout.  The work is enqueued
+    on torch's current stream.
     """
     _check(q, "q")
     _check(k, "k", q)
@@ -187,11 +211,18 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         _check(o, "o", q, od)
         if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
             raise ValueError("lse must be contiguous float32 [B, H, N]")
-    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                  B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype], _OUT_CODE[od],
-                  _stream(q))
+    if dropout is None:
+        st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
+                      _OUT_CODE[od], _stream(q))
+    else:
+        p, seed, offset = dropout
+        st = attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), float(p),
+                              int(seed) & (2**64 - 1), int(offset) & (2**32 - 1),
+                              _DTYPE_CODE[q.dtype], _OUT_CODE[od], _stream(q))
     if st != 0:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, "attn_fwd" if dropout is None else "attn_fwd_dropout")
     return o, lse
 
 
@@ -230,14 +261,16 @@ def forward_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: boo
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, dO: torch.Tensor, causal: bool = False,
-             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+             dropout: Optional[Tuple[float, int, int]] = None
              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Gradients (dq, dk, dv) of sum(o * dO) from the forward's o and lse.
 
     The backward recomputes S and P from q, k and lse.  The gradients have
     o's dtype (q's dtype, or float32 when the forward wrote float32).
     `workspace` (a uint8 device tensor of at least attn_bwd_workspace_size
-    bytes) may be passed to avoid an allocation per call.
+    bytes) may be passed to avoid an allocation per call.  dropout, if
+    given, is the forward's (p, seed, offset) for attn_bwd_dropout.
     """
     _check(q, "q")
     od = _out_dtype(q, o.dtype)
@@ -256,10 +289,16 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = (torch.empty(q.shape, dtype=od, device=q.device) for _ in range(3))
-    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
-                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                  workspace.data_ptr(), workspace.numel(), B, H, N, d, float(scale),
-                  int(bool(causal)), code, _OUT_CODE[od], _stream(q))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel())
+    if dropout is None:
+        st = attn_bwd(*ptrs, B, H, N, d, float(scale), int(bool(causal)), code, _OUT_CODE[od],
+                      _stream(q))
+    else:
+        p, seed, offset = dropout
+        st = attn_bwd_dropout(*ptrs, B, H, N, d, float(scale), int(bool(causal)), float(p),
+                              int(seed) & (2**64 - 1), int(offset) & (2**32 - 1), code,
+                              _OUT_CODE[od], _stream(q))
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd" if dropout is None else "attn_bwd_dropout")
     return dq, dk, dv

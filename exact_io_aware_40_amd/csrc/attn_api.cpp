@@ -75,13 +75,43 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_CAUSAL: return "ATTN_ERR_CAUSAL: causal must be 0 or 1";
         case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: an output overlaps an input or another output";
         case ATTN_ERR_SPLIT: return "ATTN_ERR_SPLIT: nsplit must be in 1 .. ATTN_MAX_SPLIT";
+        case ATTN_ERR_DROPOUT:
+            return "ATTN_ERR_DROPOUT: dropout_p must be finite, >= 0 and round(256 dropout_p) <= 255";
         default: return "unknown attn status";
     }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-             int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
-             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Dropout state from the caller's probability and generator state; ATTN_OK
+// or ATTN_ERR_DROPOUT.  t = floor(256 p + 1/2) must be at most 255.
+int drop_args(double p, uint64_t seed, uint32_t offset, attn::DropArgs* dr) {
+    if (!isfinite(p) || p < 0.0) return ATTN_ERR_DROPOUT;
+    const double t = floor(256.0 * p + 0.5);
+    if (t > 255.0) return ATTN_ERR_DROPOUT;
+    dr->on = 1;
+    dr->t = unsigned(t);
+    dr->scale = float(256.0 / (256.0 - t));
+    dr->seed0 = uint32_t(seed);
+    dr->seed1 = uint32_t(seed >> 32);
+    dr->offset = offset;
+    return ATTN_OK;
+}
+
+attn::DropArgs no_drop() {
+    attn::DropArgs dr;
+    dr.on = 0;
+    dr.t = 0;
+    dr.scale = 1.f;
+    dr.seed0 = dr.seed1 = dr.offset = 0;
+    return dr;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+               int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
+               const attn::DropArgs& drop, void* stream) {
     bool empty = false;
     int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
     if (st != ATTN_OK || empty) return st;
@@ -115,9 +145,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.nsplit = 0;
     a.split_o = 0;
     a.split_lse = 0;
+    a.drop = drop;
     hipError_t e = attn::launch_fwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
                                     (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
+             void* stream) {
+    return fwd_common(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, out_dtype, no_drop(), stream);
+}
+
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t N, int64_t d, float scale, int causal, float dropout_p,
+                     uint64_t seed, uint32_t offset, int dtype, int out_dtype, void* stream) {
+    attn::DropArgs dr;
+    const int st = drop_args(dropout_p, seed, offset, &dr);
+    if (st != ATTN_OK) return st;
+    return fwd_common(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, out_dtype, dr, stream);
 }
 
 size_t attn_fwd_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int nsplit) {
@@ -170,6 +220,7 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
     a.nsplit = nsplit;
     a.split_o = split_o;
     a.split_lse = split_lse;
+    a.drop = no_drop();
     // the partials are fp32 whatever the output type; the merge rounds once
     hipError_t e = attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
@@ -192,7 +243,7 @@ namespace {
 int bwd_common(int which, const void* q, const void* k, const void* v, const void* o,
                const void* dO, const float* lse, void* dq, void* dk, void* dv, const void* ws,
                size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-               int causal, int dtype, int out_dtype, void* stream) {
+               int causal, int dtype, int out_dtype, const attn::DropArgs& drop, void* stream) {
     bool empty = false;
     int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
     if (st != ATTN_OK || empty) return st;
@@ -258,6 +309,7 @@ int bwd_common(int which, const void* q, const void* k, const void* v, const voi
     a.c = scale < 0.f ? -exponent_unit(scale) : exponent_unit(scale);
     a.scale = scale;
     a.negate = scale < 0.f;
+    a.drop = drop;
     hipError_t e = attn::launch_bwd(a, which, dtype, out_dtype == ATTN_F32, int(d), causal,
                                     (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -272,7 +324,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
              int causal, int dtype, int out_dtype, void* stream) {
     return bwd_common(3, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
-                      scale, causal, dtype, out_dtype, stream);
+                      scale, causal, dtype, out_dtype, no_drop(), stream);
+}
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     int causal, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+                     int out_dtype, void* stream) {
+    attn::DropArgs dr;
+    const int st = drop_args(dropout_p, seed, offset, &dr);
+    if (st != ATTN_OK) return st;
+    return bwd_common(3, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                      scale, causal, dtype, out_dtype, dr, stream);
 }
 
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -280,7 +344,7 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, cons
                 int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
                 int out_dtype, void* stream) {
     return bwd_common(1, q, k, v, o, dO, lse, dq, nullptr, nullptr, workspace, workspace_bytes, B,
-                      H, N, d, scale, causal, dtype, out_dtype, stream);
+                      H, N, d, scale, causal, dtype, out_dtype, no_drop(), stream);
 }
 
 int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk,
@@ -288,7 +352,7 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, v
                   int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
                   void* stream) {
     return bwd_common(2, q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace,
-                      workspace_bytes, B, H, N, d, scale, causal, dtype, out_dtype, stream);
+                      workspace_bytes, B, H, N, d, scale, causal, dtype, out_dtype, no_drop(), stream);
 }
 
 }  // extern "C"

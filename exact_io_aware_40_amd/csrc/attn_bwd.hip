@@ -19,6 +19,13 @@
 // Tiles move global -> LDS with 16-byte direct copies into two stages
 // (one barrier per tile); loads past the end of the sequence read zeros,
 // which makes such rows contribute nothing (their dO, Q, lse and D are 0).
+//
+// Dropout (a separate instantiation) regenerates the forward's mask from the
+// generator state: with W_ij = keep_ij r P_ij the weights applied to V
+// (r = 256 / (256 - t)), dV_j = sum_i W_ij dO_i and dP_ij = keep_ij r
+// dO_i . v_j, while D_i = dO_i . o_i is unchanged.  The kernels use
+// D'_i = D_i / r, form dS / r = P (keep dP~ - D') with dP~ = dO_i . v_j, and
+// apply r once to dQ, dK and dV.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -145,7 +152,7 @@ __device__ __forceinline__ void tile_sources(unsigned* src, int w, int lane) {
 //   S^T = K Q^T, dP^T = V dO^T (keys x queries), P^T = 2^(S^T c - lse2),
 //   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 // --------------------------------------------------------------------------
-template <typename T, typename TO, int D, bool CAUSAL>
+template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total) {
     typedef typename Elem<T>::v8 v8;
     constexpr int ROWB = D * 2, TILE = BKT * ROWB, LOADS = TILE / (NT * 16);
@@ -191,7 +198,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
         qf[kk] = x;
         gf[kk] = g;
     }
-    const float delta = sum32(dpart);
+    // D_i, divided by the keep factor under dropout
+    const float delta = sum32(dpart) * (DROP ? 1.f / a.drop.scale : 1.f);
     const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
     if (live && h == 0) {
         a.ws[(size_t)bh * NP + qrow] = delta;
@@ -251,6 +259,17 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
         for (int b = 0; b < KB; ++b) {
             if (MASK && b >= nb) continue;
             f32x16 s, dp;
+            // the row's generator call for this 32-key block: element r is
+            // byte r % 4 of word r / 4
+            unsigned ph[4];
+            if (DROP) {
+                ph[0] = (unsigned)qrow;
+                ph[1] = (unsigned)(2 * ((j0 >> 5) + b) + h);
+                ph[2] = (unsigned)bh;
+                ph[3] = a.drop.offset;
+#pragma unroll
+                for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
+            }
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
                 const i32x4 kx = *(const i32x4*)(sK + roff[kk] + 32 * b * ROWB);
@@ -269,7 +288,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
                     const bool ok = key < N && (!CAUSAL || key <= qrow);
                     p = ok ? p : 0.f;
                 }
-                s[r] = p * (dp[r] - delta);
+                const float g = (DROP && !drop_keep(ph[r >> 2], r & 3, a.drop.t)) ? 0.f : dp[r];
+                s[r] = p * (g - delta);
             }
             dsb[b][0] = pack8<T>(s, 0);
             dsb[b][1] = pack8<T>(s, 1);
@@ -319,7 +339,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     }
     if (t < ntiles) step(IC<0>{}, t);
 
-    if (live) store_rows<TO, D>((TO*)a.dq + head + (size_t)qrow * D, acc, a.scale, h);
+    if (live) store_rows<TO, D>((TO*)a.dq + head + (size_t)qrow * D, acc, a.scale * (DROP ? a.drop.scale : 1.f), h);
 }
 
 // --------------------------------------------------------------------------
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
 // K and V rows sit in LDS for the whole kernel; the two halves' partial dK
 // and dV are added through LDS at the end.
 // --------------------------------------------------------------------------
-template <typename T, typename TO, int D, bool CAUSAL>
+template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int total) {
     typedef typename Elem<T>::v8 v8;
     constexpr int ROWB = D * 2;
@@ -342,7 +362,8 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     constexpr int STAGE = 2 * TILE;                // Q tile, dO tile
     constexpr int KOFF = 2 * STAGE;                // K block, then V block
     constexpr int LOFF = KOFF + 2 * KVB;           // per stage: lse2[64], D[64]
-    constexpr int SMEM = LOFF + 2 * 2 * BQT * 4;
+    constexpr int MOFF = LOFF + 2 * 2 * BQT * 4;   // dropout: per wave 32 x 32 mask bytes
+    constexpr int SMEM = MOFF + (DROP ? 8 * 1024 : 0);
     constexpr bool SPLIT = SplitDS<T>::value;
     static_assert(4 * 2 * DB * 16 * 64 * 4 <= SMEM, "reduction area must fit in LDS");
     static_assert(2 * STAGE <= 65536, "stage reads use 16-bit immediate offsets");
@@ -461,6 +482,25 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
             const i32x4 vx = *(const i32x4*)(smem + KVB + kaddr[kk]);
             dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vx), kk == 0 ? f32x16{} : dp);
         }
+        // Dropout: this lane runs the generator call of row 32 qh + l32 and
+        // lane half h, whose byte e % 4 of word e / 4 belongs to key
+        // 8(e/4) + 4h + e%4 of the wave's 32; the bytes pass through the
+        // wave's LDS area as [key][row], from which the lane reads, for its
+        // key, rows 8(r/4) + 4h .. + 3 as one word per r/4.
+        unsigned mw[4];
+        if (DROP) {
+            unsigned ph[4] = {(unsigned)(i0 + 32 * qh + l32), (unsigned)(2 * (kw0 >> 5) + h), (unsigned)bh,
+                              a.drop.offset};
+#pragma unroll
+            for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
+            unsigned char* mt = (unsigned char*)smem + MOFF + w * 1024;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mt[(8 * g + 4 * h + e) * 32 + l32] = (unsigned char)(ph[g] >> (8 * e));
+#pragma unroll
+            for (int g = 0; g < 4; ++g) mw[g] = *(const unsigned*)(mt + l32 * 32 + 8 * g + 4 * h);
+        }
         // rows of this block held by the lane: 32 qh + 8(r/4) + 4h + r%4
         f32x16 p;
 #pragma unroll
@@ -472,8 +512,14 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
                 const int r = 4 * rr + e;
                 float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
                 if (MASK) pv = (key <= i0 + 32 * qh + 8 * rr + 4 * h + e) ? pv : 0.f;
-                p[r] = pv;
-                s[r] = pv * (dp[r] - d4[e]);   // dS
+                if (DROP) {
+                    const bool kp = drop_keep(mw[rr], e, a.drop.t);
+                    p[r] = kp ? pv : 0.f;                    // weights applied to dO (dV)
+                    s[r] = pv * ((kp ? dp[r] : 0.f) - d4[e]);   // dS / r
+                } else {
+                    p[r] = pv;
+                    s[r] = pv * (dp[r] - d4[e]);   // dS
+                }
             }
         }
         const v8 pb0 = pack8<T>(p, 0), pb1 = pack8<T>(p, 1);
@@ -552,34 +598,41 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
                     dv[cb][4 * g + e] += xv[e];
                 }
             }
-        store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale, h);
-        store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, 1.f, h);
+        const float rs = DROP ? a.drop.scale : 1.f;
+        store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale * rs, h);
+        store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, rs, h);
     }
 }
 
-template <typename T, typename TO, int D, bool CAUSAL>
+template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 hipError_t launch(const BwdArgs& a, int which, hipStream_t stream) {
     if (which & 1) {
         const int nqb = (a.N + BQ - 1) / BQ;
         const int tq = a.BH * nqb;
-        hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq);
+        hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL, DROP>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (which & 2) {
         const int nkb = (a.N + BK - 1) / BK;
         const int tk = a.BH * nkb;
-        hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL>), dim3(tk), dim3(NTK), 0, stream, a, nkb, tk);
+        hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL, DROP>), dim3(tk), dim3(NTK), 0, stream, a, nkb, tk);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
+template <typename T, typename TO, int D, bool CAUSAL>
+hipError_t launch_d(const BwdArgs& a, int which, hipStream_t stream) {
+    return a.drop.on ? launch<T, TO, D, CAUSAL, true>(a, which, stream)
+                     : launch<T, TO, D, CAUSAL, false>(a, which, stream);
+}
+
 template <typename T, typename TO>
 hipError_t launch_t(const BwdArgs& a, int which, int d, int causal, hipStream_t stream) {
     if (d == 64)
-        return causal ? launch<T, TO, 64, true>(a, which, stream) : launch<T, TO, 64, false>(a, which, stream);
-    return causal ? launch<T, TO, 128, true>(a, which, stream) : launch<T, TO, 128, false>(a, which, stream);
+        return causal ? launch_d<T, TO, 64, true>(a, which, stream) : launch_d<T, TO, 64, false>(a, which, stream);
+    return causal ? launch_d<T, TO, 128, true>(a, which, stream) : launch_d<T, TO, 128, false>(a, which, stream);
 }
 
 }  // namespace

@@ -276,6 +276,28 @@ template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 x) { *
 // Workgroup id -> logical work item, so that consecutive logical items land
 // on the same XCD.  The dispatcher hands workgroup ids to the 8 XCDs in
 // round-robin order; XCD x receives logical items [base(x), base(x)+count(x)).
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011), the generator of the dropout mask.  A round
+// maps the counter (c0, c1, c2, c3) under key (k0, k1) to
+// (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); round n
+// (0 .. 9) uses the key advanced n times by the Weyl constants W0, W1.
+constexpr unsigned kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr unsigned kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+__device__ __forceinline__ void philox_round(unsigned (&c)[4], unsigned k0, unsigned k1, int n) {
+    const unsigned long long p0 = (unsigned long long)kPhiloxM0 * c[0];
+    const unsigned long long p1 = (unsigned long long)kPhiloxM1 * c[2];
+    const unsigned n0 = (unsigned)(p1 >> 32) ^ c[1] ^ (k0 + (unsigned)n * kPhiloxW0);
+    const unsigned n2 = (unsigned)(p0 >> 32) ^ c[3] ^ (k1 + (unsigned)n * kPhiloxW1);
+    c[1] = (unsigned)p1;
+    c[3] = (unsigned)p0;
+    c[0] = n0;
+    c[2] = n2;
+}
+// Dropout keeps an element whose generator byte is at least the threshold t.
+__device__ __forceinline__ bool drop_keep(unsigned word, int byte, unsigned t) {
+    return ((word >> (8 * byte)) & 0xFFu) >= t;
+}
+
 __device__ __forceinline__ int xcd_remap(int id, int total) {
     const int per = total >> 3, rem = total & 7, x = id & 7;
     return x * per + (x < rem ? x : rem) + (id >> 3);

@@ -37,6 +37,15 @@
 // buffer), with explicit waits where the data is consumed.  Every wave
 // walks every tile of its block: tiles past a wave's diagonal are masked
 // entirely and contribute exactly zero.
+//
+// Dropout (a separate instantiation): the pages fuse it into the kernel and
+// keep only the generator state for the backward ("13% more FLOPs, 5.7x
+// faster", "The backward pass: recompute instead of read"; explainer Step 3).
+// A lane's 16 probabilities of a 32-key block are one Philox4x32-10 call
+// (counter: its row, 2 x block + lane half, head, offset), whose ten rounds
+// run as extra softmax pieces; dropped probabilities become zero in the P.V
+// operand only, so l and lse stay those of the undropped softmax, and the
+// epilogue scales O by 256 / (256 - t).
 #include <float.h>
 
 #include <type_traits>
@@ -91,7 +100,7 @@ template <typename V> __device__ __forceinline__ void materialize(const V& x) {
     __asm__ volatile("" ::"v"(x));
 }
 
-template <typename T, typename TO, int D, bool CAUSAL>
+template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     typedef typename Elem<T>::v8 v8;
     constexpr int BC = bc<D>();
@@ -338,12 +347,29 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // that rescales O and the sums (also after the first tile, whose move
         // from the lowest finite value gives the factor 0 for an O and sums
         // that are still zero).
-        constexpr int NP_ROW = 10 * KB + 1;
+        // Under dropout, the first 10 KB pieces of a row are the rounds of its
+        // generator calls, one per 32-key block (tile j0 / 32 + b).
+        constexpr int NPD = DROP ? 10 * KB : 0;
+        constexpr int NP_ROW = NPD + 10 * KB + 1;
         constexpr int NP = QB * NP_ROW;
         float st_mt[QB], st_mold[QB], st_ls[QB], st_lfs[QB];
         unsigned pw[QB][KB][2][4];
+        unsigned ph[QB][KB][4];   // generator state, then the call's four words
+        int tile_j0 = 0;          // first key of the tile being normalised
         auto piece = [&](int p, Scores& sc, uint64_t& upd_mask) __attribute__((always_inline)) {
-            const int r = p % QB, sx = p / QB;
+            const int r = p % QB;
+            if (DROP && p / QB < NPD) {
+                const int b = (p / QB) / 10, n = (p / QB) % 10;
+                if (n == 0) {
+                    ph[r][b][0] = (unsigned)qrow[r];
+                    ph[r][b][1] = (unsigned)(2 * (tile_j0 / 32 + b) + h);
+                    ph[r][b][2] = (unsigned)bh;
+                    ph[r][b][3] = a.drop.offset;
+                }
+                philox_round(ph[r][b], a.drop.seed0, a.drop.seed1, n);
+                return;
+            }
+            const int sx = p / QB - NPD;
             if (sx < 2 * KB) {
                 // a chain of three-way maxima: 8 instructions per 16 scores
                 const int b = sx >> 1, e0 = 8 * (sx & 1);
@@ -379,7 +405,14 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                     st_lfs[r] += x1;
                     st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
                 }
-                pw[r][b][e / 8][(e % 8) / 2] = pr;
+                if (DROP) {
+                    // elements e, e + 1: bytes e % 4 and e % 4 + 1 of word e / 4
+                    const unsigned wd = ph[r][b][e >> 2];
+                    const bool k0 = drop_keep(wd, e & 3, a.drop.t), k1 = drop_keep(wd, (e & 3) + 1, a.drop.t);
+                    pw[r][b][e / 8][(e % 8) / 2] = Elem<T>::cvt2(k0 ? x0 : 0.f, k1 ? x1 : 0.f);
+                } else {
+                    pw[r][b][e / 8][(e % 8) / 2] = pr;
+                }
             }
         };
 
@@ -399,6 +432,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         auto iter = [&](auto J, int t, Scores& sc, Scores& sn, Probs& pp, Probs& pc) __attribute__((always_inline)) {
             constexpr int j = decltype(J)::value;   // t % RING
             const int j0 = (tb + t) * BC;
+            tile_j0 = j0;
             const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo);
             uint64_t upd_mask = 0;
             issue(kbase, tb + t + KLEAD, (j + KLEAD) % RING);
@@ -497,7 +531,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             const float lf_tot = sum32(lf_run[r]);
             // a row that sees no key of its chunk (split K/V only) gets O = 0 and
             // lse = -inf, which weigh nothing in the merge
-            const float inv = l_tot > 0.f ? fast_rcp(l_tot) : 0.f;
+            const float inv = l_tot > 0.f ? fast_rcp(l_tot) * (DROP ? a.drop.scale : 1.f) : 0.f;
             // (the row index passes through an empty asm statement so that
             // its 64-bit offset is formed here, not kept live through the loop)
             int qr = qrow[r];
@@ -565,7 +599,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 
 template <typename T, typename TO, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
+    if (a.drop.on)
+        hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL, true>), dim3(a.total), dim3(NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL, false>), dim3(a.total), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

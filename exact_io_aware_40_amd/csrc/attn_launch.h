@@ -9,6 +9,17 @@
 
 namespace attn {
 
+// Dropout on the probabilities (inactive when `on` is 0): an element is kept
+// when byte (j mod 4) of word ((j mod 32) / 8) of Philox4x32-10 with key
+// (seed0, seed1) and counter (i, 2 (j / 32) + (j / 4) mod 2, bh, offset) is at
+// least t; kept weights are scaled by `scale` = 256 / (256 - t).
+struct DropArgs {
+    int on;
+    unsigned t;
+    float scale;
+    unsigned seed0, seed1, offset;
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -24,6 +35,7 @@ struct FwdArgs {
                   // partial results (fp32 O, lse) to o / lse at chunk strides below
     size_t split_o;    // elements between the partial outputs of consecutive chunks
     size_t split_lse;  // elements between their partial lse
+    DropArgs drop;
 };
 
 int fwd_block_rows();
@@ -53,6 +65,7 @@ struct BwdArgs {
     float c;        // scale * log2(e) with its sign (magnitude at least FLT_MIN)
     float scale;    // the caller's scale (gradient factor)
     int negate;     // unused by the backward kernels
+    DropArgs drop;  // the forward's dropout, regenerated here
 };
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N);

@@ -30,9 +30,10 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_split",
-                                    "attn_fwd_split_workspace_size", "attn_status_str"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dropout",
+                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_dropout",
+                                    "attn_fwd_split", "attn_fwd_split_workspace_size",
+                                    "attn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for code in (OK, E_NULL, E_SHAPE, E_HD, E_DT, E_ALIGN, E_WS, E_LAUNCH, E_SCALE, E_CAUSAL,
-                 E_ALIAS, E_SPLIT):
+                 E_ALIAS, E_SPLIT, E_DROP):
         s = attn.attn_status_str(code)
         assert s.startswith("ATTN_")
     assert "unknown" in attn.attn_status_str(12345)
@@ -203,3 +204,60 @@ def test_fwd_split_rejects(kw, code):
 def test_fwd_split_empty_is_noop():
     assert fwd_split(B=0) == OK
     assert fwd_split(N=0, ws=0, wsb=0) == OK
+
+
+E_DROP = -12
+
+
+def fwd_drop(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, N=100, d=128, scale=0.1,
+             causal=0, p=0.1, seed=7, offset=3, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                 a["d"], a["scale"], a["causal"], a["p"], a["seed"], a["offset"],
+                                 a["dtype"], od, a["stream"])
+
+
+def bwd_drop(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8],
+             ws=P[9], wsb=1 << 20, B=2, H=3, N=100, d=128, scale=0.1, causal=1, p=0.1, seed=7,
+             offset=3, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["ws"], a["wsb"], a["B"], a["H"], a["N"],
+                                 a["d"], a["scale"], a["causal"], a["p"], a["seed"], a["offset"],
+                                 a["dtype"], od, a["stream"])
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 0.999, float("nan"), float("inf"), 255.5 / 256])
+def test_dropout_rejects_probability(p):
+    """p must be finite, >= 0, and round to a threshold floor(256 p + 1/2) of
+    at most 255; it is checked before anything else, also for empty calls."""
+    assert fwd_drop(p=p) == E_DROP
+    assert bwd_drop(p=p) == E_DROP
+    assert fwd_drop(p=p, B=0) == E_DROP
+
+
+@pytest.mark.parametrize("p", [0.0, 0.5, 254.49 / 256])
+def test_dropout_accepts_probability(p):
+    """A valid probability passes on to the shared checks (here: NULL o)."""
+    assert fwd_drop(p=p, o=0) == E_NULL
+    assert bwd_drop(p=p, dq=0) == E_NULL
+    assert fwd_drop(p=p, B=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=80), E_HD), (dict(causal=2), E_CAUSAL), (dict(scale=float("nan")), E_SCALE),
+    (dict(dtype=7), E_DT), (dict(q=P[0] + 2), E_ALIGN), (dict(o=P[0]), E_ALIAS),
+])
+def test_dropout_shared_validation(kw, code):
+    assert fwd_drop(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=0), E_WS), (dict(wsb=100), E_WS), (dict(dq=P[0]), E_ALIAS), (dict(d=96), E_HD),
+])
+def test_dropout_backward_validation(kw, code):
+    assert bwd_drop(**kw) == code
