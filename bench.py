@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 512 MiB copy (read + write) first, for counter scaling")
+    ap.add_argument("--dropout", type=float, default=None, metavar="P",
+                    help="time the dropout path instead (attn_fwd_dropout, attn_bwd_dropout) "
+                         "with probability P; the backward's two kernels are then timed together")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output dirs")
     return ap.parse_args()
@@ -177,7 +180,10 @@ def cpu_baseline(w, t, scale, budget_s):
     }
 
 
-def sampled_parity(w, t, o, lse, scale):
+DROP_STATE = (2024, 17)   # generator seed and offset of the dropout path
+
+
+def sampled_parity(w, t, o, lse, scale, dropout=None):
     import oracle
     BH, N, d = w.B * w.H, w.N, w.d
     rng = np.random.default_rng(7)
@@ -189,7 +195,7 @@ def sampled_parity(w, t, o, lse, scale):
     o_ref, l_ref = oracle.fwd(t["q"].reshape(BH, N, d).double().numpy(),
                               t["k"].reshape(BH, N, d).double().numpy(),
                               t["v"].reshape(BH, N, d).double().numpy(),
-                              scale, w.causal, rows=rows)
+                              scale, w.causal, rows=rows, dropout=dropout)
     idx = torch.from_numpy(rows).to(o.device)
     og = o.reshape(-1, d)[idx].double().cpu().numpy()
     lg = lse.reshape(-1)[idx].double().cpu().numpy()
@@ -250,14 +256,38 @@ def main():
         if st:
             raise attn.AttnError(st, "attn_bwd_dkdv")
 
+    drop = None if args.dropout is None else (args.dropout,) + DROP_STATE
+
+    def fwd_drop():
+        st = attn.attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), B, H, N, d, scale, causal, drop[0], drop[1],
+                                   drop[2], code, code, sp)
+        if st:
+            raise attn.AttnError(st, "attn_fwd_dropout")
+
+    def bwd_drop():
+        st = attn.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   dO.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), ws.data_ptr(), nbytes_ws, B, H, N, d, scale,
+                                   causal, drop[0], drop[1], drop[2], code, code, sp)
+        if st:
+            raise attn.AttnError(st, "attn_bwd_dropout")
+
     half = 0.5 if w.causal else 1.0
     unit = B * H * N * N * d * half
     f_fwd = 4.0 * unit
     f_bwd = 2.5 * f_fwd                      # credited: five N^2 d products
-    algo = {"fwd_kernel": 4.0 * unit, "dq_kernel": 6.0 * unit, "dkdv_kernel": 8.0 * unit}
-    calls = {"step": [("fwd_kernel", fwd), ("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)],
-             "fwd": [("fwd_kernel", fwd)],
-             "bwd": [("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)]}[args.phase]
+    algo = {"fwd_kernel": 4.0 * unit, "dq_kernel": 6.0 * unit, "dkdv_kernel": 8.0 * unit,
+            "bwd_kernels": 14.0 * unit}
+    if drop is None:
+        calls = {"step": [("fwd_kernel", fwd), ("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)],
+                 "fwd": [("fwd_kernel", fwd)],
+                 "bwd": [("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)]}[args.phase]
+    else:
+        fwd = fwd_drop
+        calls = {"step": [("fwd_kernel", fwd), ("bwd_kernels", bwd_drop)],
+                 "fwd": [("fwd_kernel", fwd)],
+                 "bwd": [("bwd_kernels", bwd_drop)]}[args.phase]
     if args.phase == "bwd":
         fwd()
     flops_step = {"step": f_fwd + f_bwd, "fwd": f_fwd, "bwd": f_bwd}[args.phase]
@@ -304,8 +334,9 @@ def main():
         m = kernels["fwd_kernel"]["ms_mean"]
         phases["fwd"] = {"ms_mean": m, "tflops": f_fwd / (m * 1e-3) / 1e12,
                          "frac_of_peak": f_fwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    if "dq_kernel" in kernels:
-        m = kernels["dq_kernel"]["ms_mean"] + kernels["dkdv_kernel"]["ms_mean"]
+    if "dq_kernel" in kernels or "bwd_kernels" in kernels:
+        m = (kernels["bwd_kernels"]["ms_mean"] if "bwd_kernels" in kernels
+             else kernels["dq_kernel"]["ms_mean"] + kernels["dkdv_kernel"]["ms_mean"])
         phases["bwd"] = {"ms_mean": m, "tflops": f_bwd / (m * 1e-3) / 1e12,
                          "frac_of_peak": f_bwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "flops": "credited 2.5x forward"}
@@ -314,7 +345,7 @@ def main():
     dom = max(kernels, key=lambda k_: kernels[k_]["ms_mean"])
     traffic = None
     tp = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tp):
+    if os.path.exists(tp) and drop is None:   # counters were taken on the plain kernels
         try:
             entry = json.load(open(tp)).get(w.name, {}).get(dom)
             if entry and entry.get("source_hash") == source_hash():
@@ -332,7 +363,8 @@ def main():
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.describe()}; step = {' + '.join(names)}",
+        "config": {"workload": f"{w.name}: {w.describe()}; step = {' + '.join(names)}"
+                               + ("" if drop is None else f"; dropout p={drop[0]} (seed, offset)={DROP_STATE}"),
                    "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
                    "causal": w.causal, "parallelism": "none (1 GPU)"},
         "frac_of_peak": value / PEAK_BF16_TFLOPS,
@@ -345,8 +377,8 @@ def main():
         if args.phase == "bwd":
             fwd()
         torch.cuda.synchronize()
-        out["parity"] = sampled_parity(w, t, o, lse, scale32)
-    if not args.no_cpu_baseline:
+        out["parity"] = sampled_parity(w, t, o, lse, scale32, dropout=drop)
+    if not args.no_cpu_baseline and drop is None:
         out["cpu_baseline"] = cpu_baseline(w, t, scale32, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
