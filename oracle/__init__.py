@@ -48,6 +48,10 @@ def _load():
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_bwd.argtypes = [_dp] * 10 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.oracle_fwd_rect.restype = ctypes.c_int
+    lib.oracle_fwd_rect.argtypes = [_dp] * 5 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_double, ctypes.c_int, _i64p,
+                                                ctypes.c_int64, ctypes.c_int]
     lib.oracle_fwd_dropout.restype = ctypes.c_int
     lib.oracle_fwd_dropout.argtypes = [_dp] * 5 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                    ctypes.c_double, ctypes.c_int, ctypes.c_double,
@@ -126,6 +130,36 @@ def fwd(q, k, v, scale, causal=False, rows=None, threads=None, dropout=None):
                                     int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError("oracle_fwd failed")
+    return o, lse
+
+
+def fwd_rect(q, k, v, scale, causal=False, rows=None, threads=None):
+    """Forward of Nq queries against Nk keys: q [..., Nq, d], k and v
+    [..., Nk, d].  Under the causal mask query i sees keys 0 .. i + Nk - Nq
+    (the queries are the last Nq positions); a row that sees no key gets
+    o = 0 and lse = -inf.  rows as for :func:`fwd` (ids bh * Nq + i)."""
+    lib = _load()
+    q, k, v = _c(q), _c(k), _c(v)
+    lead, Nq, d = q.shape[:-2], q.shape[-2], q.shape[-1]
+    Nk = k.shape[-2]
+    if k.shape[:-2] != lead or k.shape[-1] != d or v.shape != k.shape:
+        raise ValueError("k, v must be [..., Nk, d] with q's leading dims and d")
+    BH = int(np.prod(lead)) if lead else 1
+    if rows is None:
+        o = np.empty(q.shape, np.float64)
+        lse = np.empty(q.shape[:-1], np.float64)
+        rp, nr = None, BH * Nq
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = rows.size
+        o = np.empty((nr, d), np.float64)
+        lse = np.empty((nr,), np.float64)
+        rp = rows.ctypes.data_as(_i64p)
+    rc = lib.oracle_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, Nq, Nk, d,
+                             float(scale), int(bool(causal)), rp, nr,
+                             int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle_fwd_rect failed")
     return o, lse
 
 

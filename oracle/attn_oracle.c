@@ -45,6 +45,12 @@
  *    serve the pages' worked examples (the 8-score chunked softmax, and the
  *    Step 6 exactness check of tiled against standard attention).
  *
+ *  - oracle_fwd_rect: the forward definition for Nq queries against Nk keys
+ *    per head, the shape of Flash-Decoding (a few new queries against a long
+ *    key/value cache; explainer "Common questions").  Under the causal mask
+ *    the queries are the last Nq positions: query i sees keys 0 .. i+Nk-Nq
+ *    (a row that sees none gets o = 0, lse = -inf).
+ *
  *  - oracle_fwd_dropout / oracle_bwd_dropout: the same two computations with
  *    dropout on the attention probabilities, which the pages fuse into the
  *    kernel and whose mask the backward regenerates from the PRNG state the
@@ -142,20 +148,25 @@ int oracle_dropout_keep(double p, uint64_t seed, uint32_t offset, int64_t bh, in
     return 0;
 }
 
-/* Number of keys row i may attend to: all N, or i+1 under the causal mask. */
-static int64_t keys_for_row(int64_t i, int64_t N, int causal) {
-    return causal ? (i + 1) : N;
+/* Number of keys query row i may attend to: all Nk, or under the causal
+ * mask keys 0 .. i + Nk - Nq (the Nq queries are the last Nq positions of
+ * the Nk keys; i + 1 when Nq = Nk), none when that is negative. */
+static int64_t keys_for_row(int64_t i, int64_t Nq, int64_t Nk, int causal) {
+    if (!causal) return Nk;
+    const int64_t n = i + Nk - Nq + 1;
+    return n < 0 ? 0 : (n > Nk ? Nk : n);
 }
 
 /* One query row of the forward definition.
- * qi: d values; kh, vh: N x d of this (batch, head); s: scratch of N doubles;
- * dr: dropout state or NULL, bh the head's index (for the dropout mask).
- * Writes oi (d values) and *lse_i. */
+ * qi: d values; kh, vh: Nk x d of this (batch, head); s: scratch of Nk
+ * doubles; dr: dropout state or NULL, bh the head's index (for the dropout
+ * mask).  Writes oi (d values) and *lse_i; a row that sees no key gets
+ * o = 0 and lse = -inf. */
 static void fwd_row(const double* qi, const double* kh, const double* vh,
-                    int64_t i, int64_t N, int64_t d, double scale, int causal,
+                    int64_t i, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
                     const struct drop* dr, int64_t bh,
                     double* s, double* oi, double* lse_i) {
-    int64_t nk = keys_for_row(i, N, causal);
+    int64_t nk = keys_for_row(i, Nq, Nk, causal);
     /* scores s_j = scale * q_i . k_j */
     for (int64_t j = 0; j < nk; ++j) {
         double acc = 0.0;
@@ -192,15 +203,15 @@ static void fwd_row(const double* qi, const double* kh, const double* vh,
  */
 static int fwd_rows(const double* q, const double* k, const double* v,
                     double* o, double* lse,
-                    int64_t BH, int64_t N, int64_t d, double scale, int causal,
+                    int64_t BH, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
                     const struct drop* dr,
                     const int64_t* rows, int64_t n_rows, int threads) {
-    if (!q || !k || !v || !o || !lse || BH < 0 || N < 0 || d <= 0) return -1;
-    if (!rows) n_rows = BH * N;
+    if (!q || !k || !v || !o || !lse || BH < 0 || Nq < 0 || Nk < 0 || d <= 0) return -1;
+    if (!rows) n_rows = BH * Nq;
     if (n_rows < 0) return -1;
     if (rows)
         for (int64_t t = 0; t < n_rows; ++t)
-            if (rows[t] < 0 || rows[t] >= BH * N) return -1;
+            if (rows[t] < 0 || rows[t] >= BH * Nq) return -1;
 #ifdef _OPENMP
     if (threads <= 0) threads = omp_get_max_threads();
 #else
@@ -209,17 +220,17 @@ static int fwd_rows(const double* q, const double* k, const double* v,
     int failed = 0;
 #pragma omp parallel num_threads(threads) reduction(| : failed)
     {
-        double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
         if (!s) {
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 16)
             for (int64_t t = 0; t < n_rows; ++t) {
                 int64_t r = rows ? rows[t] : t;
-                int64_t bh = r / N, i = r % N;
-                const double* kh = k + bh * N * d;
-                const double* vh = v + bh * N * d;
-                fwd_row(q + r * d, kh, vh, i, N, d, scale, causal, dr, bh, s, o + t * d, lse + t);
+                int64_t bh = r / Nq, i = r % Nq;
+                const double* kh = k + bh * Nk * d;
+                const double* vh = v + bh * Nk * d;
+                fwd_row(q + r * d, kh, vh, i, Nq, Nk, d, scale, causal, dr, bh, s, o + t * d, lse + t);
             }
             free(s);
         }
@@ -231,7 +242,17 @@ int oracle_fwd(const double* q, const double* k, const double* v,
                double* o, double* lse,
                int64_t BH, int64_t N, int64_t d, double scale, int causal,
                const int64_t* rows, int64_t n_rows, int threads) {
-    return fwd_rows(q, k, v, o, lse, BH, N, d, scale, causal, NULL, rows, n_rows, threads);
+    return fwd_rows(q, k, v, o, lse, BH, N, N, d, scale, causal, NULL, rows, n_rows, threads);
+}
+
+/* oracle_fwd_rect: oracle_fwd with Nq query rows against Nk keys per head
+ * (q, o: [BH, Nq, d]; k, v: [BH, Nk, d]; lse: [BH, Nq]; row ids bh * Nq + i).
+ * Under the causal mask query i sees keys 0 .. i + Nk - Nq. */
+int oracle_fwd_rect(const double* q, const double* k, const double* v,
+                    double* o, double* lse,
+                    int64_t BH, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                    const int64_t* rows, int64_t n_rows, int threads) {
+    return fwd_rows(q, k, v, o, lse, BH, Nq, Nk, d, scale, causal, NULL, rows, n_rows, threads);
 }
 
 /* oracle_fwd_dropout: oracle_fwd with dropout probability p (quantised to
@@ -243,7 +264,7 @@ int oracle_fwd_dropout(const double* q, const double* k, const double* v,
                        const int64_t* rows, int64_t n_rows, int threads) {
     struct drop dr;
     if (drop_init(&dr, p, seed, offset)) return -1;
-    return fwd_rows(q, k, v, o, lse, BH, N, d, scale, causal, &dr, rows, n_rows, threads);
+    return fwd_rows(q, k, v, o, lse, BH, N, N, d, scale, causal, &dr, rows, n_rows, threads);
 }
 
 /*
@@ -293,11 +314,11 @@ static int bwd_heads(const double* q, const double* k, const double* v, const do
                 memset(dkh, 0, sizeof(double) * (size_t)(N * d));
                 memset(dvh, 0, sizeof(double) * (size_t)(N * d));
                 for (int64_t i = 0; i < N; ++i) {
-                    int64_t nk = keys_for_row(i, N, causal);
+                    int64_t nk = keys_for_row(i, N, N, causal);
                     const double* qi = qh + i * d;
                     const double* gi = gh + i * d;
                     /* forward quantities of this row: o_i and lse_i */
-                    fwd_row(qi, kh, vh, i, N, d, scale, causal, dr, bh, s, oh + i * d, lh + i);
+                    fwd_row(qi, kh, vh, i, N, N, d, scale, causal, dr, bh, s, oh + i * d, lh + i);
                     /* s was overwritten by fwd_row with the scaled scores; P from
                      * lse, and the weights W applied to V (W = P without dropout) */
                     for (int64_t j = 0; j < nk; ++j) {
@@ -409,7 +430,7 @@ int oracle_fwd_online(const double* q, const double* k, const double* v,
     double* s = (double*)malloc(sizeof(double) * (size_t)(tile));
     if (!s) return -1;
     for (int64_t i = 0; i < N; ++i) {
-        int64_t nk = keys_for_row(i, N, causal);
+        int64_t nk = keys_for_row(i, N, N, causal);
         double m = -INFINITY, l = 0.0;
         double* oi = o + i * d;
         for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;

@@ -167,3 +167,24 @@ def bwd_dropout(q, k, v, dO, scale, causal, p, seed, offset):
     dq = scale * (ds @ k)
     dk = scale * (np.swapaxes(ds, -1, -2) @ q)
     return o, lse, dq, dk, dv
+
+
+def fwd_rect(q, k, v, scale, causal=False):
+    """Materialised forward of Nq queries against Nk keys ([BH, Nq, d] and
+    [BH, Nk, d]); under the causal mask query i sees keys j <= i + Nk - Nq.
+    Rows with no visible key get o = 0 and lse = -inf.  Returns (o, lse)."""
+    q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+    Nq, Nk = q.shape[-2], k.shape[-2]
+    s = scale * (q @ np.swapaxes(k, -1, -2))
+    if causal:
+        keep = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
+    else:
+        keep = np.ones((Nq, Nk), dtype=bool)
+    s = np.where(keep, s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    seen = np.isfinite(m)
+    e = np.where(seen, np.exp(s - np.where(seen, m, 0.0)), 0.0)
+    l = e.sum(axis=-1, keepdims=True)
+    o = np.where(seen, (e @ v) / np.where(seen, l, 1.0), 0.0)
+    lse = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)[..., 0]
+    return o, lse

@@ -485,3 +485,64 @@ def test_dropout_delta_identity(causal):
     _, _, dq2, dk2, dv2 = oracle.bwd(q, k, v, dO, 0.6, causal, o_in=o, dropout=drop)
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert np.abs(a - b).max() <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# Queries and keys of different lengths (Flash-Decoding's shape: a few new
+# queries against a long key/value cache; explainer "Common questions").
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rect_square_is_plain_forward(causal):
+    """Nq = Nk is the square definition, bit for bit."""
+    shape = (2, 3, 41, 8)
+    q, k, v = (rand(shape, s) for s in (80, 81, 82))
+    o, lse = oracle.fwd(q, k, v, 0.3, causal)
+    o2, lse2 = oracle.fwd_rect(q, k, v, 0.3, causal)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+@pytest.mark.parametrize("Nq", [1, 5, 64])
+def test_rect_queries_are_the_last_positions(Nq):
+    """Under the causal mask, Nq queries against Nk keys are the last Nq rows
+    of the square problem whose queries continue the same sequence: this pins
+    the mask's alignment."""
+    Nk, d = 64, 8
+    q_all, k, v = (rand((2, Nk, d), s) for s in (83, 84, 85))
+    o_sq, lse_sq = oracle.fwd(q_all, k, v, 0.4, True)
+    o, lse = oracle.fwd_rect(q_all[:, Nk - Nq:], k, v, 0.4, True)
+    assert np.abs(o - o_sq[:, Nk - Nq:]).max() <= 1e-13
+    assert np.abs(lse - lse_sq[:, Nk - Nq:]).max() <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 50), (7, 50), (50, 7), (33, 100)])
+def test_rect_vs_brute(causal, Nq, Nk):
+    """Row by row C oracle against the materialised rectangular softmax,
+    including rows that see no key (Nq > Nk, causal): o = 0, lse = -inf."""
+    rng = np.random.default_rng(86)
+    q = rng.standard_normal((3, Nq, 8))
+    k, v = (rng.standard_normal((3, Nk, 8)) for _ in range(2))
+    o, lse = oracle.fwd_rect(q, k, v, 0.5, causal)
+    ob, lb = brute.fwd_rect(q, k, v, 0.5, causal)
+    assert np.abs(o - ob).max() <= 1e-12
+    fin = np.isfinite(lb)
+    np.testing.assert_array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - lb[fin]).max(initial=0.0) <= 1e-12
+    if causal and Nq > Nk:
+        assert (~fin).sum() == 3 * (Nq - Nk) and (o[~fin] == 0).all()
+
+
+def test_rect_single_query_sees_every_key():
+    """One query at the end of the sequence sees all keys under either mask,
+    and equals the softmax-weighted mean written out directly."""
+    rng = np.random.default_rng(87)
+    q = rng.standard_normal((1, 1, 6))
+    k, v = (rng.standard_normal((1, 300, 6)) for _ in range(2))
+    oc, lc = oracle.fwd_rect(q, k, v, 0.7, True)
+    on, ln = oracle.fwd_rect(q, k, v, 0.7, False)
+    s = 0.7 * (k[0] @ q[0, 0])
+    w = np.exp(s - s.max())
+    np.testing.assert_allclose(oc[0, 0], (w[:, None] * v[0]).sum(0) / w.sum(), rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(oc, on)
+    np.testing.assert_array_equal(lc, ln)
