@@ -68,6 +68,8 @@ def _load():
     lib.attn_fwd_split_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_fwd_split.restype = i32
     lib.attn_fwd_split.argtypes = [vp] * 6 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, i32, vp]
+    lib.attn_fwd_decode.restype = i32
+    lib.attn_fwd_decode.argtypes = [vp] * 6 + [sz, i64, i64, i64, i64, i64, f32, i32, i32, i32, i32, vp]
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_bwd.restype = i32
@@ -106,6 +108,13 @@ def attn_fwd_split(q: int, k: int, v: int, o: int, lse: int, workspace: int, wor
                    out_dtype: int, nsplit: int, stream: int) -> int:
     return _load().attn_fwd_split(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
                                   causal, dtype, out_dtype, nsplit, stream)
+
+
+def attn_fwd_decode(q: int, k: int, v: int, o: int, lse: int, workspace: int, workspace_bytes: int,
+                    B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int, dtype: int,
+                    out_dtype: int, nsplit: int, stream: int) -> int:
+    return _load().attn_fwd_decode(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                                   scale, causal, dtype, out_dtype, nsplit, stream)
 
 
 def attn_bwd_workspace_size(B: int, H: int, N: int, d: int, dtype: int) -> int:
@@ -256,6 +265,41 @@ def forward_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: boo
                         _OUT_CODE[od], int(nsplit), _stream(q))
     if st != 0:
         raise AttnError(st, "attn_fwd_split")
+    return o, lse
+
+
+def forward_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                   scale: Optional[float] = None, nsplit: int = 8,
+                   out_dtype: Optional[torch.dtype] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split K/V forward of q [B, H, Nq, d] against k, v [B, H, Nk, d]
+    (attn_fwd_decode); under the causal mask the queries are the last Nq
+    positions.  Returns (o [B, H, Nq, d], lse [B, H, Nq] float32)."""
+    _check(q, "q")
+    _check(k, "k")
+    _check(v, "v", k)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-d")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("k, v must be [B, H, Nk, d] with q's B, H and d")
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    od = _out_dtype(q, out_dtype)
+    o = torch.empty(q.shape, dtype=od, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = attn_fwd_split_workspace_size(B, H, Nq, d, int(nsplit))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = attn_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         B, H, Nq, Nk, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
+                         _OUT_CODE[od], int(nsplit), _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_decode")
     return o, lse
 
 

@@ -134,6 +134,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     a.o = o;
     a.lse = lse;
     a.N = int(N);
+    a.Nk = int(N);
+    a.coff = 0;
     const int br = attn::fwd_block_rows();
     a.nqb = int((N + br - 1) / br);
     // causal: one workgroup per pair of query blocks (a heavy and a light one)
@@ -177,31 +179,39 @@ size_t attn_fwd_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d,
     return attn::fwd_split_workspace_bytes(B * H, N, d, nsplit);
 }
 
-int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-                   size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                   int causal, int dtype, int out_dtype, int nsplit, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Split K/V forward of Nq query rows against Nk keys per head (Nq = Nk for
+// attn_fwd_split): partials into the workspace, then the merge.
+int fwd_split_common(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                     int64_t Nk, int64_t d, float scale, int causal, int dtype, int out_dtype,
+                     int nsplit, void* stream) {
+    if (Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
     bool empty = false;
-    int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
+    int st = check_common(B, H, Nq > Nk ? Nq : Nk, d, scale, causal, dtype, out_dtype, &empty);
     if (st != ATTN_OK) return st;
     if (nsplit < 1 || nsplit > ATTN_MAX_SPLIT) return ATTN_ERR_SPLIT;
-    if (empty) return ATTN_OK;
+    if (empty || Nq == 0) return ATTN_OK;
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_ALIGN;
     const int64_t BH = B * H;
-    const size_t need = attn::fwd_split_workspace_bytes(BH, N, d, nsplit);
+    const size_t need = attn::fwd_split_workspace_bytes(BH, Nq, d, nsplit);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-    const size_t tbytes = size_t(BH * N * d) * 2;
-    const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
-    const Range ro = range(o, obytes), rl = range(lse, size_t(BH * N) * 4), rw = range(workspace, need);
-    const Range in[3] = {range(q, tbytes), range(k, tbytes), range(v, tbytes)};
+    const size_t qbytes = size_t(BH * Nq * d) * 2, kbytes = size_t(BH * Nk * d) * 2;
+    const size_t obytes = size_t(BH * Nq * d) * (out_dtype == ATTN_F32 ? 4 : 2);
+    const Range ro = range(o, obytes), rl = range(lse, size_t(BH * Nq) * 4), rw = range(workspace, need);
+    const Range in[3] = {range(q, qbytes), range(k, kbytes), range(v, kbytes)};
     for (const Range& r : in)
         if (overlap(ro, r) || overlap(rl, r) || overlap(rw, r)) return ATTN_ERR_ALIAS;
     if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw)) return ATTN_ERR_ALIAS;
 
     attn::FwdArgs a;
-    const size_t split_o = size_t(BH * N * d), split_lse = size_t(BH * N);
+    const size_t split_o = size_t(BH * Nq * d), split_lse = size_t(BH * Nq);
     float* ws_o = static_cast<float*>(workspace);
     float* ws_lse = ws_o + size_t(nsplit) * split_o;
     a.q = q;
@@ -209,9 +219,11 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
     a.v = v;
     a.o = ws_o;
     a.lse = ws_lse;
-    a.N = int(N);
+    a.N = int(Nq);
+    a.Nk = int(Nk);
+    a.coff = int(Nk - Nq);
     const int br = attn::fwd_block_rows();
-    a.nqb = int((N + br - 1) / br);
+    a.nqb = int((Nq + br - 1) / br);
     const int64_t total = BH * a.nqb * nsplit;
     if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
     a.total = int(total);
@@ -224,9 +236,27 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
     // the partials are fp32 whatever the output type; the merge rounds once
     hipError_t e = attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
-    e = attn::launch_fwd_merge(ws_o, ws_lse, o, lse, BH * N, nsplit, split_o, split_lse, int(d), dtype,
+    e = attn::launch_fwd_merge(ws_o, ws_lse, o, lse, BH * Nq, nsplit, split_o, split_lse, int(d), dtype,
                                out_dtype == ATTN_F32, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                   int causal, int dtype, int out_dtype, int nsplit, void* stream) {
+    return fwd_split_common(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, N, d, scale, causal,
+                            dtype, out_dtype, nsplit, stream);
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    float scale, int causal, int dtype, int out_dtype, int nsplit, void* stream) {
+    return fwd_split_common(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale,
+                            causal, dtype, out_dtype, nsplit, stream);
 }
 
 size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {

@@ -122,7 +122,9 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     // K ring (RING tiles), then V ring (RING tiles)
     __shared__ __attribute__((aligned(1024))) char smem[2 * RING * TILE];
 
-    const int N = a.N;
+    const int N = a.N;                  // query rows per head
+    const int Nk = a.Nk;                // keys per head
+    const int coff = a.coff;            // causal: row i sees keys 0 .. i + coff
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int l32 = lane & 31, h = lane >> 5;
@@ -165,11 +167,12 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     for (int item = 0; item < nitems; ++item) {
         const int qb = item == 0 ? qb_first : qb_second;
         const int q0 = qb * BR;
-        const size_t head = (size_t)bh * N * D;
+        const size_t head = (size_t)bh * N * D;        // q and o of this head
+        const size_t khead = (size_t)bh * Nk * D;      // k and v of this head
         const T* __restrict__ Qh = (const T*)a.q + head;
-        const unsigned head_bytes = (unsigned)N * ROWB;
-        const char* const kbase = (const char*)((const T*)a.k + head);
-        const char* const vbase = (const char*)((const T*)a.v + head);
+        const unsigned head_bytes = (unsigned)Nk * ROWB;
+        const char* const kbase = (const char*)((const T*)a.k + khead);
+        const char* const vbase = (const char*)((const T*)a.v + khead);
 
         // This lane's query rows and their Q fragments (B operands of S^T = K Q^T).
         const int qlo = q0 + 32 * QB * w;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             }
         }
 
-        const int kend = CAUSAL ? min(N, q0 + BR) : N;
+        const int kend = CAUSAL ? max(0, min(Nk, q0 + BR + coff)) : Nk;
         const int ntiles = (kend + BC - 1) / BC;   // tiles the block's rows can see
         // The tiles of this work item, tb .. te-1: all of the block's, or one
         // chunk of them under split K/V (possibly none); keys from klim on are
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         auto apply_mask = [&](Scores& sc, int j0) __attribute__((always_inline)) {
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
-                const int lim = (CAUSAL ? min(klim - 1, qrow[r]) : klim - 1) - j0 - 4 * h;
+                const int lim = (CAUSAL ? min(klim - 1, qrow[r] + coff) : klim - 1) - j0 - 4 * h;
     #pragma unroll
                 for (int b = 0; b < KB; ++b)
     #pragma unroll
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             constexpr int j = decltype(J)::value;   // t % RING
             const int j0 = (tb + t) * BC;
             tile_j0 = j0;
-            const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo);
+            const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo + coff);
             uint64_t upd_mask = 0;
             issue(kbase, tb + t + KLEAD, (j + KLEAD) % RING);
             issue(vbase, tb + t + VLEAD, RING + (j + VLEAD) % RING);

@@ -26,7 +26,9 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int N;        // sequence length
+    int N;        // query rows per (batch, head)
+    int Nk;       // keys per (batch, head) (N for self-attention)
+    int coff;     // causal offset Nk - N: query row i sees keys 0 .. i + coff
     int nqb;      // query blocks per (batch, head)
     int total;    // workgroups: B * H * nqb, or B * H * ceil(nqb / 2) under causal masking
     float c;      // |scale| * log2(e): exponent units of the kernel

@@ -139,6 +139,33 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
+ * attn_fwd_decode -- the split K/V forward for Nq query rows against Nk keys
+ * per head, the shape Flash-Decoding is for: a few new queries against a
+ * long key/value cache, whose keys are split over many workgroups
+ * (explainer "Common questions").  For every (b, h) and query row i, with
+ * A(i) = {0..Nk-1}, or under the causal mask {0 .. i + Nk - Nq} (the queries
+ * are the last Nq positions of the sequence; i's own key is Nk - Nq + i):
+ *     o_i = sum_{j in A(i)} exp(s_ij - m_i) v_j / l_i,  lse_i = m_i + ln(l_i)
+ * as for attn_fwd; a row with A(i) empty (causal, Nq > Nk) gets o_i = 0 and
+ * lse_i = -inf.  With Nq = Nk this is attn_fwd_split.
+ *
+ *   q, o    : [B, H, Nq, d] (q of `dtype`, o of `out_dtype`)
+ *   k, v    : [B, H, Nk, d] of `dtype`
+ *   lse     : [B, H, Nq] float
+ *   workspace, workspace_bytes : at least
+ *             attn_fwd_split_workspace_size(B, H, Nq, d, nsplit) bytes,
+ *             16-byte aligned, overlapping no input or output
+ *   nsplit  : chunks of each query block's keys, 1 .. ATTN_MAX_SPLIT
+ *   the rest: as for attn_fwd; Nq, Nk >= 0 (Nq = 0 does nothing),
+ *             Nq * d and Nk * d below 2^30
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                    int64_t Nk, int64_t d, float scale, int causal, int dtype, int out_dtype,
+                    int nsplit, void* stream);
+
+/*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
  * these sizes (0 when there is nothing to do; otherwise a multiple of 256).
  * Returns 0 for invalid arguments as well; attn_bwd validates them.

@@ -31,9 +31,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dropout",
-                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_dropout",
-                                    "attn_fwd_split", "attn_fwd_split_workspace_size",
-                                    "attn_status_str"]
+                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode",
+                                    "attn_fwd_dropout", "attn_fwd_split",
+                                    "attn_fwd_split_workspace_size", "attn_status_str"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -261,3 +261,34 @@ def test_dropout_shared_validation(kw, code):
 ])
 def test_dropout_backward_validation(kw, code):
     assert bwd_drop(**kw) == code
+
+
+def fwd_decode(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], wsb=None, B=2, H=3, Nq=4, Nk=1000,
+             d=128, scale=0.1, causal=1, dtype=1, out_dtype=None, nsplit=8, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    wsb = a["wsb"]
+    if wsb is None:
+        wsb = attn.attn_fwd_split_workspace_size(a["B"], a["H"], max(a["Nq"], 1), a["d"], a["nsplit"])
+    return attn.attn_fwd_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], wsb, a["B"],
+                                a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                a["dtype"], od, a["nsplit"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nq=-1), E_SHAPE), (dict(Nk=-5), E_SHAPE), (dict(Nk=2**23), E_SHAPE),
+    (dict(nsplit=0), E_SPLIT), (dict(nsplit=65), E_SPLIT), (dict(ws=0), E_WS), (dict(wsb=64), E_WS),
+    (dict(k=0), E_NULL), (dict(o=P[1]), E_ALIAS), (dict(ws=P[2]), E_ALIAS), (dict(d=32), E_HD),
+    (dict(causal=3), E_CAUSAL), (dict(v=P[2] + 4), E_ALIGN),
+])
+def test_fwd_decode_rejects(kw, code):
+    assert fwd_decode(**kw) == code
+
+
+def test_fwd_decode_empty_is_noop():
+    """No query rows (or no heads) means nothing to do; no keys still has
+    rows to write (o = 0, lse = -inf), so the pointers are checked."""
+    assert fwd_decode(Nq=0, ws=0, wsb=0) == OK
+    assert fwd_decode(B=0) == OK
+    assert fwd_decode(Nk=0, o=0) == E_NULL
