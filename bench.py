@@ -76,6 +76,11 @@ def parse():
     ap.add_argument("--dropout", type=float, default=None, metavar="P",
                     help="time the dropout path instead (attn_fwd_dropout, attn_bwd_dropout) "
                          "with probability P; the backward's two kernels are then timed together")
+    ap.add_argument("--decode", type=int, default=None, metavar="NQ",
+                    help="time a decode step instead: attn_fwd_decode of NQ new queries against "
+                         "a 16384-key cache (B=16, H=32, d=128, bf16, causal), against the HBM "
+                         "roofline")
+    ap.add_argument("--nsplit", type=int, default=8, help="key chunks of the decode step")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output dirs")
     return ap.parse_args()
@@ -203,10 +208,85 @@ def sampled_parity(w, t, o, lse, scale, dropout=None):
             "max_abs_lse": float(np.abs(lg - l_ref).max())}
 
 
+PEAK_HBM_GBS = 8000.0
+
+
+def bench_decode(args):
+    """One decode step per call: attn_fwd_decode (split kernel and merge).
+    Algorithmic bytes: K and V read once, q read, o and lse written, and the
+    fp32 partials written and read back by the merge."""
+    import oracle
+    dev = torch.device("cuda:0")
+    B, H, Nk, d, Nq, ns = 16, 32, 16384, 128, int(args.decode), int(args.nsplit)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    q = torch.randn((B, H, Nq, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    need = attn.attn_fwd_split_workspace_size(B, H, Nq, d, ns)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def call():
+        st = attn.attn_fwd_decode(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, Nq, Nk, d, scale,
+                                  1, attn.ATTN_BF16, attn.ATTN_BF16, ns, sp)
+        if st:
+            raise attn.AttnError(st, "attn_fwd_decode")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    BH = B * H
+    kv = 2 * BH * Nk * d * 2
+    partial = ns * BH * Nq * (d + 1) * 4 * 2
+    byts = kv + BH * Nq * d * 2 * 2 + BH * Nq * 4 + partial
+    ms = float(per.mean())
+    gbs = byts / (ms * 1e-3) / 1e9
+    rows = np.array([0, BH * Nq // 2, BH * Nq - 1], dtype=np.int64)
+    o_ref, l_ref = oracle.fwd_rect(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                   float(np.float32(scale)), True, rows=rows)
+    idx = torch.from_numpy(rows).to(dev)
+    out = {
+        "metric": "decode step: K/V cache read GB/s at 1 GPU + % of HBM peak",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode: B={B} H={H} Nq={Nq} Nk={Nk} d={d} bf16 causal, "
+                               f"nsplit={ns}; step = attn_fwd_decode (split kernel + merge)"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_call": byts,
+                     "call_ms": ms},
+        "parity": {"rows": int(len(rows)),
+                   "max_abs_o": float(np.abs(o.view(-1, d)[idx].double().cpu().numpy() - o_ref).max()),
+                   "max_abs_lse": float(np.abs(lse.view(-1)[idx].double().cpu().numpy() - l_ref).max())},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.workload)
+        return
+    if args.decode is not None:
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        bench_decode(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
