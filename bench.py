@@ -289,8 +289,8 @@ def main():
         bench_decode(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every (batch, head) is independent; see the sharding notes). "
+        print("bench.py measures one GPU and has no multi-GPU path: every (batch, head) "
+              "is independent, so heads shard across GPUs without communication. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
