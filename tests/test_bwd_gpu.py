@@ -160,3 +160,11 @@ def test_workload_full_size():
     report_rounded("full dq", sel(hq), sq, tol, w.torch_dtype)
     report_rounded("full dk", sel(hk), sk, tol, w.torch_dtype)
     report_rounded("full dv", sel(hv), sv, tol, w.torch_dtype)
+
+
+def test_many_heads():
+    """4,097 (batch, head) pairs of 70 rows (a prime-ish count of workgroups
+    for both kernels): every gradient element against the oracle."""
+    q, k, v, dO = (randn((17, 241, 70, 64), torch.bfloat16, 360 + i) for i in range(4))
+    for causal in (False, True):
+        compare(q, k, v, dO, causal, 0.125, "many heads")

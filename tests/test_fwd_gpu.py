@@ -226,3 +226,13 @@ def test_workload_full_size(name):
     o1, _ = attn.forward(qd, kd, vd, causal=w.causal, scale=scale)
     err = (o1[..., 0].float() - 1).abs().max().item()
     assert err <= TOL[w.torch_dtype], err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads(causal):
+    """16,384 (batch, head) pairs of 40 rows: a grid far larger than the chip,
+    with a total not a multiple of the XCD count, checks the mapping from
+    workgroup to (batch, head, block) at scale (every row against the
+    oracle)."""
+    q, k, v = (randn((64, 256, 40, 64), torch.bfloat16, 150 + i) for i in range(3))
+    run_and_compare(q, k, v, causal, 0.125, "many heads")
