@@ -38,6 +38,13 @@
 // walks every tile of its block: tiles past a wave's diagonal are masked
 // entirely and contribute exactly zero.
 //
+// Split K/V (Flash-Decoding, explainer "Common questions"): a work item is one
+// query block and one chunk of its tiles; the item writes its own softmax's
+// normalised O (fp32) and lse to a workspace, and merge_kernel combines the
+// chunks.  Queries and keys may differ in length (a decode step against a
+// key/value cache): the queries are then the last positions of the sequence,
+// and under the causal mask query row i sees keys 0 .. i + (Nk - Nq).
+//
 // Dropout (a separate instantiation): the pages fuse it into the kernel and
 // keep only the generator state for the backward ("13% more FLOPs, 5.7x
 // faster", "The backward pass: recompute instead of read"; explainer Step 3).
