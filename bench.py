@@ -29,6 +29,7 @@ kernel, each counter scaled by the copy's known bytes over its reading.
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -51,10 +52,16 @@ KERNEL_SOURCES = ["exact_io_aware_40_amd/csrc/attn_fwd.hip",
 
 
 def source_hash() -> str:
+    """Hash of the kernel sources with comments removed and whitespace
+    collapsed: it keys the committed counter data, which stays valid across
+    edits of comments and layout only."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -206,9 +213,6 @@ def sampled_parity(w, t, o, lse, scale, dropout=None):
     lg = lse.reshape(-1)[idx].double().cpu().numpy()
     return {"rows": int(len(rows)), "max_abs_o": float(np.abs(og - o_ref).max()),
             "max_abs_lse": float(np.abs(lg - l_ref).max())}
-
-
-PEAK_HBM_GBS = 8000.0
 
 
 def bench_decode(args):
