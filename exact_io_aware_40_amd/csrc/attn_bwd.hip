@@ -45,6 +45,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int V> using IC = std::integral_constant<int, V>;
 
+// lds_wait_upto<2 K>(a, b) for a K in 0..KMAX known only after unrolling.
+template <int KMAX> struct WaitSel2 {
+    static __device__ __forceinline__ void run(int k, i32x4& a, i32x4& b) {
+        if (k >= KMAX) lds_wait_upto<2 * KMAX>(a, b);
+        else WaitSel2<KMAX - 1>::run(k, a, b);
+    }
+};
+template <> struct WaitSel2<0> {
+    static __device__ __forceinline__ void run(int, i32x4& a, i32x4& b) { lds_wait_upto<0>(a, b); }
+};
+
 __host__ __device__ inline int padded_rows(int N) { return (N + PADR - 1) / PADR * PADR; }
 
 template <typename T> __device__ __forceinline__ float to_f32(unsigned short x);
@@ -434,12 +445,16 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
 
     // Per-lane LDS offsets; every read below adds only a compile-time
     // immediate (stage, tensor, half tile) below 64 KiB.
-    int qaddr[DK], kaddr[DK];         // rows l32 (+ this wave's 32 rows) at granule 2kk + h
+    // LDS byte addresses of this lane's Q (dO) and K (V) operand reads: rows l32
+    // (+ this wave's 32 rows) at granule 2kk + h; stage, tensor and V offsets
+    // are added as immediates
+    unsigned qaddr[DK], kaddr[DK];
+    const unsigned lbase = lds_addr(smem);
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
         const int o = t_off<D>(l32, 2 * kk + h);
-        qaddr[kk] = o + 32 * qh * ROWB;
-        kaddr[kk] = o + 32 * kg * ROWB + KOFF;
+        qaddr[kk] = lbase + o + 32 * qh * ROWB;
+        kaddr[kk] = lbase + o + 32 * kg * ROWB + KOFF;
     }
     int toff[2][DB];                  // transposing reads: rows 32qh + 4h + s16/4 (+8)
 #pragma unroll
@@ -469,18 +484,29 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         constexpr bool MASK = decltype(mask)::value;
         const char* sQ = smem + STG * STAGE;
         const char* sG = sQ + TILE;
+        // S = Q K^T and dP = dO V^T: the two chains alternate (step i is
+        // chain i % 2, k-step i / 2), and each step's operand pair is read
+        // DSD steps ahead by inline assembly, waited for explicitly
+        constexpr int NSD = 2 * DK, DSD = 3;
         f32x16 s, dp;
+        i32x4 fa[DSD + 1], fb[DSD + 1];
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            const int kk = i >> 1, g = i & 1;
+            fa[i % (DSD + 1)] = lds_read_b128_asm(qaddr[kk], STG * STAGE + g * TILE);
+            fb[i % (DSD + 1)] = lds_read_b128_asm(kaddr[kk], g * KVB);
+        };
 #pragma unroll
-        for (int kk = 0; kk < DK; ++kk) {
-            const i32x4 qx = *(const i32x4*)(sQ + qaddr[kk]);
-            const i32x4 kx = *(const i32x4*)(smem + kaddr[kk]);
-            s = Elem<T>::mma(bit_cast<v8>(qx), bit_cast<v8>(kx), kk == 0 ? f32x16{} : s);
-        }
+        for (int i = 0; i < DSD; ++i) rd(i);
 #pragma unroll
-        for (int kk = 0; kk < DK; ++kk) {
-            const i32x4 gx = *(const i32x4*)(sG + qaddr[kk]);
-            const i32x4 vx = *(const i32x4*)(smem + KVB + kaddr[kk]);
-            dp = Elem<T>::mma(bit_cast<v8>(gx), bit_cast<v8>(vx), kk == 0 ? f32x16{} : dp);
+        for (int i = 0; i < NSD; ++i) {
+            const int later = min(DSD - 1, NSD - 1 - i);   // pairs read after this one
+            WaitSel2<DSD - 1>::run(later, fa[i % (DSD + 1)], fb[i % (DSD + 1)]);
+            const int kk = i >> 1;
+            if ((i & 1) == 0)
+                s = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? f32x16{} : s);
+            else
+                dp = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? f32x16{} : dp);
+            if (i + DSD < NSD) rd(i + DSD);
         }
         // Dropout: this lane runs the generator call of row 32 qh + l32 and
         // lane half h, whose byte e % 4 of word e / 4 belongs to key
