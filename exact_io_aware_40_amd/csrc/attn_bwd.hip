@@ -55,6 +55,16 @@ template <int KMAX> struct WaitSel2 {
 template <> struct WaitSel2<0> {
     static __device__ __forceinline__ void run(int, i32x4& a, i32x4& b) { lds_wait_upto<0>(a, b); }
 };
+// lds_wait_upto<K>(a) for a K in 0..KMAX known only after unrolling.
+template <int KMAX> struct WaitSel1 {
+    static __device__ __forceinline__ void run(int k, i32x4& a) {
+        if (k >= KMAX) lds_wait_upto<KMAX>(a);
+        else WaitSel1<KMAX - 1>::run(k, a);
+    }
+};
+template <> struct WaitSel1<0> {
+    static __device__ __forceinline__ void run(int, i32x4& a) { lds_wait_upto<0>(a); }
+};
 
 __host__ __device__ inline int padded_rows(int N) { return (N + PADR - 1) / PADR * PADR; }
 
@@ -232,10 +242,12 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
         }
     };
 
-    // K and V rows as A operands (16-byte reads), K^T through transposing reads
-    int roff[DK];
+    // K and V rows as A operands (16-byte reads, LDS byte addresses), K^T
+    // through transposing reads
+    unsigned roff[DK];
+    const unsigned lbase = lds_addr(smem);
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) roff[kk] = t_off<D>(l32, 2 * kk + h);
+    for (int kk = 0; kk < DK; ++kk) roff[kk] = lbase + t_off<D>(l32, 2 * kk + h);
     int toff[2][DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) {
@@ -281,15 +293,25 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
 #pragma unroll
                 for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
             }
+            // S^T = K Q^T and dP^T = V dO^T alternate (step i is chain i % 2,
+            // k-step i / 2); each step's K or V fragment is read DSD steps
+            // ahead by inline assembly and waited for explicitly
+            constexpr int NSD = 2 * DK, DSD = 3;
+            i32x4 fr[DSD + 1];
+            auto rd = [&](int i) __attribute__((always_inline)) {
+                fr[i % (DSD + 1)] = lds_read_b128_asm(roff[i >> 1], STG * 2 * TILE + (i & 1) * TILE + 32 * b * ROWB);
+            };
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) {
-                const i32x4 kx = *(const i32x4*)(sK + roff[kk] + 32 * b * ROWB);
-                s = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
-            }
+            for (int i = 0; i < DSD; ++i) rd(i);
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) {
-                const i32x4 vx = *(const i32x4*)(sV + roff[kk] + 32 * b * ROWB);
-                dp = Elem<T>::mma(bit_cast<v8>(vx), bit_cast<v8>(gf[kk]), kk == 0 ? f32x16{} : dp);
+            for (int i = 0; i < NSD; ++i) {
+                WaitSel1<DSD - 1>::run(min(DSD - 1, NSD - 1 - i), fr[i % (DSD + 1)]);
+                const int kk = i >> 1;
+                if ((i & 1) == 0)
+                    s = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
+                else
+                    dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? f32x16{} : dp);
+                if (i + DSD < NSD) rd(i + DSD);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
