@@ -65,6 +65,16 @@ template <int KMAX> struct WaitSel1 {
 template <> struct WaitSel1<0> {
     static __device__ __forceinline__ void run(int, i32x4& a) { lds_wait_upto<0>(a); }
 };
+// lds_wait_upto<2 K>(a, b) for two 8-byte results.
+template <int KMAX> struct WaitSelT {
+    static __device__ __forceinline__ void run(int k, i32x2& a, i32x2& b) {
+        if (k >= KMAX) lds_wait_upto<2 * KMAX>(a, b);
+        else WaitSelT<KMAX - 1>::run(k, a, b);
+    }
+};
+template <> struct WaitSelT<0> {
+    static __device__ __forceinline__ void run(int, i32x2& a, i32x2& b) { lds_wait_upto<0>(a, b); }
+};
 
 __host__ __device__ inline int padded_rows(int N) { return (N + PADR - 1) / PADR * PADR; }
 
@@ -478,13 +488,14 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         qaddr[kk] = lbase + o + 32 * qh * ROWB;
         kaddr[kk] = lbase + o + 32 * kg * ROWB + KOFF;
     }
-    int toff[2][DB];                  // transposing reads: rows 32qh + 4h + s16/4 (+8)
+    // transposing reads (LDS byte addresses): rows 32qh + 4h + s16/4 (+8)
+    unsigned taddr[2][DB];
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) {
         const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
         const int r0 = 4 * h + (s16 >> 2);
-        toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
-        toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
+        taddr[0][cb] = lbase + t_off<D>(r0, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
+        taddr[1][cb] = lbase + t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
     }
     const int laddr = LOFF + (32 * qh + 4 * h) * 4;   // lse2 / D of this lane's rows
 
@@ -577,20 +588,31 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
             dl0 = pack8_lo<T>(s, 0, db0);
             dl1 = pack8_lo<T>(s, 1, db1);
         }
-        // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles)
+        // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles):
+        // step i is column block i / 4, half (i / 2) % 2, dV for even i and dK
+        // for odd i; its two reads are issued DTR steps ahead
+        constexpr int NTR = 4 * DB, DTR = 3;
+        i32x2 ta[DTR + 1], tb[DTR + 1];
+        auto rdt = [&](int i) __attribute__((always_inline)) {
+            const int cb = i >> 2, q = (i >> 1) & 1, isq = i & 1;
+            const int imm = STG * STAGE + (isq ? 0 : TILE) + 16 * q * ROWB;
+            ta[i % (DTR + 1)] = lds_read_tr16_asm(taddr[0][cb], imm);
+            tb[i % (DTR + 1)] = lds_read_tr16_asm(taddr[1][cb], imm);
+        };
 #pragma unroll
-        for (int cb = 0; cb < DB; ++cb) {
+        for (int i = 0; i < DTR; ++i) rdt(i);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int ro = 16 * q * ROWB;
-                const v8 gt = join8<v8>(lds_read_tr16(sG, toff[0][cb] + ro),
-                                        lds_read_tr16(sG, toff[1][cb] + ro));
-                dv[cb] = Elem<T>::mma(gt, q ? pb1 : pb0, dv[cb]);
-                const v8 qt = join8<v8>(lds_read_tr16(sQ, toff[0][cb] + ro),
-                                        lds_read_tr16(sQ, toff[1][cb] + ro));
-                dk[cb] = Elem<T>::mma(qt, q ? db1 : db0, dk[cb]);
-                if (SPLIT) dk[cb] = Elem<T>::mma(qt, q ? dl1 : dl0, dk[cb]);
+        for (int i = 0; i < NTR; ++i) {
+            WaitSelT<DTR - 1>::run(min(DTR - 1, NTR - 1 - i), ta[i % (DTR + 1)], tb[i % (DTR + 1)]);
+            const int cb = i >> 2, q = (i >> 1) & 1;
+            const v8 op = join8<v8>(bit_cast<i16x4>(ta[i % (DTR + 1)]), bit_cast<i16x4>(tb[i % (DTR + 1)]));
+            if ((i & 1) == 0) {
+                dv[cb] = Elem<T>::mma(op, q ? pb1 : pb0, dv[cb]);
+            } else {
+                dk[cb] = Elem<T>::mma(op, q ? db1 : db0, dk[cb]);
+                if (SPLIT) dk[cb] = Elem<T>::mma(op, q ? dl1 : dl0, dk[cb]);
             }
+            if (i + DTR < NTR) rdt(i + DTR);
         }
     };
 

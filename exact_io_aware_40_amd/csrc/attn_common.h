@@ -230,6 +230,13 @@ __device__ __forceinline__ void lds_wait_upto(i32x4& a) {
     __asm__ volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
 }
 
+// The same wait for two 8-byte results.
+template <int N>
+__device__ __forceinline__ void lds_wait_upto(i32x2& a, i32x2& b) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+    __asm__ volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
 // The same wait for two 16-byte results.
 template <int N>
 __device__ __forceinline__ void lds_wait_upto(i32x4& a, i32x4& b) {
