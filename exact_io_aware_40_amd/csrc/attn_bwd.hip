@@ -198,8 +198,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     const int s16 = lane & 15, grp = lane >> 4;
 
     const int L = xcd_remap(blockIdx.x, total);
-    const int bh = L / nqb;
-    int qb = L - bh * nqb;
+    // (wave-uniform: kept in scalar registers)
+    const int bh = __builtin_amdgcn_readfirstlane(L / nqb);
+    int qb = __builtin_amdgcn_readfirstlane(L - bh * nqb);
     if (CAUSAL) qb = nqb - 1 - qb;     // heaviest query blocks first
     const int q0 = qb * BQ;
     const size_t head = (size_t)bh * N * D;
@@ -342,19 +343,45 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
             }
         }
         // dQ^T += K^T dS^T
+        if constexpr (MASK) {
 #pragma unroll
-        for (int cb = 0; cb < DB; ++cb) {
+            for (int cb = 0; cb < DB; ++cb) {
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                if (MASK && b >= nb) continue;
+                for (int b = 0; b < KB; ++b) {
+                    if (b >= nb) continue;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int ro = (32 * b + 16 * q) * ROWB;
-                    const v8 kt = join8<v8>(lds_read_tr16(sK, toff[0][cb] + ro),
-                                            lds_read_tr16(sK, toff[1][cb] + ro));
-                    acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
-                    if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
+                    for (int q = 0; q < 2; ++q) {
+                        const int ro = (32 * b + 16 * q) * ROWB;
+                        const v8 kt = join8<v8>(lds_read_tr16(sK, toff[0][cb] + ro),
+                                                lds_read_tr16(sK, toff[1][cb] + ro));
+                        acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
+                        if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
+                    }
                 }
+            }
+        } else {
+            // every key block: step i is column block i / (2 KB), key block
+            // (i / 2) % KB, half i % 2; its two transposing reads are issued
+            // DTR steps ahead by inline assembly and waited for explicitly
+            constexpr int NTR = DB * KB * 2, DTR = 2;
+            i32x2 ta[DTR + 1], tb[DTR + 1];
+            const unsigned kl = lds_addr(smem);
+            auto rdt = [&](int i) __attribute__((always_inline)) {
+                const int cb = i / (2 * KB), b = (i >> 1) % KB, q = i & 1;
+                const int imm = STG * 2 * TILE + (32 * b + 16 * q) * ROWB;
+                ta[i % (DTR + 1)] = lds_read_tr16_asm(kl + toff[0][cb], imm);
+                tb[i % (DTR + 1)] = lds_read_tr16_asm(kl + toff[1][cb], imm);
+            };
+#pragma unroll
+            for (int i = 0; i < DTR; ++i) rdt(i);
+#pragma unroll
+            for (int i = 0; i < NTR; ++i) {
+                WaitSelT<DTR - 1>::run(min(DTR - 1, NTR - 1 - i), ta[i % (DTR + 1)], tb[i % (DTR + 1)]);
+                const int cb = i / (2 * KB), b = (i >> 1) % KB, q = i & 1;
+                const v8 kt = join8<v8>(bit_cast<i16x4>(ta[i % (DTR + 1)]), bit_cast<i16x4>(tb[i % (DTR + 1)]));
+                acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
+                if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
+                if (i + DTR < NTR) rdt(i + DTR);
             }
         }
     };
@@ -422,8 +449,9 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     const int s16 = lane & 15, grp = lane >> 4;
 
     const int L = xcd_remap(blockIdx.x, total);
-    const int bh = L / nkb;
-    const int kblk = L - bh * nkb;     // ascending: most queries first under the mask
+    // (wave-uniform: kept in scalar registers)
+    const int bh = __builtin_amdgcn_readfirstlane(L / nkb);
+    const int kblk = __builtin_amdgcn_readfirstlane(L - bh * nkb);   // ascending: most queries first under the mask
     const int kb0 = kblk * BK;
     const size_t head = (size_t)bh * N * D;
     const unsigned head_bytes = (unsigned)N * ROWB;
