@@ -104,6 +104,31 @@ def make_inputs(w: Workload, seed: Optional[int] = None, shape=None) -> Dict[str
     return out
 
 
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor scaled E4M3 codes of a CPU tensor: with a = max |x| (in
+    fp32), the codes are x * (448 / a) rounded to nearest even E4M3 by torch
+    (the product clamped to +-448 first), and descale = a / 448 in fp32, so
+    that decode(code) * descale approximates x.  Returns (codes as a uint8
+    tensor of x's shape, descale as a Python float)."""
+    xf = x.float()
+    amax = float(xf.abs().max())
+    amax = amax if amax > 0 else 1.0
+    s = np.float32(448.0) / np.float32(amax)
+    codes = (xf * float(s)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, float(np.float32(1.0) / s)
+
+
+def make_fp8_inputs(w: Workload, seed: Optional[int] = None, shape=None):
+    """The workload's q, k, v (make_inputs) quantised per tensor to E4M3:
+    returns ({"q", "k", "v"}: uint8 code tensors, (q, k, v) descales)."""
+    src = make_inputs(w, seed, shape)
+    out, desc = {}, []
+    for name in ("q", "k", "v"):
+        out[name], ds = quantize_e4m3(src[name])
+        desc.append(ds)
+    return out, tuple(desc)
+
+
 def checksum(t: torch.Tensor) -> str:
     """sha256 of the tensor's raw bytes (first 16 hex digits)."""
     raw = t.contiguous().view(torch.uint8).numpy().tobytes()

@@ -16,6 +16,9 @@ Two independent implementations live here:
   :func:`fwd_online`.
 * :mod:`oracle.brute` (NumPy, fp64): standard attention with the N x N score
   and probability matrices materialised, for tiny inputs.
+* :mod:`oracle.fp8` (NumPy): decoding of E4M3 inputs from the format's
+  definition, the FP8 forward's definition (the C oracle on the decoded
+  values) and the element-wise error bound of rounding P to E4M3.
 
 Inputs are fp64 NumPy arrays; fp16/bf16 tensors are upcast exactly by the
 caller (every fp16/bf16 value is representable in fp64).
