@@ -9,9 +9,8 @@ d=128, bf16, causal, 1% of K rows x8), inputs resident in HBM.
 Prints ONE JSON line: TFLOP/s of the step (credited FLOPs: forward
 4*B*H*N^2*d/2 under the causal mask, backward 2.5x that), with a per-phase
 and per-kernel breakdown, the roofline of the dominant kernel measured live
-with HIP events on the launch stream, a sampled parity check against the
-fp64 oracle, and the oracle itself timed on the host cores on a bounded
-sample.
+with HIP events on the launch stream, and the fp64 oracle timed on the host
+cores on a bounded sample (its forward rows also compared with the GPU's).
 
 Each kernel has its own entry point (attn_fwd, attn_bwd_dq, attn_bwd_dkdv;
 attn_bwd is the last two in order), so the events bracket one kernel each.
@@ -25,6 +24,11 @@ Counter support: --copy-calibration adds a plain copy of known size
 WRITE_DIR turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
 such a command into profiles/traffic.json: HBM bytes per launch of each
 kernel, each counter scaled by the copy's known bytes over its reading.
+
+Side measurements (not the headline line): --decode NQ times a decode step
+against the HBM roofline, --dropout P the dropout path, and --fp8 the E4M3
+forward (attn_fwd_fp8) on the same workload quantised per tensor, against the
+dense fp8 matrix peak.
 """
 import argparse
 import hashlib
@@ -45,6 +49,7 @@ import exact_io_aware_40_amd as attn  # noqa: E402
 from exact_io_aware_40_amd import inputs  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16/fp16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 matrix peak
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_io_aware_40_amd/csrc/attn_fwd.hip",
                   "exact_io_aware_40_amd/csrc/attn_bwd.hip",
@@ -77,7 +82,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of each oracle sample")
-    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="do not compare the GPU output on the CPU baseline's rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 512 MiB copy (read + write) first, for counter scaling")
     ap.add_argument("--dropout", type=float, default=None, metavar="P",
@@ -88,6 +94,9 @@ def parse():
                          "a 16384-key cache (B=16, H=32, d=128, bf16, causal), against the HBM "
                          "roofline")
     ap.add_argument("--nsplit", type=int, default=8, help="key chunks of the decode step")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the E4M3 forward (attn_fwd_fp8) on the workload quantised per "
+                         "tensor, against the dense fp8 matrix peak")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output dirs")
     return ap.parse_args()
@@ -141,10 +150,12 @@ def write_traffic(fetch_dir, write_dir, workload):
     print(json.dumps(rec[workload], indent=1))
 
 
-def cpu_baseline(w, t, scale, budget_s):
+def cpu_baseline(w, t, scale, budget_s, gpu_out=None):
     """The fp64 oracle on this host's cores over a bounded sample of the
     same workload: query rows drawn from many heads for the forward, whole
     heads for the backward, each sized to about `budget_s` seconds.
+    With gpu_out = (o, lse) of the timed forward, the oracle's rows are also
+    compared with the GPU's (max |gpu - oracle| in the result's "parity").
     Returns the JSON object."""
     import oracle
     cores = oracle.default_threads()
@@ -164,8 +175,16 @@ def cpu_baseline(w, t, scale, budget_s):
     n_rows = int(min(len(heads) * N, max(n_cal, n_cal * budget_s / max(t_cal, 1e-3))))
     rows = rng.choice(len(heads) * N, size=n_rows, replace=False)
     t0 = time.perf_counter()
-    oracle.fwd(qs, ks, vs, scale, w.causal, rows=rows, threads=cores)
+    o_ref, l_ref = oracle.fwd(qs, ks, vs, scale, w.causal, rows=rows, threads=cores)
     t_fwd = time.perf_counter() - t0
+    parity = None
+    if gpu_out is not None:
+        o, lse = gpu_out
+        grow = torch.from_numpy(heads[rows // N] * N + rows % N).to(o.device)
+        og = o.reshape(-1, d)[grow].double().cpu().numpy()
+        lg = lse.reshape(-1)[grow].double().cpu().numpy()
+        parity = {"rows": int(len(rows)), "max_abs_o": float(np.abs(og - o_ref).max()),
+                  "max_abs_lse": float(np.abs(lg - l_ref).max())}
     i = rows % N
     keys = (i + 1) if w.causal else np.full_like(i, N)
     f_fwd = float(np.sum(4.0 * keys * d))
@@ -189,37 +208,17 @@ def cpu_baseline(w, t, scale, budget_s):
                    f"{nh} whole heads (backward, {t_bwd:.1f} s) of {w.name}; fp64, one thread "
                    f"per row or head; credited FLOPs as on the GPU"),
         "fwd_tflops": f_fwd / t_fwd / 1e12, "bwd_tflops": f_bwd / t_bwd / 1e12,
+        **({} if parity is None else {"parity": parity}),
     }
 
 
 DROP_STATE = (2024, 17)   # generator seed and offset of the dropout path
 
 
-def sampled_parity(w, t, o, lse, scale, dropout=None):
-    import oracle
-    BH, N, d = w.B * w.H, w.N, w.d
-    rng = np.random.default_rng(7)
-    heads = [0, BH - 1] + list(rng.choice(BH, size=2, replace=False))
-    rows = []
-    for hd in heads:
-        rows += [hd * N + r for r in (0, N // 2, N - 1)] + list(hd * N + rng.choice(N, 13, replace=False))
-    rows = np.array(sorted(set(rows)), dtype=np.int64)
-    o_ref, l_ref = oracle.fwd(t["q"].reshape(BH, N, d).double().numpy(),
-                              t["k"].reshape(BH, N, d).double().numpy(),
-                              t["v"].reshape(BH, N, d).double().numpy(),
-                              scale, w.causal, rows=rows, dropout=dropout)
-    idx = torch.from_numpy(rows).to(o.device)
-    og = o.reshape(-1, d)[idx].double().cpu().numpy()
-    lg = lse.reshape(-1)[idx].double().cpu().numpy()
-    return {"rows": int(len(rows)), "max_abs_o": float(np.abs(og - o_ref).max()),
-            "max_abs_lse": float(np.abs(lg - l_ref).max())}
-
-
 def bench_decode(args):
     """One decode step per call: attn_fwd_decode (split kernel and merge).
     Algorithmic bytes: K and V read once, q read, o and lse written, and the
     fp32 partials written and read back by the merge."""
-    import oracle
     dev = torch.device("cuda:0")
     B, H, Nk, d, Nq, ns = 16, 32, 16384, 128, int(args.decode), int(args.nsplit)
     g = torch.Generator(device="cpu").manual_seed(11)
@@ -260,10 +259,6 @@ def bench_decode(args):
     byts = kv + BH * Nq * d * 2 * 2 + BH * Nq * 4 + partial
     ms = float(per.mean())
     gbs = byts / (ms * 1e-3) / 1e9
-    rows = np.array([0, BH * Nq // 2, BH * Nq - 1], dtype=np.int64)
-    o_ref, l_ref = oracle.fwd_rect(q.double().numpy(), k.double().numpy(), v.double().numpy(),
-                                   float(np.float32(scale)), True, rows=rows)
-    idx = torch.from_numpy(rows).to(dev)
     out = {
         "metric": "decode step: K/V cache read GB/s at 1 GPU + % of HBM peak",
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -274,29 +269,86 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_call": byts,
                      "call_ms": ms},
-        "parity": {"rows": int(len(rows)),
-                   "max_abs_o": float(np.abs(o.view(-1, d)[idx].double().cpu().numpy() - o_ref).max()),
-                   "max_abs_lse": float(np.abs(lse.view(-1)[idx].double().cpu().numpy() - l_ref).max())},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_fp8(args):
+    """The E4M3 forward, one launch per call, on the workload's inputs
+    quantised per tensor (inputs.make_fp8_inputs); bf16 output.  FLOPs as
+    for the 16-bit forward: 4 B H N^2 d, halved under the causal mask."""
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    if w.d != 128:
+        print("the fp8 forward takes d = 128", file=sys.stderr)
+        sys.exit(2)
+    x, ds = inputs.make_fp8_inputs(w)
+    q, k, v = (x[n].to(dev) for n in "qkv")
+    B, H, N, d = w.B, w.H, w.N, w.d
+    scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def call():
+        st = attn.attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, scale, ds[0], ds[1], ds[2], int(w.causal), attn.ATTN_BF16, sp)
+        if st:
+            raise attn.AttnError(st, "attn_fwd_fp8")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    flops = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
+    ms = float(per.mean())
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "fp8 (E4M3) attention forward TFLOP/s at 1 GPU + % of fp8 MFMA peak",
+        "value": flops / (wall / args.steps) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": f"{w.name} quantised per tensor to E4M3: B={B} H={H} N={N} d={d} "
+                               f"{'causal' if w.causal else 'non-causal'}, bf16 output; "
+                               f"step = fwd_kernel (8-bit)"},
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel<fp8e4m3>", "achieved": tf,
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS,
+                     "traffic": None, "flops_per_launch": flops, "launch_ms": ms,
+                     "launch_ms_min": float(per.min())},
+        "kernel_source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)
 
 
 def main():
     args = parse()
-    if args.traffic:
-        write_traffic(args.traffic[0], args.traffic[1], args.workload)
-        return
-    if args.decode is not None:
-        if not torch.cuda.is_available():
-            print("no GPU visible", file=sys.stderr)
-            sys.exit(1)
-        bench_decode(args)
-        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU and has no multi-GPU path: every (batch, head) "
               "is independent, so heads shard across GPUs without communication. "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.workload)
+        return
+    if args.decode is not None or args.fp8:
+        if not torch.cuda.is_available():
+            print("no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        if args.fp8:
+            bench_fp8(args)
+        else:
+            bench_decode(args)
+        return
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -457,13 +509,10 @@ def main():
         "roofline": roofline,
         "kernel_source_hash": source_hash(),
     }
-    if not args.no_parity:
-        if args.phase == "bwd":
-            fwd()
-        torch.cuda.synchronize()
-        out["parity"] = sampled_parity(w, t, o, lse, scale32, dropout=drop)
     if not args.no_cpu_baseline and drop is None:
-        out["cpu_baseline"] = cpu_baseline(w, t, scale32, args.cpu_seconds)
+        torch.cuda.synchronize()
+        out["cpu_baseline"] = cpu_baseline(w, t, scale32, args.cpu_seconds,
+                                           gpu_out=None if args.no_parity else (o, lse))
     print(json.dumps(out), flush=True)
 
 

@@ -8,9 +8,11 @@ memory and the current stream.
 Low level (same names and argument order as the C ABI, raw integers and
 device pointers):  :func:`attn_fwd`, :func:`attn_fwd_split`,
 :func:`attn_fwd_split_workspace_size`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
-:func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`, :func:`attn_status_str`.
+:func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`, :func:`attn_fwd_fp8`,
+:func:`attn_status_str`.
 
-Tensor level:  :func:`forward`, :func:`forward_split` and :func:`backward`.
+Tensor level:  :func:`forward`, :func:`forward_split`, :func:`forward_decode`,
+:func:`forward_fp8` and :func:`backward`.
 """
 from __future__ import annotations
 
@@ -24,8 +26,8 @@ import torch
 __all__ = [
     "attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_size",
     "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
-    "attn_status_str",
-    "forward", "forward_split", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
+    "attn_fwd_fp8", "attn_status_str",
+    "forward", "forward_split", "forward_decode", "forward_fp8", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
 ]
 
 ATTN_F16 = 0
@@ -84,6 +86,8 @@ def _load():
     lib.attn_bwd_dropout.restype = i32
     lib.attn_bwd_dropout.argtypes = [vp] * 10 + [sz, i64, i64, i64, i64, f32, i32, f32, u64, u32, i32,
                                                  i32, vp]
+    lib.attn_fwd_fp8.restype = i32
+    lib.attn_fwd_fp8.argtypes = [vp] * 5 + [i64, i64, i64, i64, f32, f32, f32, f32, i32, i32, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -156,6 +160,13 @@ def attn_bwd_dropout(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int,
     return _load().attn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes,
                                     B, H, N, d, scale, causal, dropout_p, seed, offset, dtype,
                                     out_dtype, stream)
+
+
+def attn_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+                 scale: float, q_descale: float, k_descale: float, v_descale: float, causal: int,
+                 out_dtype: int, stream: int) -> int:
+    return _load().attn_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale,
+                                causal, out_dtype, stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -232,6 +243,49 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
                               _DTYPE_CODE[q.dtype], _OUT_CODE[od], _stream(q))
     if st != 0:
         raise AttnError(st, "attn_fwd" if dropout is None else "attn_fwd_dropout")
+    return o, lse
+
+
+_FP8_TYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def forward_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                descale: Tuple[float, float, float] = (1.0, 1.0, 1.0), causal: bool = False,
+                scale: Optional[float] = None, out_dtype: torch.dtype = torch.bfloat16,
+                out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward with E4M3 inputs (attn_fwd_fp8).  q, k, v: [B, H, N, 128] GPU
+    tensors of E4M3 codes (torch.float8_e4m3fn, or their bytes as uint8),
+    standing for code * descale[i].  Returns (o [B, H, N, 128] of out_dtype
+    (float16, bfloat16 or float32), lse [B, H, N] float32); scale defaults
+    to 1/sqrt(d).  The work is enqueued on torch's current stream."""
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dtype not in _FP8_TYPES:
+        raise ValueError(f"q, k, v must hold E4M3 codes (float8_e4m3fn or uint8), got {q.dtype}")
+    if out_dtype not in _OUT_CODE:
+        raise ValueError(f"out_dtype must be float16, bfloat16 or float32, got {out_dtype}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    od = out_dtype if out is None else out[0].dtype
+    if od not in _OUT_CODE:
+        raise ValueError(f"o must be float16, bfloat16 or float32, got {od}")
+    if out is None:
+        o = torch.empty(q.shape, dtype=od, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _check(o, "o", q, od)
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous float32 [B, H, N]")
+    qd, kd, vd = (float(x) for x in descale)
+    st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, float(scale), qd, kd, vd, int(bool(causal)), _OUT_CODE[od], _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
     return o, lse
 
 

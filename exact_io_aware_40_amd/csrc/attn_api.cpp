@@ -71,7 +71,7 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: pointers must be 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
         case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
-        case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale must be finite";
+        case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale must be finite (descale factors finite and > 0)";
         case ATTN_ERR_CAUSAL: return "ATTN_ERR_CAUSAL: causal must be 0 or 1";
         case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS: an output overlaps an input or another output";
         case ATTN_ERR_SPLIT: return "ATTN_ERR_SPLIT: nsplit must be in 1 .. ATTN_MAX_SPLIT";
@@ -148,6 +148,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     a.split_o = 0;
     a.split_lse = 0;
     a.drop = drop;
+    a.oscale = 1.f;
     hipError_t e = attn::launch_fwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
                                     (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -170,6 +171,57 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float
     const int st = drop_args(dropout_p, seed, offset, &dr);
     if (st != ATTN_OK) return st;
     return fwd_common(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, out_dtype, dr, stream);
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                 int64_t H, int64_t N, int64_t d, float scale, float q_descale, float k_descale,
+                 float v_descale, int causal, int out_dtype, void* stream) {
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+    if (d != 128) return ATTN_ERR_HEAD_DIM;
+    if (out_dtype != ATTN_F16 && out_dtype != ATTN_BF16 && out_dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+    const float qk = scale * q_descale * k_descale;   // the scores' scale
+    if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale) ||
+        !(q_descale > 0.f) || !(k_descale > 0.f) || !(v_descale > 0.f) || !isfinite(qk))
+        return ATTN_ERR_SCALE;
+    bool empty = false;
+    const int st = check_common(B, H, N, d, qk, causal, ATTN_BF16, ATTN_BF16, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const size_t tbytes = size_t(BH * N * d);
+    const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
+    const Range ro = range(o, obytes), rl = range(lse, size_t(BH * N) * 4);
+    const Range in[3] = {range(q, tbytes), range(k, tbytes), range(v, tbytes)};
+    for (const Range& r : in)
+        if (overlap(ro, r) || overlap(rl, r)) return ATTN_ERR_ALIAS;
+    if (overlap(ro, rl)) return ATTN_ERR_ALIAS;
+
+    attn::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.N = int(N);
+    a.Nk = int(N);
+    a.coff = 0;
+    const int br = attn::fwd_block_rows();
+    a.nqb = int((N + br - 1) / br);
+    const int64_t total = BH * (causal ? (a.nqb + 1) / 2 : a.nqb);
+    if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
+    a.total = int(total);
+    a.c = exponent_unit(qk);
+    a.negate = qk < 0.f;
+    a.nsplit = 0;
+    a.split_o = 0;
+    a.split_lse = 0;
+    a.drop = no_drop();
+    a.oscale = v_descale;
+    hipError_t e = attn::launch_fwd_fp8(a, out_dtype, causal, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 size_t attn_fwd_split_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int nsplit) {
@@ -233,6 +285,7 @@ int fwd_split_common(const void* q, const void* k, const void* v, void* o, float
     a.split_o = split_o;
     a.split_lse = split_lse;
     a.drop = no_drop();
+    a.oscale = 1.f;
     // the partials are fp32 whatever the output type; the merge rounds once
     hipError_t e = attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;

@@ -110,6 +110,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <> struct Elem<__bf16> {
     typedef bf16x8 v8;
     typedef bf16x4 v4;
+    typedef i32x4 raw;                          // an operand's bits
+    static constexpr int KSTEP = 16;            // k of one product
+    static constexpr unsigned kSign = 0x80008000u;
     static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
@@ -139,6 +142,9 @@ template <> struct Elem<__bf16> {
 template <> struct Elem<_Float16> {
     typedef f16x8 v8;
     typedef f16x4 v4;
+    typedef i32x4 raw;
+    static constexpr int KSTEP = 16;
+    static constexpr unsigned kSign = 0x80008000u;
     static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
@@ -159,6 +165,35 @@ template <> struct Elem<_Float16> {
             acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
         }
         return acc;
+    }
+};
+
+// 8-bit E4M3 elements (the OCP format: sign, 4 exponent bits with bias 7, 3
+// mantissa bits, no infinity; largest value 448), the format of gfx950's
+// 8-bit conversions and of format selector 0 of its 8-bit products.
+struct fp8e4m3 {
+    unsigned char bits;
+};
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <> struct Elem<fp8e4m3> {
+    typedef i32x8 v8;   // 32 elements: one operand of the 32x32x64 product
+    typedef i32x8 raw;
+    static constexpr int KSTEP = 64;
+    static constexpr unsigned kSign = 0x80808080u;
+    // D[32x32] += A[32x64] * B[64x32] (v_mfma_f32_32x32x64_f8f6f4, both
+    // operands E4M3, no block scales).  Lane l holds 32 elements of row l % 32
+    // of A and of column l % 32 of B; which k an element stands for depends
+    // only on l / 32 and its position, the same way for A and B, so a
+    // contraction laid out consistently in both is exact whatever that map is.
+    static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    }
+    // a and b rounded to nearest even E4M3 (|a|, |b| <= 448), written to bytes
+    // 0, 1 (hi false) or 2, 3 (hi true) of w; the other two bytes are kept
+    static __device__ __forceinline__ unsigned cvt2_into(float a, float b, unsigned w, bool hi) {
+        return hi ? (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, true)
+                  : (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, false);
     }
 };
 
@@ -209,6 +244,14 @@ __device__ __forceinline__ i32x4 lds_read_b128_asm(unsigned addr, int off) {
 __device__ __forceinline__ i32x2 lds_read_tr16_asm(unsigned addr, int off) {
     i32x2 r;
     __asm__ volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
+    return r;
+}
+// The 8-bit transposing read: within each group of 16 lanes, lane t receives
+// byte (t % 8) of the 8-byte piece addressed by lane (t % 16) / 8 + 2 j of its
+// group as its byte j, j = 0..7.
+__device__ __forceinline__ i32x2 lds_read_tr8_asm(unsigned addr, int off) {
+    i32x2 r;
+    __asm__ volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(off));
     return r;
 }
 // Wait until at most N LDS operations of this wave are outstanding; the six

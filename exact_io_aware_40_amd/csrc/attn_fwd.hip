@@ -70,7 +70,7 @@ constexpr int BR = 32 * QB * NW;  // query rows per workgroup
 constexpr int NT = 64 * NW;       // threads per workgroup
 constexpr int OCC = 2;            // workgroups per CU
 // keys per K/V tile: 8 KiB tiles
-template <int D> constexpr int bc() { return 8192 / (2 * D); }
+template <typename T, int D> constexpr int bc() { return 8192 / ((int)sizeof(T) * D); }
 // LDS buffers for K tiles, and as many for V tiles, within a workgroup's
 // share of the 160 KiB (an even count)
 constexpr int RING = ((160 * 1024 / OCC) / (2 * 8192)) & ~1;
@@ -79,8 +79,16 @@ constexpr int RING = ((160 * 1024 / OCC) / (2 * 8192)) & ~1;
 // more than kTau binades, so P <= 2^kTau and most tiles skip the rescale of
 // the accumulator.  The bound keeps P representable in the operand type
 // (fp16 holds up to 65504 < 2^16) and far below fp32's range for O and l.
+// With 8-bit E4M3 probabilities (largest value 448) the reference is set
+// kShift binades below the row maximum when it moves and moves once the
+// maximum exceeds it by kTau = 8, so every P is at most 2^8 and the row's
+// largest P, once its tile is in, at least 2^4: E4M3's normal range then
+// covers P down to 2^-10 of the reference.
 template <typename T> constexpr float kTau = 32.f;
 template <> constexpr float kTau<_Float16> = 15.f;
+template <> constexpr float kTau<fp8e4m3> = 8.f;
+template <typename T> constexpr float kShift = 0.f;
+template <> constexpr float kShift<fp8e4m3> = 4.f;
 
 template <int V> using IC = std::integral_constant<int, V>;
 
@@ -100,30 +108,57 @@ template <int KMAX> struct WaitSel3 {
 template <> struct WaitSel3<0> {
     static __device__ __forceinline__ void run(int, i32x4& a, i32x2& b, i32x2& c) { lds_wait_upto<0>(a, b, c); }
 };
+// lds_wait_upto<6 K> likewise (six reads per fragment)
+template <int KMAX> struct WaitSel6 {
+    static __device__ __forceinline__ void run(int k, i32x4& a, i32x4& b, i32x2& c, i32x2& d, i32x2& e,
+                                               i32x2& f) {
+        if (k >= KMAX) lds_wait_upto<6 * KMAX>(a, b, c, d, e, f);
+        else WaitSel6<KMAX - 1>::run(k, a, b, c, d, e, f);
+    }
+};
+template <> struct WaitSel6<0> {
+    static __device__ __forceinline__ void run(int, i32x4& a, i32x4& b, i32x2& c, i32x2& d, i32x2& e,
+                                               i32x2& f) {
+        lds_wait_upto<0>(a, b, c, d, e, f);
+    }
+};
 
 // An empty use of a register value: it must be computed at this point of
 // the program (the compiler would otherwise sink work past later branches).
 template <typename V> __device__ __forceinline__ void materialize(const V& x) {
     __asm__ volatile("" ::"v"(x));
 }
+// (a 32-byte operand as its two 16-byte halves)
+__device__ __forceinline__ void materialize(const i32x8& x) {
+    const i32x4 lo = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    const i32x4 hi = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    __asm__ volatile("" ::"v"(lo), "v"(hi));
+}
 
 template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     typedef typename Elem<T>::v8 v8;
-    constexpr int BC = bc<D>();
+    typedef typename Elem<T>::raw raw;
+    constexpr bool F8 = sizeof(T) == 1;   // E4M3 operands (d = 128, no dropout)
+    static_assert(!F8 || (D == 128 && !DROP), "the 8-bit forward is instantiated for d = 128 only");
+    constexpr int BC = bc<T, D>();
     static_assert(RING >= 4, "the pipeline needs four buffers per tensor");
     constexpr int KLEAD = RING - 1;   // iteration t starts the copy of K(t + KLEAD) ...
     constexpr int VLEAD = RING - 3;   // ... and of V(t + VLEAD)
-    constexpr int ROWB = D * 2;            // bytes per tile row
-    constexpr int GR = D / 8;              // 16-byte granules per row
+    constexpr int ROWB = D * (int)sizeof(T);   // bytes per tile row
+    constexpr int LD = ROWB / 2;           // rows are placed as rows of LD 16-bit elements
+    constexpr int GR = ROWB / 16;          // 16-byte granules per row
     constexpr int TILE = BC * ROWB;        // bytes of one K (or V) tile
     constexpr int LOADS = TILE / (NT * 16);  // 16-byte loads per thread per tile and tensor
     static_assert(LOADS * NT * 16 == TILE, "a tile splits evenly over the workgroup");
+    constexpr int KS = Elem<T>::KSTEP;     // k of one product
     constexpr int KB = BC / 32;            // 32-key blocks per tile
-    constexpr int DK = D / 16;             // k-steps of the S product
+    constexpr int DK = D / KS;             // k-steps of the S product
     constexpr int DB = D / 32;             // 32-wide output column blocks
+    constexpr int VK = BC / KS;            // k-steps of the P.V product
     constexpr int NF = KB * DK;            // K fragments per tile (and as many V fragments)
-    static_assert(NF == DB * KB * 2, "");
+    static_assert(NF == DB * VK, "");
+    constexpr int NG = (int)sizeof(raw) / 16;   // 16-byte granules of one operand
     constexpr int NMM = 2 * QB * NF;       // products per iteration
 
     // K ring (RING tiles), then V ring (RING tiles)
@@ -184,15 +219,15 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // This lane's query rows and their Q fragments (B operands of S^T = K Q^T).
         const int qlo = q0 + 32 * QB * w;
         int qrow[QB];
-        i32x4 qf[QB][DK];
+        raw qf[QB][DK];
     #pragma unroll
         for (int r = 0; r < QB; ++r) {
             qrow[r] = qlo + 32 * r + l32;
     #pragma unroll
             for (int kk = 0; kk < DK; ++kk) {
-                i32x4 x = {0, 0, 0, 0};
-                if (qrow[r] < N) x = *(const i32x4*)(Qh + (size_t)qrow[r] * D + 16 * kk + 8 * h);
-                if (a.negate) x ^= (int)0x80008000;   // scale < 0: use -Q and |scale|
+                raw x = {};
+                if (qrow[r] < N) x = *(const raw*)(Qh + (size_t)qrow[r] * D + KS * kk + (KS / 2) * h);
+                if (a.negate) x ^= (int)Elem<T>::kSign;   // scale < 0: use -Q and |scale|
                 qf[r][kk] = x;
             }
         }
@@ -218,7 +253,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         for (int p = 0; p < LOADS; ++p) {
             const int slot = (p * NW + w) * 64 + lane;
             const int row = slot / GR, pg = slot % GR;
-            src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
+            src_off[p] = (unsigned)(row * ROWB + (pg ^ lds_key<LD>(row)) * 16);
         }
         // The copies of tile t go through a buffer descriptor whose base is the
         // tile's first byte and whose size is what is left of the head (none
@@ -236,16 +271,32 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // Loop-invariant LDS addresses of this lane's operand reads (those of V
         // include the V ring's base); the block, half-tile and buffer parts are
         // added as immediates (the swizzle key depends on the row modulo 16 only).
-        int koff[DK];
+        // (K: row l32 of a 32-key block, the operand's granules of k-step kk)
+        int koff[DK][NG];
     #pragma unroll
-        for (int kk = 0; kk < DK; ++kk) koff[kk] = t_off<D>(l32, 2 * kk + h);
+        for (int kk = 0; kk < DK; ++kk)
+    #pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+                koff[kk][gi] = t_off<LD>(l32, (KS * kk + (KS / 2) * h) * (int)sizeof(T) / 16 + gi);
         int voff[2][DB];
     #pragma unroll
         for (int cb = 0; cb < DB; ++cb) {
-            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-            const int r0 = 4 * h + (s16 >> 2);
-            voff[0][cb] = RING * TILE + t_off<D>(r0, col >> 3) + (col & 7) * 2;
-            voff[1][cb] = RING * TILE + t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+            if constexpr (F8) {
+                // 8-bit transposing reads: lane a of 16-lane group g (a % 16 =
+                // 2 j + pi) addresses row 8 (j / 4) + 4 (g / 2) + j % 4 of a
+                // 16-key group at columns 32 cb + 16 (g % 2) + 8 pi .. +7, so
+                // that the lane at column m of the block receives the keys its
+                // P operand holds (see product)
+                const int jv = s16 >> 1, pv = lane & 1;
+                const int rv = 8 * (jv >> 2) + 4 * (grp >> 1) + (jv & 3);
+                voff[0][cb] = RING * TILE + t_off<LD>(rv, 2 * cb + (grp & 1)) + 8 * pv;
+                voff[1][cb] = voff[0][cb];
+            } else {
+                const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+                const int r0 = 4 * h + (s16 >> 2);
+                voff[0][cb] = RING * TILE + t_off<D>(r0, col >> 3) + (col & 7) * 2;
+                voff[1][cb] = RING * TILE + t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+            }
         }
 
         const float c = a.c;   // > 0 (the host maps a zero scale to the smallest normal unit)
@@ -267,13 +318,20 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < QB; ++r) mc_run[r] = -FLT_MAX, l_run[r] = 0.f, lf_run[r] = 0.f;
 
         typedef f32x16 Scores[QB][KB];   // S^T of one tile, per row block and 32-key block
-        typedef v8 Probs[QB][KB][2];     // P of one tile packed as B operands
+        typedef v8 Probs[QB][VK];        // P of one tile packed as B operands, per k-step
 
         // S^T = K Q^T for the tile in K buffer kb_, row blocks accumulated from
         // each K fragment in turn.
         auto s_frag = [&](int kbuf, int i, Scores& sn) __attribute__((always_inline)) {
             const int b = i % KB, kk = i / KB;
-            const i32x4 kx = *(const i32x4*)(smem + kbuf * TILE + koff[kk] + 32 * b * ROWB);
+            raw kx;
+            if constexpr (NG == 1) {
+                kx = *(const i32x4*)(smem + kbuf * TILE + koff[kk][0] + 32 * b * ROWB);
+            } else {
+                const i32x4 lo = *(const i32x4*)(smem + kbuf * TILE + koff[kk][0] + 32 * b * ROWB);
+                const i32x4 hi = *(const i32x4*)(smem + kbuf * TILE + koff[kk][1] + 32 * b * ROWB);
+                kx = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
     #pragma unroll
             for (int r = 0; r < QB; ++r)
                 sn[r][b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[r][kk]), kk == 0 ? f32x16{} : sn[r][b]);
@@ -302,9 +360,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
         for (int r = 0; r < QB; ++r)
     #pragma unroll
-            for (int b = 0; b < KB; ++b)
-    #pragma unroll
-                for (int q = 0; q < 2; ++q) pA[r][b][q] = v8{};
+            for (int jj = 0; jj < VK; ++jj) pA[r][jj] = v8{};
 
         // An iteration runs in NF steps; step k reads K fragment k and V
         // fragment k and issues 2 QB products: per row block, one of S (for the
@@ -312,39 +368,68 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // DIST steps ahead by inline assembly and waited for explicitly.  The
         // softmax of the current tile is cut into pieces, placed between the
         // products; scheduling fences keep every piece in its slot.
-        constexpr int DIST = QB == 1 ? 4 : 3;
-        struct Frag {
+        constexpr int DIST = F8 ? 3 : QB == 1 ? 4 : 3;   // (8-bit: 6 reads per step, lgkmcnt <= 15)
+        struct Frag16 {
             i32x4 k;
             i32x2 v0, v1;
         };
+        struct Frag8 {
+            i32x4 k, k1;
+            i32x2 v0, v1, v2, v3;
+        };
+        typedef std::conditional_t<F8, Frag8, Frag16> Frag;
         const unsigned lbase = lds_addr(smem);
-        unsigned kaddr[DK];
+        unsigned kaddr[DK][NG];
     #pragma unroll
-        for (int kk = 0; kk < DK; ++kk) kaddr[kk] = lbase + koff[kk];
+        for (int kk = 0; kk < DK; ++kk)
+    #pragma unroll
+            for (int gi = 0; gi < NG; ++gi) kaddr[kk][gi] = lbase + koff[kk][gi];
         unsigned vaddr[2][DB];
     #pragma unroll
         for (int cb = 0; cb < DB; ++cb) vaddr[0][cb] = lbase + voff[0][cb], vaddr[1][cb] = lbase + voff[1][cb];
         auto load_frag = [&](int kbuf, int vbuf, int k, Frag& f) __attribute__((always_inline)) {
             const int b = k % KB, kk = k / KB;
-            f.k = lds_read_b128_asm(kaddr[kk], kbuf * TILE + 32 * b * ROWB);
-            const int cb = k % DB, jj = k / DB, bv = jj >> 1, q = jj & 1;
-            const int roff = vbuf * TILE + (32 * bv + 16 * q) * ROWB;
-            f.v0 = lds_read_tr16_asm(vaddr[0][cb], roff);
-            f.v1 = lds_read_tr16_asm(vaddr[1][cb], roff);
+            f.k = lds_read_b128_asm(kaddr[kk][0], kbuf * TILE + 32 * b * ROWB);
+            const int cb = k % DB, jj = k / DB;
+            if constexpr (F8) {
+                f.k1 = lds_read_b128_asm(kaddr[kk][1], kbuf * TILE + 32 * b * ROWB);
+                const int roff = vbuf * TILE + 64 * jj * ROWB;
+                f.v0 = lds_read_tr8_asm(vaddr[0][cb], roff);
+                f.v1 = lds_read_tr8_asm(vaddr[0][cb], roff + 16 * ROWB);
+                f.v2 = lds_read_tr8_asm(vaddr[0][cb], roff + 32 * ROWB);
+                f.v3 = lds_read_tr8_asm(vaddr[0][cb], roff + 48 * ROWB);
+            } else {
+                const int bv = jj >> 1, q = jj & 1;
+                const int roff = vbuf * TILE + (32 * bv + 16 * q) * ROWB;
+                f.v0 = lds_read_tr16_asm(vaddr[0][cb], roff);
+                f.v1 = lds_read_tr16_asm(vaddr[1][cb], roff);
+            }
         };
         // product m of step k: row block r = m / 2, S for even m, P.V for odd m.
-        // B operand chunk (b, q) of P holds, at k = 8h + e, the probability of
-        // key 32b + 16q + 8(e/4) + 4h + e%4; the transposing reads fetch V at
+        // 16-bit: B operand jj = 2b + q of P holds, at k = 8h + e, the
+        // probability of key 32b + 16q + 8(e/4) + 4h + e%4; 8-bit: B operand jj
+        // holds as its element 16 b' + e (b' = 0, 1) the probability of key
+        // 64 jj + 32 b' + 8(e/4) + 4h + e%4.  The transposing reads fetch V at
         // exactly those keys.
         auto product = [&](int k, int m, const Frag& f, Scores& sn, const Probs& pp) __attribute__((always_inline)) {
             const int r = m >> 1;
             if ((m & 1) == 0) {
                 const int b = k % KB, kk = k / KB;
-                sn[r][b] = Elem<T>::mma(bit_cast<v8>(f.k), bit_cast<v8>(qf[r][kk]), kk == 0 ? f32x16{} : sn[r][b]);
+                raw kx;
+                if constexpr (F8) kx = __builtin_shufflevector(f.k, f.k1, 0, 1, 2, 3, 4, 5, 6, 7);
+                else kx = f.k;
+                sn[r][b] = Elem<T>::mma(bit_cast<v8>(kx), bit_cast<v8>(qf[r][kk]), kk == 0 ? f32x16{} : sn[r][b]);
             } else {
-                const int cb = k % DB, jj = k / DB, bv = jj >> 1, q = jj & 1;
-                const i32x4 vx = __builtin_shufflevector(f.v0, f.v1, 0, 1, 2, 3);
-                oacc[r][cb] = Elem<T>::mma(bit_cast<v8>(vx), pp[r][bv][q], oacc[r][cb]);
+                const int cb = k % DB, jj = k / DB;
+                raw vx;
+                if constexpr (F8) {
+                    const i32x4 v01 = __builtin_shufflevector(f.v0, f.v1, 0, 1, 2, 3);
+                    const i32x4 v23 = __builtin_shufflevector(f.v2, f.v3, 0, 1, 2, 3);
+                    vx = __builtin_shufflevector(v01, v23, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+                    vx = __builtin_shufflevector(f.v0, f.v1, 0, 1, 2, 3);
+                }
+                oacc[r][cb] = Elem<T>::mma(bit_cast<v8>(vx), pp[r][jj], oacc[r][cb]);
             }
         };
 
@@ -363,7 +448,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         constexpr int NP_ROW = NPD + 10 * KB + 1;
         constexpr int NP = QB * NP_ROW;
         float st_mt[QB], st_mold[QB], st_ls[QB], st_lfs[QB];
-        unsigned pw[QB][KB][2][4];
+        constexpr int PWD = (int)sizeof(raw) / 4;   // words of one P operand
+        unsigned pw[QB][VK][PWD];
         unsigned ph[QB][KB][4];   // generator state, then the call's four words
         int tile_j0 = 0;          // first key of the tile being normalised
         auto piece = [&](int p, Scores& sc, uint64_t& upd_mask) __attribute__((always_inline)) {
@@ -400,28 +486,44 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 const float tc = max32(st_mt[r]) * c;
                 const bool upd = tc > mc_run[r] + kTau<T>;
                 st_mold[r] = mc_run[r];
-                mc_run[r] = upd ? tc : mc_run[r];
+                float tnew = tc;
+                if constexpr (kShift<T> != 0.f) tnew = tc - kShift<T>;
+                mc_run[r] = upd ? tnew : mc_run[r];
                 upd_mask |= __builtin_amdgcn_ballot_w64(upd);
             } else {
                 const int q = sx - 2 * KB - 1, b = q / 8, e = 2 * (q % 8);
                 const float x0 = fast_exp2(fmaf(sc[r][b][e], c, -mc_run[r]));
                 const float x1 = fast_exp2(fmaf(sc[r][b][e + 1], c, -mc_run[r]));
-                const unsigned pr = Elem<T>::cvt2(x0, x1);
-                if (q == 0) {
-                    st_lfs[r] = x0 + x1;
-                    st_ls[r] = Elem<T>::sum2(pr, 0.f);
+                if constexpr (F8) {
+                    // bytes (16 (b % 2) + e) % 4, +1 of word 4 (b % 2) + e / 4 of P operand
+                    // b / 2; the row sum is that of the fp32 probabilities
+                    const int jj = b >> 1, wd = 4 * (b & 1) + (e >> 2);
+                    const bool hi = (e >> 1) & 1;
+                    pw[r][jj][wd] = Elem<T>::cvt2_into(x0, x1, hi ? pw[r][jj][wd] : 0u, hi);
+                    if (q == 0) {
+                        st_lfs[r] = x0 + x1;
+                    } else {
+                        st_lfs[r] += x0;
+                        st_lfs[r] += x1;
+                    }
                 } else {
-                    st_lfs[r] += x0;
-                    st_lfs[r] += x1;
-                    st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
-                }
-                if (DROP) {
-                    // elements e, e + 1: bytes e % 4 and e % 4 + 1 of word e / 4
-                    const unsigned wd = ph[r][b][e >> 2];
-                    const bool k0 = drop_keep(wd, e & 3, a.drop.t), k1 = drop_keep(wd, (e & 3) + 1, a.drop.t);
-                    pw[r][b][e / 8][(e % 8) / 2] = Elem<T>::cvt2(k0 ? x0 : 0.f, k1 ? x1 : 0.f);
-                } else {
-                    pw[r][b][e / 8][(e % 8) / 2] = pr;
+                    const unsigned pr = Elem<T>::cvt2(x0, x1);
+                    if (q == 0) {
+                        st_lfs[r] = x0 + x1;
+                        st_ls[r] = Elem<T>::sum2(pr, 0.f);
+                    } else {
+                        st_lfs[r] += x0;
+                        st_lfs[r] += x1;
+                        st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
+                    }
+                    if (DROP) {
+                        // elements e, e + 1: bytes e % 4 and e % 4 + 1 of word e / 4
+                        const unsigned wd = ph[r][b][e >> 2];
+                        const bool k0 = drop_keep(wd, e & 3, a.drop.t), k1 = drop_keep(wd, (e & 3) + 1, a.drop.t);
+                        pw[r][2 * b + e / 8][(e % 8) / 2] = Elem<T>::cvt2(k0 ? x0 : 0.f, k1 ? x1 : 0.f);
+                    } else {
+                        pw[r][2 * b + e / 8][(e % 8) / 2] = pr;
+                    }
                 }
             }
         };
@@ -458,7 +560,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 for (int k = 0; k < NF; ++k) {
                     Frag& cur = f[k % (DIST + 1)];
                     const int later = min(DIST - 1, NF - 1 - k);   // steps read after this one
-                    WaitSel3<DIST - 1>::run(later, cur.k, cur.v0, cur.v1);
+                    if constexpr (F8) WaitSel6<DIST - 1>::run(later, cur.k, cur.k1, cur.v0, cur.v1, cur.v2, cur.v3);
+                    else WaitSel3<DIST - 1>::run(later, cur.k, cur.v0, cur.v1);
                     __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
                     for (int m = 0; m < NS; ++m) {
@@ -474,13 +577,13 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
     #pragma unroll
-                for (int b = 0; b < KB; ++b)
+                for (int jj = 0; jj < VK; ++jj) {
+                    raw x;
     #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const i32x4 x = {(int)pw[r][b][q][0], (int)pw[r][b][q][1], (int)pw[r][b][q][2], (int)pw[r][b][q][3]};
-                        pc[r][b][q] = bit_cast<v8>(x);
-                        materialize(pc[r][b][q]);
-                    }
+                    for (int wd = 0; wd < PWD; ++wd) x[wd] = (int)pw[r][jj][wd];
+                    pc[r][jj] = bit_cast<v8>(x);
+                    materialize(pc[r][jj]);
+                }
             }
             if (upd_mask != 0) [[unlikely]] {
     #pragma unroll
@@ -490,13 +593,13 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                     for (int cb = 0; cb < DB; ++cb)
     #pragma unroll
                         for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha;
-                    l_run[r] *= alpha;
+                    if constexpr (!F8) l_run[r] *= alpha;
                     lf_run[r] *= alpha;
                 }
             }
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
-                l_run[r] += st_ls[r];
+                if constexpr (!F8) l_run[r] += st_ls[r];
                 lf_run[r] += st_lfs[r];
             }
             wait_vmem_upto<INFLIGHT>();
@@ -537,11 +640,19 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
     #pragma unroll
         for (int r = 0; r < QB; ++r) {
-            const float l_tot = sum32(l_run[r]);
-            const float lf_tot = sum32(lf_run[r]);
+            // (8-bit: O is normalised by the fp32 sum and scaled by V's descale)
+            float l_tot, lf_tot;
+            if constexpr (F8) {
+                lf_tot = sum32(lf_run[r]);
+                l_tot = lf_tot;
+            } else {
+                l_tot = sum32(l_run[r]);
+                lf_tot = sum32(lf_run[r]);
+            }
             // a row that sees no key of its chunk (split K/V only) gets O = 0 and
             // lse = -inf, which weigh nothing in the merge
-            const float inv = l_tot > 0.f ? fast_rcp(l_tot) * (DROP ? a.drop.scale : 1.f) : 0.f;
+            float inv = l_tot > 0.f ? fast_rcp(l_tot) * (DROP ? a.drop.scale : 1.f) : 0.f;
+            if constexpr (F8) inv *= a.oscale;
             // (the row index passes through an empty asm statement so that
             // its 64-bit offset is formed here, not kept live through the loop)
             int qr = qrow[r];
@@ -609,10 +720,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 
 template <typename T, typename TO, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    if (a.drop.on)
-        hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL, true>), dim3(a.total), dim3(NT), 0, stream, a);
-    else
+    if constexpr (sizeof(T) == 1) {
         hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL, false>), dim3(a.total), dim3(NT), 0, stream, a);
+    } else {
+        if (a.drop.on)
+            hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL, true>), dim3(a.total), dim3(NT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((fwd_kernel<T, TO, D, CAUSAL, false>), dim3(a.total), dim3(NT), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -651,6 +766,14 @@ hipError_t launch_fwd_merge(const float* ws_o, const float* ws_lse, void* o, flo
                        : launch_merge_t<__bf16, 128>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream);
     return d == 64 ? launch_merge_t<_Float16, 64>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream)
                    : launch_merge_t<_Float16, 128>(ws_o, ws_lse, o, lse, rows, nsplit, split_o, split_lse, stream);
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, int out_dtype, int causal, hipStream_t stream) {
+    if (out_dtype == 2)
+        return causal ? launch<fp8e4m3, float, 128, true>(a, stream) : launch<fp8e4m3, float, 128, false>(a, stream);
+    if (out_dtype == 1)
+        return causal ? launch<fp8e4m3, __bf16, 128, true>(a, stream) : launch<fp8e4m3, __bf16, 128, false>(a, stream);
+    return causal ? launch<fp8e4m3, _Float16, 128, true>(a, stream) : launch<fp8e4m3, _Float16, 128, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream) {

@@ -38,10 +38,14 @@ struct FwdArgs {
     size_t split_o;    // elements between the partial outputs of consecutive chunks
     size_t split_lse;  // elements between their partial lse
     DropArgs drop;
+    float oscale;      // 8-bit inputs only: factor applied to O (V's descale)
 };
 
 int fwd_block_rows();
 hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
+// 8-bit E4M3 q, k, v (d = 128, whole query blocks, no dropout); out_dtype:
+// 0 fp16, 1 bf16, 2 fp32
+hipError_t launch_fwd_fp8(const FwdArgs& a, int out_dtype, int causal, hipStream_t stream);
 
 // Split K/V: workspace bytes for nsplit chunks (fp32 partial O and lse), and
 // the merge of the partials into o (dtype, or fp32) and lse.

@@ -68,7 +68,7 @@ enum attn_status {
     ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = -6, /* backward workspace missing or too small */
     ATTN_ERR_LAUNCH = -7,    /* the HIP runtime rejected a kernel launch */
-    ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite */
+    ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite (or a bad descale factor) */
     ATTN_ERR_CAUSAL = -9,    /* causal is neither 0 nor 1 */
     ATTN_ERR_ALIAS = -10,    /* an output overlaps an input or another output */
     ATTN_ERR_SPLIT = -11,    /* nsplit outside 1 .. ATTN_MAX_SPLIT */
@@ -266,6 +266,35 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                      float dropout_p, uint64_t seed, uint32_t offset,
                      int dtype, int out_dtype, void* stream);
+
+/*
+ * attn_fwd_fp8 -- the forward with 8-bit inputs: q, k, v hold E4M3 codes
+ * (the OCP 8-bit floating-point format: sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinity, largest value 448; one byte per element,
+ * [B, H, N, d] as above), each tensor with one descale factor, so that code
+ * x stands for decode(x) * descale.  The low-precision forward is the one the
+ * pages name for FlashAttention-3 ("FlashAttention" explainer, "Common
+ * questions" and its references); they fix no details, so the operation is
+ * the exact attention of attn_fwd on those values, with scores
+ * scale * q_descale * k_descale * (Q K^T) and o scaled by v_descale.  The
+ * probabilities enter the P.V product rounded to nearest even E4M3 (each
+ * within 2^-4 of its value, or 2^-10 of a row's largest below E4M3's normal
+ * range); the row sums and lse use them in fp32.
+ *
+ *   q, k, v     : device pointers, E4M3 codes, [B, H, N, d], 16-byte aligned
+ *   o, lse      : outputs as for attn_fwd, o of `out_dtype`
+ *                 (ATTN_F16, ATTN_BF16 or ATTN_F32)
+ *   d           : 128
+ *   q_descale, k_descale, v_descale : finite and > 0
+ *   the rest    : as for attn_fwd
+ * Returns ATTN_OK or a negative attn_status (ATTN_ERR_HEAD_DIM for d != 128,
+ * ATTN_ERR_SCALE for a descale factor that is not finite and positive, or a
+ * score scale that overflows).
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 float q_descale, float k_descale, float v_descale, int causal,
+                 int out_dtype, void* stream);
 
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dropout",
                                     "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode",
-                                    "attn_fwd_dropout", "attn_fwd_split",
+                                    "attn_fwd_dropout", "attn_fwd_fp8", "attn_fwd_split",
                                     "attn_fwd_split_workspace_size", "attn_status_str"]
 
 
@@ -292,3 +292,31 @@ def test_fwd_decode_empty_is_noop():
     assert fwd_decode(Nq=0, ws=0, wsb=0) == OK
     assert fwd_decode(B=0) == OK
     assert fwd_decode(Nk=0, o=0) == E_NULL
+
+
+def fwd_fp8(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, H=3, N=100, d=128, scale=0.1,
+             qd=0.01, kd=0.02, vd=0.03, causal=1, out_dtype=1, stream=0)
+    a.update(kw)
+    return attn.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                             a["d"], a["scale"], a["qd"], a["kd"], a["vd"], a["causal"],
+                             a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), E_HD), (dict(d=96), E_HD), (dict(out_dtype=3), E_DT), (dict(out_dtype=-1), E_DT),
+    (dict(causal=2), E_CAUSAL), (dict(B=-1), E_SHAPE), (dict(N=-5), E_SHAPE),
+    (dict(scale=float("inf")), E_SCALE), (dict(scale=float("nan")), E_SCALE),
+    (dict(qd=0.0), E_SCALE), (dict(kd=-1.0), E_SCALE), (dict(vd=float("nan")), E_SCALE),
+    (dict(vd=0.0), E_SCALE), (dict(kd=float("inf")), E_SCALE),
+    (dict(scale=1e30, qd=1e30, kd=1e30), E_SCALE),
+    (dict(q=0), E_NULL), (dict(lse=0), E_NULL), (dict(o=P[3] + 8), E_ALIGN),
+    (dict(o=P[0]), E_ALIAS), (dict(lse=P[2] + 16), E_ALIAS), (dict(N=1 << 23), E_SHAPE),
+])
+def test_fwd_fp8_rejects(kw, code):
+    assert fwd_fp8(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=0, o=0)])
+def test_fwd_fp8_empty_is_noop(kw):
+    assert fwd_fp8(**kw) == OK
