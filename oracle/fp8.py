@@ -24,6 +24,7 @@ fix nothing about it.  The reading taken here:
 import numpy as np
 
 from . import fwd as _fwd
+from . import fwd_rect as _fwd_rect
 
 E4M3_MAX = 448.0
 
@@ -55,6 +56,15 @@ def fwd_fp8(q8, k8, v8, scale, descale, causal=False, rows=None, threads=None):
     return _fwd(q, k, v, scale, causal, rows=rows, threads=threads)
 
 
+def fwd_fp8_rect(q8, k8, v8, scale, descale, causal=False, rows=None, threads=None):
+    """:func:`oracle.fwd_rect` (Nq queries against Nk keys, causal query i
+    seeing keys 0 .. i + Nk - Nq) of the dequantised inputs."""
+    q = dequantize(q8, descale[0])
+    k = dequantize(k8, descale[1])
+    v = dequantize(v8, descale[2])
+    return _fwd_rect(q, k, v, scale, causal, rows=rows, threads=threads)
+
+
 def error_bound(q8, k8, v8, scale, descale, causal=False, rows=None, out_rel=0.0):
     """:func:`error_bound_values` of the dequantised inputs."""
     q = dequantize(q8, descale[0])
@@ -65,7 +75,8 @@ def error_bound(q8, k8, v8, scale, descale, causal=False, rows=None, out_rel=0.0
 
 def error_bound_values(q, k, v, scale, causal=False, rows=None, out_rel=0.0):
     """Element-wise bound on |O_fp8 - O| for the method read as above, for
-    fp64 inputs q, k, v [..., N, d] (the values the codes stand for).
+    fp64 inputs q [..., Nq, d] and k, v [..., Nk, d] (the values the codes
+    stand for; under the causal mask query i sees keys 0 .. i + Nk - Nq).
 
     With w_j the exact softmax weights of a row and v_j its visible V rows:
     rounding P_j to nearest in E4M3 changes it by at most 2^-4 P_j while P_j
@@ -80,11 +91,16 @@ def error_bound_values(q, k, v, scale, causal=False, rows=None, out_rel=0.0):
                   + 2^-10 sum_j w_j |v_jc| + out_rel |O_c| + 1e-6,
     the third term a generous allowance for fp32 accumulation over up to
     N keys and the fourth the rounding of the output (2^-8 for bf16, 0 for
-    fp32).  Returns the bound in the layout of :func:`fwd_fp8`'s o."""
+    fp32).  The same bound holds when the keys are processed in chunks whose
+    normalised partial outputs are merged with exact weights: each chunk's
+    error is bounded by its own terms, and the merge weights turn the chunk
+    weights back into w.  A row that sees no key has O = 0 and bound 1e-6.
+    Returns the bound in the layout of :func:`fwd_fp8`'s o."""
     q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
     lead, N, d = q.shape[:-2], q.shape[-2], q.shape[-1]
+    Nk = k.shape[-2]
     BH = int(np.prod(lead)) if lead else 1
-    q, k, v = q.reshape(BH, N, d), k.reshape(BH, N, d), v.reshape(BH, N, d)
+    q, k, v = q.reshape(BH, N, d), k.reshape(BH, Nk, d), v.reshape(BH, Nk, d)
     all_rows = rows is None
     if all_rows:
         rows = np.arange(BH * N, dtype=np.int64)
@@ -94,10 +110,15 @@ def error_bound_values(q, k, v, scale, causal=False, rows=None, out_rel=0.0):
         sel = np.nonzero(rows // N == bh)[0]
         i = rows[sel] % N
         s = float(scale) * (q[bh, i] @ k[bh].T)
-        vis = np.arange(N)[None, :] <= i[:, None] if causal else np.ones((i.size, N), bool)
+        if causal:
+            vis = np.arange(Nk)[None, :] <= i[:, None] + (Nk - N)
+        else:
+            vis = np.ones((i.size, Nk), bool)
         s = np.where(vis, s, -np.inf)
-        w = np.exp(s - s.max(axis=1, keepdims=True))
-        w /= w.sum(axis=1, keepdims=True)
+        top = s.max(axis=1, keepdims=True)
+        seen = np.isfinite(top)
+        w = np.where(seen, np.exp(s - np.where(seen, top, 0.0)), 0.0)
+        w /= np.where(seen, w.sum(axis=1, keepdims=True), 1.0)
         av = np.abs(v[bh])
         o = w @ v[bh]
         t1 = w @ av

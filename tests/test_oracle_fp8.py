@@ -140,3 +140,88 @@ def test_bound_catches_mistakes(mistake):
     assert np.all(np.abs(o_ok - o_ref) <= bound)
     o_bad = _emulate(q, k, v, scale, True, mistake=mistake)
     assert np.any(np.abs(o_bad - o_ref) > bound)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_rect_equals_materialised(causal):
+    w = WORKLOADS["long_context_fwd"]
+    xq, ds = make_fp8_inputs(w, seed=14, shape=(1, 2, 5, 128))
+    xk, dk = make_fp8_inputs(w, seed=15, shape=(1, 2, 90, 128))
+    desc = (ds[0], dk[1], dk[2])
+    scale = 1 / math.sqrt(128)
+    o, lse = ofp8.fwd_fp8_rect(xq["q"], xk["k"], xk["v"], scale, desc, causal)
+    q = ofp8.dequantize(xq["q"].numpy(), desc[0])
+    k = ofp8.dequantize(xk["k"].numpy(), desc[1])
+    v = ofp8.dequantize(xk["v"].numpy(), desc[2])
+    o2, lse2 = brute.fwd_rect(q, k, v, scale, causal)
+    assert np.abs(o - o2).max() <= 1e-12
+    assert np.abs(lse - lse2).max() <= 1e-12
+
+
+def _emulate_split(q, k, v, scale, causal, tiles_per_chunk, mistake=None):
+    """Nq queries against Nk keys in chunks of whole 64-key tiles: per chunk
+    and row the method as in _emulate (own reference, P rounded to E4M3,
+    normalised by the chunk's fp32 sum), then the exact logsumexp merge.
+    Rows that see no key get 0."""
+    BH, Nq, d = q.shape
+    Nk = k.shape[1]
+    o = np.zeros((BH, Nq, d))
+    for bh in range(BH):
+        s = scale * (q[bh] @ k[bh].T) * math.log2(math.e)
+        for i in range(Nq):
+            kend = min(Nk, i + 1 + Nk - Nq) if causal else Nk
+            parts = []
+            for c0 in range(0, max(kend, 0), 64 * tiles_per_chunk):
+                ref, l, acc = -np.inf, 0.0, np.zeros(d)
+                for j0 in range(c0, min(kend, c0 + 64 * tiles_per_chunk), 64):
+                    x = s[i, j0:min(kend, j0 + 64)]
+                    tmax = x.max()
+                    if tmax > ref + 8:
+                        alpha = 0.0 if ref == -np.inf else 2.0 ** (ref - (tmax - 4))
+                        acc *= alpha
+                        l *= alpha
+                        ref = tmax - 4
+                    p = np.exp2(x - ref)
+                    acc += _e4m3_round(p) @ v[bh, j0:j0 + x.size]
+                    l += p.sum()
+                parts.append((acc / l, (ref + math.log2(l)) * math.log(2)))
+            if not parts:
+                continue
+            lses = np.array([lc for _, lc in parts])
+            wts = np.exp(lses - lses.max())
+            if mistake == "equal_weights":
+                wts = np.ones_like(wts)
+            o[bh, i] = sum(wc * oc for wc, (oc, _) in zip(wts, parts)) / wts.sum()
+    return o
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk,tpc", [(1, 700, 2), (4, 300, 1), (16, 16, 1), (40, 20, 1), (130, 500, 3)])
+def test_bound_holds_for_chunked_rect(Nq, Nk, tpc, causal):
+    w = WORKLOADS["llama7b_layer_fwd"]
+    xq, ds = make_fp8_inputs(w, seed=16, shape=(1, 1, Nq, 128))
+    xk, dk = make_fp8_inputs(w, seed=17, shape=(1, 1, Nk, 128))
+    desc = (ds[0], dk[1], dk[2])
+    scale = 1 / math.sqrt(128)
+    q = ofp8.dequantize(xq["q"].numpy(), desc[0]).reshape(1, Nq, 128)
+    k = ofp8.dequantize(xk["k"].numpy(), desc[1]).reshape(1, Nk, 128)
+    v = ofp8.dequantize(xk["v"].numpy(), desc[2]).reshape(1, Nk, 128)
+    o_ref, _ = ofp8.fwd_fp8_rect(xq["q"], xk["k"], xk["v"], scale, desc, causal)
+    bound = ofp8.error_bound(xq["q"], xk["k"], xk["v"], scale, desc, causal).reshape(1, Nq, 128)
+    o_emu = _emulate_split(q, k, v, scale, causal, tpc)
+    assert np.all(np.abs(o_emu - o_ref.reshape(1, Nq, 128)) <= bound)
+
+
+def test_bound_catches_wrong_merge():
+    w = WORKLOADS["llama7b_layer_fwd"]
+    xq, ds = make_fp8_inputs(w, seed=18, shape=(1, 1, 2, 128))
+    xk, dk = make_fp8_inputs(w, seed=19, shape=(1, 1, 640, 128))
+    desc = (ds[0], dk[1], dk[2])
+    scale = 1 / math.sqrt(128)
+    q = ofp8.dequantize(xq["q"].numpy(), desc[0]).reshape(1, 2, 128)
+    k = ofp8.dequantize(xk["k"].numpy(), desc[1]).reshape(1, 640, 128)
+    v = ofp8.dequantize(xk["v"].numpy(), desc[2]).reshape(1, 640, 128)
+    o_ref, _ = ofp8.fwd_fp8_rect(xq["q"], xk["k"], xk["v"], scale, desc, False)
+    bound = ofp8.error_bound(xq["q"], xk["k"], xk["v"], scale, desc, False).reshape(1, 2, 128)
+    o_bad = _emulate_split(q, k, v, scale, False, 2, mistake="equal_weights")
+    assert np.any(np.abs(o_bad - o_ref.reshape(1, 2, 128)) > bound)
