@@ -96,7 +96,8 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=8, help="key chunks of the decode step")
     ap.add_argument("--fp8", action="store_true",
                     help="time the E4M3 forward (attn_fwd_fp8) on the workload quantised per "
-                         "tensor, against the dense fp8 matrix peak")
+                         "tensor, against the dense fp8 matrix peak; with --decode, the E4M3 "
+                         "decode step (attn_fwd_decode_fp8)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output dirs")
     return ap.parse_args()
@@ -218,16 +219,23 @@ DROP_STATE = (2024, 17)   # generator seed and offset of the dropout path
 def bench_decode(args):
     """One decode step per call: attn_fwd_decode (split kernel and merge).
     Algorithmic bytes: K and V read once, q read, o and lse written, and the
-    fp32 partials written and read back by the merge."""
+    fp32 partials written and read back by the merge.  With --fp8 the step
+    is attn_fwd_decode_fp8 on E4M3 q, k, v (inputs.make_decode_fp8_inputs),
+    one byte per element read, bf16 output."""
     dev = torch.device("cuda:0")
     B, H, Nk, d, Nq, ns = 16, 32, 16384, 128, int(args.decode), int(args.nsplit)
-    g = torch.Generator(device="cpu").manual_seed(11)
-    q = torch.randn((B, H, Nq, d), generator=g).to(torch.bfloat16)
-    k = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16)
-    v = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    f8 = bool(args.fp8)
+    if f8:
+        x, desc = inputs.make_decode_fp8_inputs(B, H, Nq, Nk, d, seed=12)
+        qd, kd, vd = (x[n].to(dev) for n in "qkv")
+    else:
+        g = torch.Generator(device="cpu").manual_seed(11)
+        q = torch.randn((B, H, Nq, d), generator=g).to(torch.bfloat16)
+        k = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16)
+        v = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(qd)
+    o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     need = attn.attn_fwd_split_workspace_size(B, H, Nq, d, ns)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -235,11 +243,16 @@ def bench_decode(args):
     sp = stream.cuda_stream
 
     def call():
-        st = attn.attn_fwd_decode(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
-                                  lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, Nq, Nk, d, scale,
-                                  1, attn.ATTN_BF16, attn.ATTN_BF16, ns, sp)
+        if f8:
+            st = attn.attn_fwd_decode_fp8(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                          lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, Nq, Nk, d,
+                                          scale, desc[0], desc[1], desc[2], 1, attn.ATTN_BF16, ns, sp)
+        else:
+            st = attn.attn_fwd_decode(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, Nq, Nk, d, scale,
+                                      1, attn.ATTN_BF16, attn.ATTN_BF16, ns, sp)
         if st:
-            raise attn.AttnError(st, "attn_fwd_decode")
+            raise attn.AttnError(st, "attn_fwd_decode_fp8" if f8 else "attn_fwd_decode")
 
     for _ in range(args.warmup):
         call()
@@ -254,18 +267,20 @@ def bench_decode(args):
     wall = time.perf_counter() - wall0
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
     BH = B * H
-    kv = 2 * BH * Nk * d * 2
+    esz = 1 if f8 else 2                      # bytes per input element
+    kv = 2 * BH * Nk * d * esz
     partial = ns * BH * Nq * (d + 1) * 4 * 2
-    byts = kv + BH * Nq * d * 2 * 2 + BH * Nq * 4 + partial
+    byts = kv + BH * Nq * d * (esz + 2) + BH * Nq * 4 + partial
     ms = float(per.mean())
     gbs = byts / (ms * 1e-3) / 1e9
     out = {
         "metric": "decode step: K/V cache read GB/s at 1 GPU + % of HBM peak",
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"decode: B={B} H={H} Nq={Nq} Nk={Nk} d={d} bf16 causal, "
-                               f"nsplit={ns}; step = attn_fwd_decode (split kernel + merge)"},
+        "vs_baseline": None, "dtype": "fp8_e4m3" if f8 else "bf16", "data": "synthetic",
+        "config": {"workload": f"decode: B={B} H={H} Nq={Nq} Nk={Nk} d={d} "
+                               f"{'E4M3 q, k, v' if f8 else 'bf16'} causal, nsplit={ns}; step = "
+                               f"{'attn_fwd_decode_fp8' if f8 else 'attn_fwd_decode'} (split kernel + merge)"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_call": byts,
                      "call_ms": ms},
@@ -344,7 +359,7 @@ def main():
         if not torch.cuda.is_available():
             print("no GPU visible", file=sys.stderr)
             sys.exit(1)
-        if args.fp8:
+        if args.decode is None:
             bench_fp8(args)
         else:
             bench_decode(args)

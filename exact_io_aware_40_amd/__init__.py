@@ -9,10 +9,10 @@ Low level (same names and argument order as the C ABI, raw integers and
 device pointers):  :func:`attn_fwd`, :func:`attn_fwd_split`,
 :func:`attn_fwd_split_workspace_size`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
 :func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`, :func:`attn_fwd_fp8`,
-:func:`attn_status_str`.
+:func:`attn_fwd_decode_fp8`, :func:`attn_status_str`.
 
 Tensor level:  :func:`forward`, :func:`forward_split`, :func:`forward_decode`,
-:func:`forward_fp8` and :func:`backward`.
+:func:`forward_fp8`, :func:`forward_decode_fp8` and :func:`backward`.
 """
 from __future__ import annotations
 
@@ -26,8 +26,8 @@ import torch
 __all__ = [
     "attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_size",
     "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
-    "attn_fwd_fp8", "attn_status_str",
-    "forward", "forward_split", "forward_decode", "forward_fp8", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
+    "attn_fwd_fp8", "attn_fwd_decode_fp8", "attn_status_str",
+    "forward", "forward_split", "forward_decode", "forward_fp8", "forward_decode_fp8", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
 ]
 
 ATTN_F16 = 0
@@ -88,6 +88,9 @@ def _load():
                                                  i32, vp]
     lib.attn_fwd_fp8.restype = i32
     lib.attn_fwd_fp8.argtypes = [vp] * 5 + [i64, i64, i64, i64, f32, f32, f32, f32, i32, i32, vp]
+    lib.attn_fwd_decode_fp8.restype = i32
+    lib.attn_fwd_decode_fp8.argtypes = [vp] * 6 + [sz, i64, i64, i64, i64, i64, f32, f32, f32, f32,
+                                                   i32, i32, i32, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -167,6 +170,15 @@ def attn_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: in
                  out_dtype: int, stream: int) -> int:
     return _load().attn_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale,
                                 causal, out_dtype, stream)
+
+
+def attn_fwd_decode_fp8(q: int, k: int, v: int, o: int, lse: int, workspace: int,
+                        workspace_bytes: int, B: int, H: int, Nq: int, Nk: int, d: int, scale: float,
+                        q_descale: float, k_descale: float, v_descale: float, causal: int,
+                        out_dtype: int, nsplit: int, stream: int) -> int:
+    return _load().attn_fwd_decode_fp8(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                                       scale, q_descale, k_descale, v_descale, causal, out_dtype,
+                                       nsplit, stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -286,6 +298,47 @@ def forward_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       B, H, N, d, float(scale), qd, kd, vd, int(bool(causal)), _OUT_CODE[od], _stream(q))
     if st != 0:
         raise AttnError(st, "attn_fwd_fp8")
+    return o, lse
+
+
+def forward_decode_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       descale: Tuple[float, float, float] = (1.0, 1.0, 1.0), causal: bool = False,
+                       scale: Optional[float] = None, nsplit: int = 8,
+                       out_dtype: torch.dtype = torch.bfloat16,
+                       workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_fwd_decode_fp8: E4M3 q [B, H, Nq, 128] against E4M3 k, v
+    [B, H, Nk, 128] (codes as float8_e4m3fn or uint8), keys split in nsplit
+    chunks and merged.  Returns (o [B, H, Nq, 128] of out_dtype, lse
+    [B, H, Nq] float32).  A workspace (uint8, at least
+    attn_fwd_split_workspace_size(B, H, Nq, 128, nsplit) bytes) is allocated
+    when none is given."""
+    _check(q, "q")
+    _check(k, "k")
+    _check(v, "v", k)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dtype not in _FP8_TYPES or k.dtype not in _FP8_TYPES:
+        raise ValueError("q, k, v must hold E4M3 codes (float8_e4m3fn or uint8)")
+    if out_dtype not in _OUT_CODE:
+        raise ValueError(f"out_dtype must be float16, bfloat16 or float32, got {out_dtype}")
+    B, H, Nq, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or k.device != q.device:
+        raise ValueError("k, v must be [B, H, Nk, d] on q's device")
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = attn_fwd_split_workspace_size(B, H, Nq, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    qd, kd, vd = (float(x) for x in descale)
+    st = attn_fwd_decode_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             B, H, Nq, Nk, d, float(scale), qd, kd, vd, int(bool(causal)),
+                             _OUT_CODE[out_dtype], int(nsplit), _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_decode_fp8")
     return o, lse
 
 

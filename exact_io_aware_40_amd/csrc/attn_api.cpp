@@ -237,11 +237,29 @@ namespace {
 
 // Split K/V forward of Nq query rows against Nk keys per head (Nq = Nk for
 // attn_fwd_split): partials into the workspace, then the merge.
+// Descale factors of 8-bit inputs (q, k, v); `on` false for 16-bit inputs.
+struct Fp8Args {
+    bool on;
+    float qd, kd, vd;
+};
+
 int fwd_split_common(const void* q, const void* k, const void* v, void* o, float* lse,
                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
                      int64_t Nk, int64_t d, float scale, int causal, int dtype, int out_dtype,
-                     int nsplit, void* stream) {
+                     int nsplit, void* stream, Fp8Args f8 = Fp8Args{false, 1.f, 1.f, 1.f}) {
     if (Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+    if (f8.on) {
+        // 8-bit inputs: d = 128; the output type alone selects the merge's output
+        if (B < 0 || H < 0) return ATTN_ERR_SHAPE;
+        if (d != 128) return ATTN_ERR_HEAD_DIM;
+        if (out_dtype != ATTN_F16 && out_dtype != ATTN_BF16 && out_dtype != ATTN_F32)
+            return ATTN_ERR_DTYPE;
+        if (!isfinite(scale) || !isfinite(f8.qd) || !isfinite(f8.kd) || !isfinite(f8.vd) ||
+            !(f8.qd > 0.f) || !(f8.kd > 0.f) || !(f8.vd > 0.f) || !isfinite(scale * f8.qd * f8.kd))
+            return ATTN_ERR_SCALE;
+        scale = scale * f8.qd * f8.kd;
+        dtype = out_dtype == ATTN_F32 ? ATTN_BF16 : out_dtype;
+    }
     bool empty = false;
     int st = check_common(B, H, Nq > Nk ? Nq : Nk, d, scale, causal, dtype, out_dtype, &empty);
     if (st != ATTN_OK) return st;
@@ -254,7 +272,8 @@ int fwd_split_common(const void* q, const void* k, const void* v, void* o, float
     const size_t need = attn::fwd_split_workspace_bytes(BH, Nq, d, nsplit);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-    const size_t qbytes = size_t(BH * Nq * d) * 2, kbytes = size_t(BH * Nk * d) * 2;
+    const size_t esz = f8.on ? 1 : 2;   // bytes per input element
+    const size_t qbytes = size_t(BH * Nq * d) * esz, kbytes = size_t(BH * Nk * d) * esz;
     const size_t obytes = size_t(BH * Nq * d) * (out_dtype == ATTN_F32 ? 4 : 2);
     const Range ro = range(o, obytes), rl = range(lse, size_t(BH * Nq) * 4), rw = range(workspace, need);
     const Range in[3] = {range(q, qbytes), range(k, kbytes), range(v, kbytes)};
@@ -285,9 +304,10 @@ int fwd_split_common(const void* q, const void* k, const void* v, void* o, float
     a.split_o = split_o;
     a.split_lse = split_lse;
     a.drop = no_drop();
-    a.oscale = 1.f;
+    a.oscale = f8.on ? f8.vd : 1.f;
     // the partials are fp32 whatever the output type; the merge rounds once
-    hipError_t e = attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
+    hipError_t e = f8.on ? attn::launch_fwd_fp8(a, ATTN_F32, causal, (hipStream_t)stream)
+                         : attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
     e = attn::launch_fwd_merge(ws_o, ws_lse, o, lse, BH * Nq, nsplit, split_o, split_lse, int(d), dtype,
                                out_dtype == ATTN_F32, (hipStream_t)stream);
@@ -310,6 +330,15 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, int dtype, int out_dtype, int nsplit, void* stream) {
     return fwd_split_common(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale,
                             causal, dtype, out_dtype, nsplit, stream);
+}
+
+int attn_fwd_decode_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nk, int64_t d, float scale, float q_descale, float k_descale,
+                        float v_descale, int causal, int out_dtype, int nsplit, void* stream) {
+    return fwd_split_common(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+                            ATTN_BF16, out_dtype, nsplit, stream,
+                            Fp8Args{true, q_descale, k_descale, v_descale});
 }
 
 size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {

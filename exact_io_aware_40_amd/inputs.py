@@ -129,6 +129,19 @@ def make_fp8_inputs(w: Workload, seed: Optional[int] = None, shape=None):
     return out, tuple(desc)
 
 
+def make_decode_fp8_inputs(B: int, H: int, Nq: int, Nk: int, d: int, seed: int):
+    """A decode step's E4M3 inputs: q [B, H, Nq, d] and a key/value cache k, v
+    [B, H, Nk, d], each drawn as normal() with its tensor id (bf16) and
+    quantised per tensor by quantize_e4m3.  Returns ({"q", "k", "v"}: uint8
+    code tensors, (q, k, v) descales)."""
+    shapes = {"q": (B, H, Nq, d), "k": (B, H, Nk, d), "v": (B, H, Nk, d)}
+    out, desc = {}, []
+    for name in ("q", "k", "v"):
+        out[name], ds = quantize_e4m3(normal(shapes[name], seed, TENSOR_IDS[name], torch.bfloat16))
+        desc.append(ds)
+    return out, tuple(desc)
+
+
 def checksum(t: torch.Tensor) -> str:
     """sha256 of the tensor's raw bytes (first 16 hex digits)."""
     raw = t.contiguous().view(torch.uint8).numpy().tobytes()

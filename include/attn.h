@@ -296,6 +296,27 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  float q_descale, float k_descale, float v_descale, int causal,
                  int out_dtype, void* stream);
 
+/*
+ * attn_fwd_decode_fp8 -- attn_fwd_decode with 8-bit inputs: Nq queries
+ * against Nk keys per (batch, head) (causal query i sees keys 0 ..
+ * i + Nk - Nq), each query block's keys split in nsplit chunks and merged,
+ * with q, k, v as E4M3 codes and their descale factors as for attn_fwd_fp8
+ * (a key/value cache held in 8 bits; q quantised by the caller).  The
+ * chunks' partial outputs obey the same element-wise error statement as
+ * attn_fwd_fp8, and the merge's exact weights keep it for the result.
+ *
+ *   q, o       : [B, H, Nq, d]; k, v : [B, H, Nk, d]; lse : [B, H, Nq]
+ *   workspace  : attn_fwd_split_workspace_size(B, H, Nq, d, nsplit) bytes
+ *   d          : 128; out_dtype : ATTN_F16, ATTN_BF16 or ATTN_F32
+ *   the rest   : as for attn_fwd_decode and attn_fwd_fp8
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_fwd_decode_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                        int64_t Nq, int64_t Nk, int64_t d, float scale, float q_descale,
+                        float k_descale, float v_descale, int causal, int out_dtype, int nsplit,
+                        void* stream);
+
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);
 

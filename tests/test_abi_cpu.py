@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dropout",
-                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode",
+                                    "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode", "attn_fwd_decode_fp8",
                                     "attn_fwd_dropout", "attn_fwd_fp8", "attn_fwd_split",
                                     "attn_fwd_split_workspace_size", "attn_status_str"]
 
@@ -320,3 +320,33 @@ def test_fwd_fp8_rejects(kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=0, o=0)])
 def test_fwd_fp8_empty_is_noop(kw):
     assert fwd_fp8(**kw) == OK
+
+
+def fwd_decode_fp8(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], wsb=None, B=2, H=3, Nq=4, Nk=300,
+             d=128, scale=0.1, qd=0.01, kd=0.02, vd=0.03, causal=1, out_dtype=1, nsplit=4, stream=0)
+    a.update(kw)
+    wsb = a["wsb"]
+    if wsb is None:
+        wsb = attn.attn_fwd_split_workspace_size(max(a["B"], 0), max(a["H"], 0), max(a["Nq"], 0), 128,
+                                                 min(max(a["nsplit"], 1), 64))
+    return attn.attn_fwd_decode_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], wsb, a["B"],
+                                    a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"], a["kd"],
+                                    a["vd"], a["causal"], a["out_dtype"], a["nsplit"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), E_HD), (dict(out_dtype=3), E_DT), (dict(causal=2), E_CAUSAL),
+    (dict(Nq=-1), E_SHAPE), (dict(Nk=-1), E_SHAPE), (dict(B=-1), E_SHAPE),
+    (dict(qd=0.0), E_SCALE), (dict(vd=float("inf")), E_SCALE), (dict(scale=float("nan")), E_SCALE),
+    (dict(nsplit=0), E_SPLIT), (dict(nsplit=65), E_SPLIT),
+    (dict(q=0), E_NULL), (dict(ws=0), E_WS), (dict(wsb=16), E_WS), (dict(ws=P[5] + 8), E_ALIGN),
+    (dict(o=P[1]), E_ALIAS), (dict(ws=P[0]), E_ALIAS),
+])
+def test_fwd_decode_fp8_rejects(kw, code):
+    assert fwd_decode_fp8(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(Nq=0, q=0, ws=0)])
+def test_fwd_decode_fp8_empty_is_noop(kw):
+    assert fwd_decode_fp8(**kw) == OK

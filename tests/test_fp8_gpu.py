@@ -1,4 +1,5 @@
-"""FP8 (E4M3) forward on the GPU (attn_fwd_fp8) against the CPU oracle.
+"""FP8 (E4M3) forward and decode step on the GPU (attn_fwd_fp8,
+attn_fwd_decode_fp8) against the CPU oracle.
 
 The oracle is exact attention on the decoded, descaled inputs; the kernel
 rounds P to E4M3 for the P.V product, so each fp32 output element must lie
@@ -7,7 +8,10 @@ within LSE_TOL, and a 16-bit output must be exactly the fp32 output rounded
 to nearest even.  Cases: ragged tails and a single row, both masks, inputs
 with outlier keys, every output type, both tensor types that carry the
 codes, a negative scale, and sampled rows of the seven-billion-parameter
-layer's full shape in the launch the benchmark times.
+layer's full shape in the launch the benchmark times.  The decode step
+(Nq queries against an Nk-key cache, keys split in chunks and merged) is
+held to the same bound, including rows that see no key (O = 0, lse = -inf),
+and at the benchmark's 16 x 32 x 16384-key cache.
 """
 import math
 
@@ -140,3 +144,78 @@ def test_fp8_llama7b_layer_sampled():
         rr |= set(rng.choice(N, size=24, replace=False).tolist())
         rows += [hd * N + r for r in sorted(rr)]
     run_fp8(x, ds, True, 1 / math.sqrt(w.d), "llama7b layer", rows=np.array(rows), heads=heads)
+
+
+def run_decode_fp8(x, ds, causal, nsplit, tag, out_dtype=torch.bfloat16, heads=None):
+    """x: uint8 codes q [B, H, Nq, d], k, v [B, H, Nk, d] on the CPU.  heads:
+    the (b H + h) ids whose rows are checked (all when None)."""
+    B, H, Nq, d = x["q"].shape
+    Nk = x["k"].shape[2]
+    announce(f"fp8 decode {tag} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} nsplit={nsplit} out={out_dtype}")
+    q, k, v = (x[n].to(DEV) for n in "qkv")
+    o32, lse32 = attn.forward_decode_fp8(q, k, v, descale=ds, causal=causal, nsplit=nsplit,
+                                         out_dtype=torch.float32)
+    if out_dtype != torch.float32:
+        o, lse = attn.forward_decode_fp8(q, k, v, descale=ds, causal=causal, nsplit=nsplit,
+                                         out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    if out_dtype != torch.float32:
+        assert torch.equal(o, o32.to(out_dtype)), f"{tag}: 16-bit O is not RNE(fp32 O)"
+        assert torch.equal(lse, lse32)
+    hs = np.arange(B * H) if heads is None else np.asarray(heads)
+    cq = x["q"].numpy().reshape(B * H, Nq, d)[hs]
+    ck = x["k"].numpy().reshape(B * H, Nk, d)[hs]
+    cv = x["v"].numpy().reshape(B * H, Nk, d)[hs]
+    idx = torch.from_numpy(hs.astype(np.int64)).to(DEV)
+    got_o = f64(o32.view(B * H, Nq, d)[idx])
+    got_l = f64(lse32.view(B * H, Nq)[idx])
+    sc = s32(1 / math.sqrt(d))
+    o_ref, lse_ref = ofp8.fwd_fp8_rect(cq, ck, cv, sc, ds, causal)
+    bound = ofp8.error_bound(cq, ck, cv, sc, ds, causal)
+    check_bound(f"{tag} O(fp32 out)", got_o.reshape(-1, d), o_ref.reshape(-1, d), bound.reshape(-1, d))
+    lr, lg = lse_ref.reshape(-1), got_l.reshape(-1)
+    assert np.array_equal(np.isfinite(lr), np.isfinite(lg)), f"{tag}: rows without keys differ"
+    fin = np.isfinite(lr)
+    assert np.all(lg[~fin] == -np.inf) and np.all(got_o.reshape(-1, d)[~fin] == 0)
+    err_l = float(np.abs(lg[fin] - lr[fin]).max()) if fin.any() else 0.0
+    _emit(f"[err] {tag} lse: max|gpu-oracle| = {err_l:.3e} (tol {LSE_TOL:.1e})")
+    assert err_l <= LSE_TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk,nsplit", [(1, 1, 1), (1, 700, 8), (4, 300, 3), (16, 2000, 16),
+                                          (130, 500, 2), (40, 20, 2), (3, 64, 64)])
+def test_fp8_decode_small(Nq, Nk, nsplit, causal):
+    from exact_io_aware_40_amd.inputs import make_decode_fp8_inputs
+    x, ds = make_decode_fp8_inputs(2, 2, Nq, Nk, 128, seed=400 + Nq + Nk)
+    run_decode_fp8(x, ds, causal, nsplit, f"Nq={Nq} Nk={Nk}")
+
+
+def test_fp8_decode_output_types():
+    from exact_io_aware_40_amd.inputs import make_decode_fp8_inputs
+    x, ds = make_decode_fp8_inputs(1, 3, 5, 900, 128, seed=420)
+    for od in (torch.float16, torch.float32):
+        run_decode_fp8(x, ds, True, 4, f"out={od}", out_dtype=od)
+
+
+def test_fp8_decode_equals_square_when_nq_is_nk():
+    """Nq = Nk with one chunk: the split kernel's partial is the whole
+    softmax, so the merged result equals attn_fwd_fp8's within the merge's
+    fp32 rounding."""
+    x, ds = make_fp8_inputs(WORKLOADS["long_context_fwd"], seed=430, shape=(1, 2, 300, 128))
+    q, k, v = (x[n].to(DEV) for n in "qkv")
+    o1, l1 = attn.forward_fp8(q, k, v, descale=ds, causal=True, out_dtype=torch.float32)
+    o2, l2 = attn.forward_decode_fp8(q, k, v, descale=ds, causal=True, nsplit=1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (o1 - o2).abs().max().item() <= 1e-5
+    assert (l1 - l2).abs().max().item() <= 1e-5
+
+
+def test_fp8_decode_cache_16k_sampled():
+    """The decode step the benchmark times (B=16 H=32, one query against a
+    16384-key cache, 8 chunks), with six heads checked against the oracle."""
+    from exact_io_aware_40_amd.inputs import make_decode_fp8_inputs
+    B, H, Nq, Nk = 16, 32, 1, 16384
+    x, ds = make_decode_fp8_inputs(B, H, Nq, Nk, 128, seed=12)
+    heads = np.sort(np.random.default_rng(3).choice(B * H, size=6, replace=False))
+    run_decode_fp8(x, ds, True, 8, "16k cache", heads=heads)
