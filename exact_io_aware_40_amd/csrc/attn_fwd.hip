@@ -13,12 +13,17 @@
 // too"; explainer Step 4):
 //   S^T = K Q^T         on the matrix cores (keys x queries, fp32)
 //   mask                causal, ragged-tail and out-of-range tiles only
-//   m_t = rowmax S               lanes own query rows; one cross-lane step
-//   reference mc: the scaled running maximum, moved to m_t c only when
+//   P = 2^(S c - mc),  c = |scale| log2(e), with the reference mc as it
+//                 stands; l = alpha l + rowsum P
+//   reference mc: the scaled running maximum, moved to m_t c, m_t = rowmax S
+//                 (lanes own query rows; one cross-lane step), only when
 //                 that exceeds it by more than kTau binades (32 for bf16
 //                 operands, 15 for fp16; the first tile always moves it);
-//                 alpha = 2^(mc_old - mc_new)
-//   P = 2^(S c - mc),  c = |scale| log2(e);  l = alpha l + rowsum P
+//                 alpha = 2^(mc_old - mc_new).  With 16-bit operands the
+//                 row maximum is taken only for a tile in which some lane's
+//                 sum of P exceeds 2^kTau (then P is formed again); every
+//                 other tile leaves the reference where it is, since all
+//                 its P are within 2^kTau.  8-bit: m_t first, then P.
 //   O^T = alpha O^T + V^T P^T    V^T read from the row-major tile with
 //                                transposing LDS reads
 // and after the last tile O = O^T / l (rounded once), lse = (mc + log2 l) ln 2.
@@ -89,6 +94,10 @@ template <> constexpr float kTau<_Float16> = 15.f;
 template <> constexpr float kTau<fp8e4m3> = 8.f;
 template <typename T> constexpr float kShift = 0.f;
 template <> constexpr float kShift<fp8e4m3> = 4.f;
+// 2^kTau
+template <typename T> constexpr float kBound = 4294967296.f;
+template <> constexpr float kBound<_Float16> = 32768.f;
+template <> constexpr float kBound<fp8e4m3> = 256.f;
 
 template <int V> using IC = std::integral_constant<int, V>;
 
@@ -140,6 +149,14 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     typedef typename Elem<T>::v8 v8;
     typedef typename Elem<T>::raw raw;
     constexpr bool F8 = sizeof(T) == 1;   // E4M3 operands (d = 128, no dropout)
+    // 16-bit operands: whether the reference must move is read off each lane's
+    // fp32 sum of the tile's P, formed with the current reference (see the
+    // softmax pieces); 8-bit: from the tile's row maximum, computed first.
+    constexpr bool LAZY = !F8;
+    // fp16: O is normalised by the sum of P as rounded for the P.V product
+    // (its rounding, 2^-11 relative, would otherwise reach the fp16 output
+    // bound on rows dominated by one key); bf16 and 8-bit: by the fp32 sum
+    constexpr bool RSUM = std::is_same_v<T, _Float16>;
     static_assert(!F8 || (D == 128 && !DROP), "the 8-bit forward is instantiated for d = 128 only");
     constexpr int BC = bc<T, D>();
     static_assert(RING >= 4, "the pipeline needs four buffers per tensor");
@@ -308,9 +325,10 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[r][cb][e] = 0.f;
         // per row: exponent reference (scaled units), and this lane's share of
-        // the row's normaliser twice: the sum of P as rounded for the P.V product
-        // (it normalises O, so O's weights sum to one exactly as used) and the
-        // fp32 sum of P (it gives lse)
+        // the row's normaliser: the fp32 sum of P (it gives lse, and normalises
+        // O except under fp16) and, under fp16, the sum of P as rounded for the
+        // P.V product (it normalises O, so O's weights sum to one exactly as
+        // used)
         float mc_run[QB], l_run[QB], lf_run[QB];
         // (the reference starts at the lowest finite value: the first tile, whose
         // key 0 every row sees, always moves it, with alpha = 0)
@@ -433,25 +451,86 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             }
         };
 
-        // Softmax of one tile, as pieces p = 0 .. NP-1 (row block p % QB):
-        // row maximum over 8 scores (2 KB pieces); the reference and the wave's
-        // rescale flags (1); two probabilities, their fp32 sum, their packed
-        // pair and its sum as rounded (8 KB pieces).  The reference moves when
-        // the row maximum rose by more than kTau binades; the factor for the
-        // older accumulation, 2^(old - new), is formed only in the rare branch
-        // that rescales O and the sums (also after the first tile, whose move
-        // from the lowest finite value gives the factor 0 for an O and sums
-        // that are still zero).
+        // Softmax of one tile, as pieces p = 0 .. NP-1 (row block p % QB).
+        // 8-bit operands: row maximum over 8 scores (2 KB pieces); the
+        // reference and the wave's rescale flags (1); then the probabilities.
+        // 16-bit operands: the probabilities only, formed with the reference
+        // as it stands; the check after the tile's products finds the lanes
+        // whose fp32 sum of P exceeds 2^kTau (which holds for every lane whose
+        // P all stay within the bound, and fails for a P that is infinite or
+        // above it), and only then does the wave take the row maximum and
+        // redo the tile (slow_tile).  A probability piece forms two
+        // probabilities, their fp32 sum, their packed pair and (fp16) its sum
+        // as rounded (8 KB pieces).  The reference moves when the row maximum
+        // rose by more than kTau binades; the factor for the older
+        // accumulation, 2^(old - new), is formed only in the rare branch that
+        // rescales O and the sums (also after the first tile, whose move from
+        // the lowest finite value gives the factor 0 for an O and sums that
+        // are still zero).
         // Under dropout, the first 10 KB pieces of a row are the rounds of its
         // generator calls, one per 32-key block (tile j0 / 32 + b).
         constexpr int NPD = DROP ? 10 * KB : 0;
-        constexpr int NP_ROW = NPD + 10 * KB + 1;
+        constexpr int NP_ROW = NPD + (LAZY ? 8 * KB : 10 * KB + 1);
         constexpr int NP = QB * NP_ROW;
         float st_mt[QB], st_mold[QB], st_ls[QB], st_lfs[QB];
         constexpr int PWD = (int)sizeof(raw) / 4;   // words of one P operand
         unsigned pw[QB][VK][PWD];
         unsigned ph[QB][KB][4];   // generator state, then the call's four words
         int tile_j0 = 0;          // first key of the tile being normalised
+        // probabilities q = 0 .. 8 KB - 1 of row block r: elements 2 (q % 8),
+        // +1 of 32-key block q / 8, with the reference mc_run[r]
+        auto probs = [&](int r, int q, const Scores& sc) __attribute__((always_inline)) {
+            const int b = q / 8, e = 2 * (q % 8);
+            const float x0 = fast_exp2(fmaf(sc[r][b][e], c, -mc_run[r]));
+            const float x1 = fast_exp2(fmaf(sc[r][b][e + 1], c, -mc_run[r]));
+            if constexpr (F8) {
+                // bytes (16 (b % 2) + e) % 4, +1 of word 4 (b % 2) + e / 4 of P operand
+                // b / 2; the row sum is that of the fp32 probabilities
+                const int jj = b >> 1, wd = 4 * (b & 1) + (e >> 2);
+                const bool hi = (e >> 1) & 1;
+                pw[r][jj][wd] = Elem<T>::cvt2_into(x0, x1, hi ? pw[r][jj][wd] : 0u, hi);
+                if (q == 0) {
+                    st_lfs[r] = x0 + x1;
+                } else {
+                    st_lfs[r] += x0;
+                    st_lfs[r] += x1;
+                }
+            } else {
+                const unsigned pr = Elem<T>::cvt2(x0, x1);
+                if (q == 0) {
+                    st_lfs[r] = x0 + x1;
+                    if constexpr (RSUM) st_ls[r] = Elem<T>::sum2(pr, 0.f);
+                } else {
+                    st_lfs[r] += x0;
+                    st_lfs[r] += x1;
+                    if constexpr (RSUM) st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
+                }
+                if (DROP) {
+                    // elements e, e + 1: bytes e % 4 and e % 4 + 1 of word e / 4
+                    const unsigned wd = ph[r][b][e >> 2];
+                    const bool k0 = drop_keep(wd, e & 3, a.drop.t), k1 = drop_keep(wd, (e & 3) + 1, a.drop.t);
+                    pw[r][2 * b + e / 8][(e % 8) / 2] = Elem<T>::cvt2(k0 ? x0 : 0.f, k1 ? x1 : 0.f);
+                } else {
+                    pw[r][2 * b + e / 8][(e % 8) / 2] = pr;
+                }
+            }
+        };
+        // the tile's row maximum (over both lanes of the row), moved reference
+        // and rescale flag of row block r
+        auto move_ref = [&](int r, const Scores& sc) __attribute__((always_inline)) {
+            float m = -INFINITY;
+    #pragma unroll
+            for (int b = 0; b < KB; ++b)
+    #pragma unroll
+                for (int e = 0; e < 16; e += 2) m = fmaxf(fmaxf(m, sc[r][b][e]), sc[r][b][e + 1]);
+            const float tc = max32(m) * c;
+            const bool upd = tc > mc_run[r] + kTau<T>;
+            st_mold[r] = mc_run[r];
+            float tnew = tc;
+            if constexpr (kShift<T> != 0.f) tnew = tc - kShift<T>;
+            mc_run[r] = upd ? tnew : mc_run[r];
+            return upd;
+        };
         auto piece = [&](int p, Scores& sc, uint64_t& upd_mask) __attribute__((always_inline)) {
             const int r = p % QB;
             if (DROP && p / QB < NPD) {
@@ -466,7 +545,9 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 return;
             }
             const int sx = p / QB - NPD;
-            if (sx < 2 * KB) {
+            if constexpr (LAZY) {
+                probs(r, sx, sc);
+            } else if (sx < 2 * KB) {
                 // a chain of three-way maxima: 8 instructions per 16 scores
                 const int b = sx >> 1, e0 = 8 * (sx & 1);
                 const f32x16& x = sc[r][b];
@@ -491,40 +572,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 mc_run[r] = upd ? tnew : mc_run[r];
                 upd_mask |= __builtin_amdgcn_ballot_w64(upd);
             } else {
-                const int q = sx - 2 * KB - 1, b = q / 8, e = 2 * (q % 8);
-                const float x0 = fast_exp2(fmaf(sc[r][b][e], c, -mc_run[r]));
-                const float x1 = fast_exp2(fmaf(sc[r][b][e + 1], c, -mc_run[r]));
-                if constexpr (F8) {
-                    // bytes (16 (b % 2) + e) % 4, +1 of word 4 (b % 2) + e / 4 of P operand
-                    // b / 2; the row sum is that of the fp32 probabilities
-                    const int jj = b >> 1, wd = 4 * (b & 1) + (e >> 2);
-                    const bool hi = (e >> 1) & 1;
-                    pw[r][jj][wd] = Elem<T>::cvt2_into(x0, x1, hi ? pw[r][jj][wd] : 0u, hi);
-                    if (q == 0) {
-                        st_lfs[r] = x0 + x1;
-                    } else {
-                        st_lfs[r] += x0;
-                        st_lfs[r] += x1;
-                    }
-                } else {
-                    const unsigned pr = Elem<T>::cvt2(x0, x1);
-                    if (q == 0) {
-                        st_lfs[r] = x0 + x1;
-                        st_ls[r] = Elem<T>::sum2(pr, 0.f);
-                    } else {
-                        st_lfs[r] += x0;
-                        st_lfs[r] += x1;
-                        st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
-                    }
-                    if (DROP) {
-                        // elements e, e + 1: bytes e % 4 and e % 4 + 1 of word e / 4
-                        const unsigned wd = ph[r][b][e >> 2];
-                        const bool k0 = drop_keep(wd, e & 3, a.drop.t), k1 = drop_keep(wd, (e & 3) + 1, a.drop.t);
-                        pw[r][2 * b + e / 8][(e % 8) / 2] = Elem<T>::cvt2(k0 ? x0 : 0.f, k1 ? x1 : 0.f);
-                    } else {
-                        pw[r][2 * b + e / 8][(e % 8) / 2] = pr;
-                    }
-                }
+                probs(r, sx - 2 * KB - 1, sc);
             }
         };
 
@@ -574,6 +622,33 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                     }
                 }
             }
+            if constexpr (LAZY) {
+                // a lane whose sum of P is at most 2^kTau has every P within the
+                // bound; otherwise (a P above it or infinite, as on the first
+                // tile) the wave moves the reference where the row maximum asks
+                // for it and forms the tile's probabilities again
+                bool over = false;
+    #pragma unroll
+                for (int r = 0; r < QB; ++r) over |= st_lfs[r] > kBound<T>;
+                upd_mask = __builtin_amdgcn_ballot_w64(over);
+            }
+            if (upd_mask != 0) [[unlikely]] {
+    #pragma unroll
+                for (int r = 0; r < QB; ++r) {
+                    if constexpr (LAZY) {
+                        move_ref(r, sc);
+    #pragma unroll
+                        for (int q = 0; q < 8 * KB; ++q) probs(r, q, sc);
+                    }
+                    const float alpha = fast_exp2(st_mold[r] - mc_run[r]);   // 1 for a row that stays
+    #pragma unroll
+                    for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+                        for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha;
+                    if constexpr (RSUM) l_run[r] *= alpha;
+                    lf_run[r] *= alpha;
+                }
+            }
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
     #pragma unroll
@@ -585,21 +660,9 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                     materialize(pc[r][jj]);
                 }
             }
-            if (upd_mask != 0) [[unlikely]] {
-    #pragma unroll
-                for (int r = 0; r < QB; ++r) {
-                    const float alpha = fast_exp2(st_mold[r] - mc_run[r]);   // 1 for a row that stays
-    #pragma unroll
-                    for (int cb = 0; cb < DB; ++cb)
-    #pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha;
-                    if constexpr (!F8) l_run[r] *= alpha;
-                    lf_run[r] *= alpha;
-                }
-            }
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
-                if constexpr (!F8) l_run[r] += st_ls[r];
+                if constexpr (RSUM) l_run[r] += st_ls[r];
                 lf_run[r] += st_lfs[r];
             }
             wait_vmem_upto<INFLIGHT>();
@@ -640,9 +703,10 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
     #pragma unroll
         for (int r = 0; r < QB; ++r) {
-            // (8-bit: O is normalised by the fp32 sum and scaled by V's descale)
+            // (bf16 and 8-bit: O is normalised by the fp32 sum; 8-bit: and scaled
+            // by V's descale)
             float l_tot, lf_tot;
-            if constexpr (F8) {
+            if constexpr (!RSUM) {
                 lf_tot = sum32(lf_run[r]);
                 l_tot = lf_tot;
             } else {
