@@ -12,7 +12,7 @@
 // Two kernels, both deterministic (every output element is owned by one
 // lane of one wave, no atomics):
 //   dq_kernel   one workgroup per 128 query rows; streams K/V tiles.  It
-//               also stores D_i and lse_i log2(e) of its rows in the
+//               also stores -D_i and lse_i log2(e) of its rows in the
 //               workspace for the second kernel.
 //   dkdv_kernel one workgroup per 128 keys; streams Q/dO tiles together
 //               with their D and lse values.
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     const float delta = sum32(dpart) * (DROP ? 1.f / a.drop.scale : 1.f);
     const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
     if (live && h == 0) {
-        a.ws[(size_t)bh * NP + qrow] = delta;
+        a.ws[(size_t)bh * NP + qrow] = -delta;   // the dk/dv kernel starts its dP sums from it
         a.ws[((size_t)a.BH + bh) * NP + qrow] = lse2;
     }
 
@@ -550,6 +550,16 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         // DSD steps ahead by inline assembly, waited for explicitly
         constexpr int NSD = 2 * DK, DSD = 3;
         f32x16 s, dp;
+        // the dP chain starts from -D of the lane's rows (the workspace holds
+        // -D; -D' under dropout), so that it ends at dP - D; element r of the
+        // accumulator is row 32 qh + 8(r/4) + 4h + r%4, as -D is laid out
+        f32x16 dinit;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 nd = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dinit[4 * rr + e] = nd[e];
+        }
         i32x4 fa[DSD + 1], fb[DSD + 1];
         auto rd = [&](int i) __attribute__((always_inline)) {
             const int kk = i >> 1, g = i & 1;
@@ -566,7 +576,7 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
             if ((i & 1) == 0)
                 s = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? f32x16{} : s);
             else
-                dp = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? f32x16{} : dp);
+                dp = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? dinit : dp);
             if (i + DSD < NSD) rd(i + DSD);
         }
         // Dropout: this lane runs the generator call of row 32 qh + l32 and
@@ -593,7 +603,8 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const f32x4 l4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + 32 * rr);
-            const f32x4 d4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
+            f32x4 nd4 = {};   // -D' (dropout)
+            if (DROP) nd4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rr + e;
@@ -602,10 +613,10 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
                 if (DROP) {
                     const bool kp = drop_keep(mw[rr], e, a.drop.t);
                     p[r] = kp ? pv : 0.f;                    // weights applied to dO (dV)
-                    s[r] = pv * ((kp ? dp[r] : 0.f) - d4[e]);   // dS / r
+                    s[r] = pv * (kp ? dp[r] : nd4[e]);   // dS / r (dp holds dP~ - D')
                 } else {
                     p[r] = pv;
-                    s[r] = pv * (dp[r] - d4[e]);   // dS
+                    s[r] = pv * dp[r];   // dS (dp holds dP - D)
                 }
             }
         }

@@ -207,7 +207,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * the same stream with the same arguments.
  *
  * attn_bwd_dq computes dq and fills `workspace` with two values per query
- * row (D_i = dO_i . o_i and lse_i log2(e)); it reads q, k, v, o, dO, lse and
+ * row (-D_i, D_i = dO_i . o_i, and lse_i log2(e)); it reads q, k, v, o, dO, lse and
  * writes dq and the workspace.  attn_bwd_dkdv computes dk and dv; it reads
  * q, k, v, dO and a workspace filled by attn_bwd_dq for the same inputs,
  * sizes and flags (enqueued earlier on the same stream, or otherwise
