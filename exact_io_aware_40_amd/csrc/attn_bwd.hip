@@ -189,6 +189,14 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     constexpr int ROWB = D * 2, TILE = BKT * ROWB, LOADS = TILE / (NT * 16);
     constexpr int KB = BKT / 32, DK = D / 16, DB = D / 32;
     constexpr bool SPLIT = SplitDS<T>::value;
+    // SEED: every dP^T chain starts from -D_i (the lane's row) held in 16
+    // registers for the whole kernel, so that it ends at dP - D and dS takes
+    // one multiply.  Used where it measured faster: bf16, d = 128, causal
+    // (at d = 128 the other types and the unmasked kernel spill with it; at
+    // d = 64 the fp16 kernel ran 4% slower).  Elsewhere dS subtracts D.
+    // Plain and dropout instantiations of one type, size and mask make the
+    // same choice.
+    constexpr bool SEED = D == 128 && CAUSAL && std::is_same_v<T, __bf16>;
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // [stage][K | V]
 
@@ -233,6 +241,11 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     // D_i, divided by the keep factor under dropout
     const float delta = sum32(dpart) * (DROP ? 1.f / a.drop.scale : 1.f);
     const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+    f32x16 ndseed = {};
+    if constexpr (SEED) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ndseed[r] = -delta;
+    }
     if (live && h == 0) {
         a.ws[(size_t)bh * NP + qrow] = -delta;   // the dk/dv kernel starts its dP sums from it
         a.ws[((size_t)a.BH + bh) * NP + qrow] = lse2;
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
                 if ((i & 1) == 0)
                     s = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
                 else
-                    dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? f32x16{} : dp);
+                    dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? ndseed : dp);
                 if (i + DSD < NSD) rd(i + DSD);
             }
 #pragma unroll
@@ -332,8 +345,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
                     const bool ok = key < N && (!CAUSAL || key <= qrow);
                     p = ok ? p : 0.f;
                 }
-                const float g = (DROP && !drop_keep(ph[r >> 2], r & 3, a.drop.t)) ? 0.f : dp[r];
-                s[r] = p * (g - delta);
+                const bool kp = !DROP || drop_keep(ph[r >> 2], r & 3, a.drop.t);
+                if constexpr (SEED) s[r] = p * (kp ? dp[r] : -delta);   // dp holds dP - D
+                else s[r] = p * ((kp ? dp[r] : 0.f) - delta);
             }
             dsb[b][0] = pack8<T>(s, 0);
             dsb[b][1] = pack8<T>(s, 1);
