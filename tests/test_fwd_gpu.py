@@ -91,6 +91,38 @@ def test_outlier_scores():
         run_and_compare(q, k, v, causal, 1 / math.sqrt(128), "outliers")
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_moves_and_bound(dtype, d, causal):
+    """Scores placed in binades around the exponent reference's bound (2^32
+    for bf16 operands, 2^15 for fp16; one K/V tile is 8 KiB of keys):
+    tile 0 all zero (the first tile moves the reference to 0); in tile 2
+    the keys held by one lane half sit one binade below the bound, so those
+    lanes' sums of P exceed it while no score asks the reference to move;
+    tile 4 has one key one binade past the bound (it must move); tile 6 a
+    whole tile a further 27 binades up (under the bf16 bound, whose lane
+    sums stay below 2^32; past the fp16 one, a second move).  The other
+    keys are N(0,1) / 4.  q = e_0 and scale = 1 make the score of key j its
+    k_j[0]."""
+    tau = 32.0 if dtype == torch.bfloat16 else 15.0
+    bc = 8192 // (2 * d)                     # keys per tile
+    N = 8 * bc
+    log2e = 1.0 / math.log(2.0)
+    B, H = 1, 2
+    k = randn((B, H, N, d), torch.float32, 4100 + d, scale=0.25)
+    q = torch.zeros((B, H, N, d))
+    q[..., 0] = 1.0
+    k[..., 0:bc, 0] = 0.0
+    j = torch.arange(2 * bc, 3 * bc)
+    k[..., j[(j % 8) < 4], 0] = (tau - 1.0) / log2e    # lane half 0 of every 32-key block
+    k[..., 4 * bc + 5, 0] = (tau + 1.0) / log2e
+    k[..., 6 * bc:7 * bc, 0] = (tau + 1.0 + 27.0) / log2e
+    v = randn((B, H, N, d), torch.float32, 4200 + d)
+    q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
+    run_and_compare(q, k, v, causal, 1.0, f"reference bound d={d}")
+
+
 def test_page_example_probe():
     """Explainer Step 4's eight scores through the kernel: q = e0,
     k_j = x_j e0, one-hot v_j = e_j, scale 1 -> each row of O is the
