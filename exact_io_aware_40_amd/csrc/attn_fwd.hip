@@ -153,9 +153,13 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     // fp32 sum of the tile's P, formed with the current reference (see the
     // softmax pieces); 8-bit: from the tile's row maximum, computed first.
     constexpr bool LAZY = !F8;
-    // fp16: O is normalised by the sum of P as rounded for the P.V product
-    // (its rounding, 2^-11 relative, would otherwise reach the fp16 output
-    // bound on rows dominated by one key); bf16 and 8-bit: by the fp32 sum
+    // The row normaliser l (it divides O and gives lse) is one sum per row.
+    // fp16: the sum of P as rounded for the P.V product, so that O's weights
+    // sum to one exactly as used (P's rounding, 2^-11 relative, would
+    // otherwise reach the fp16 output bound on rows dominated by one key),
+    // and lse is within 2^-11 relative of l's exact value.  bf16 and 8-bit:
+    // the fp32 sum of P (their P rounding, 2^-9 and 2^-4 relative, would move
+    // lse too far); O then carries that rounding, at most 2^-9 max|v| for bf16.
     constexpr bool RSUM = std::is_same_v<T, _Float16>;
     static_assert(!F8 || (D == 128 && !DROP), "the 8-bit forward is instantiated for d = 128 only");
     constexpr int BC = bc<T, D>();
@@ -325,15 +329,12 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[r][cb][e] = 0.f;
         // per row: exponent reference (scaled units), and this lane's share of
-        // the row's normaliser: the fp32 sum of P (it gives lse, and normalises
-        // O except under fp16) and, under fp16, the sum of P as rounded for the
-        // P.V product (it normalises O, so O's weights sum to one exactly as
-        // used)
-        float mc_run[QB], l_run[QB], lf_run[QB];
+        // the row's normaliser l
+        float mc_run[QB], l_run[QB];
         // (the reference starts at the lowest finite value: the first tile, whose
         // key 0 every row sees, always moves it, with alpha = 0)
     #pragma unroll
-        for (int r = 0; r < QB; ++r) mc_run[r] = -FLT_MAX, l_run[r] = 0.f, lf_run[r] = 0.f;
+        for (int r = 0; r < QB; ++r) mc_run[r] = -FLT_MAX, l_run[r] = 0.f;
 
         typedef f32x16 Scores[QB][KB];   // S^T of one tile, per row block and 32-key block
         typedef v8 Probs[QB][VK];        // P of one tile packed as B operands, per k-step
@@ -455,24 +456,25 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // 8-bit operands: row maximum over 8 scores (2 KB pieces); the
         // reference and the wave's rescale flags (1); then the probabilities.
         // 16-bit operands: the probabilities only, formed with the reference
-        // as it stands; the check after the tile's products finds the lanes
-        // whose fp32 sum of P exceeds 2^kTau (which holds for every lane whose
-        // P all stay within the bound, and fails for a P that is infinite or
-        // above it), and only then does the wave take the row maximum and
-        // redo the tile (slow_tile).  A probability piece forms two
-        // probabilities, their fp32 sum, their packed pair and (fp16) its sum
-        // as rounded (8 KB pieces).  The reference moves when the row maximum
+        // as it stands.  After the tile's products every lane compares its
+        // share of the tile's l with 2^kTau: a lane at or below it has all its
+        // P within the bound; a lane above it may hold a P above the bound or
+        // an infinite one (always so on the first tile), and then the wave
+        // takes the row maximum, moves the reference where that asks for it
+        // and forms the tile's probabilities again.  A probability piece
+        // forms two probabilities, their packed pair and their share of l
+        // (fp32, or fp16 as rounded) (8 KB pieces).  The reference moves when the row maximum
         // rose by more than kTau binades; the factor for the older
         // accumulation, 2^(old - new), is formed only in the rare branch that
-        // rescales O and the sums (also after the first tile, whose move from
-        // the lowest finite value gives the factor 0 for an O and sums that
-        // are still zero).
+        // rescales O and l (also after the first tile, whose move from the
+        // lowest finite value gives the factor 0 for an O and l that are
+        // still zero).
         // Under dropout, the first 10 KB pieces of a row are the rounds of its
         // generator calls, one per 32-key block (tile j0 / 32 + b).
         constexpr int NPD = DROP ? 10 * KB : 0;
         constexpr int NP_ROW = NPD + (LAZY ? 8 * KB : 10 * KB + 1);
         constexpr int NP = QB * NP_ROW;
-        float st_mt[QB], st_mold[QB], st_ls[QB], st_lfs[QB];
+        float st_mt[QB], st_mold[QB], st_l[QB];
         constexpr int PWD = (int)sizeof(raw) / 4;   // words of one P operand
         unsigned pw[QB][VK][PWD];
         unsigned ph[QB][KB][4];   // generator state, then the call's four words
@@ -490,20 +492,20 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 const bool hi = (e >> 1) & 1;
                 pw[r][jj][wd] = Elem<T>::cvt2_into(x0, x1, hi ? pw[r][jj][wd] : 0u, hi);
                 if (q == 0) {
-                    st_lfs[r] = x0 + x1;
+                    st_l[r] = x0 + x1;
                 } else {
-                    st_lfs[r] += x0;
-                    st_lfs[r] += x1;
+                    st_l[r] += x0;
+                    st_l[r] += x1;
                 }
             } else {
                 const unsigned pr = Elem<T>::cvt2(x0, x1);
-                if (q == 0) {
-                    st_lfs[r] = x0 + x1;
-                    if constexpr (RSUM) st_ls[r] = Elem<T>::sum2(pr, 0.f);
+                if constexpr (RSUM) {
+                    st_l[r] = Elem<T>::sum2(pr, q == 0 ? 0.f : st_l[r]);
+                } else if (q == 0) {
+                    st_l[r] = x0 + x1;
                 } else {
-                    st_lfs[r] += x0;
-                    st_lfs[r] += x1;
-                    if constexpr (RSUM) st_ls[r] = Elem<T>::sum2(pr, st_ls[r]);
+                    st_l[r] += x0;
+                    st_l[r] += x1;
                 }
                 if (DROP) {
                     // elements e, e + 1: bytes e % 4 and e % 4 + 1 of word e / 4
@@ -629,7 +631,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 // for it and forms the tile's probabilities again
                 bool over = false;
     #pragma unroll
-                for (int r = 0; r < QB; ++r) over |= st_lfs[r] > kBound<T>;
+                for (int r = 0; r < QB; ++r) over |= st_l[r] > kBound<T>;
                 upd_mask = __builtin_amdgcn_ballot_w64(over);
             }
             if (upd_mask != 0) [[unlikely]] {
@@ -645,8 +647,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                     for (int cb = 0; cb < DB; ++cb)
     #pragma unroll
                         for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha;
-                    if constexpr (RSUM) l_run[r] *= alpha;
-                    lf_run[r] *= alpha;
+                    l_run[r] *= alpha;
                 }
             }
     #pragma unroll
@@ -662,8 +663,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             }
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
-                if constexpr (RSUM) l_run[r] += st_ls[r];
-                lf_run[r] += st_lfs[r];
+                l_run[r] += st_l[r];
             }
             wait_vmem_upto<INFLIGHT>();
             barrier_only();
@@ -703,16 +703,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // epilogue: O = O^T / l, one rounding; lse = (mc + log2 l) ln 2
     #pragma unroll
         for (int r = 0; r < QB; ++r) {
-            // (bf16 and 8-bit: O is normalised by the fp32 sum; 8-bit: and scaled
-            // by V's descale)
-            float l_tot, lf_tot;
-            if constexpr (!RSUM) {
-                lf_tot = sum32(lf_run[r]);
-                l_tot = lf_tot;
-            } else {
-                l_tot = sum32(l_run[r]);
-                lf_tot = sum32(lf_run[r]);
-            }
+            // (8-bit: O is also scaled by V's descale)
+            const float l_tot = sum32(l_run[r]);
             // a row that sees no key of its chunk (split K/V only) gets O = 0 and
             // lse = -inf, which weigh nothing in the merge
             float inv = l_tot > 0.f ? fast_rcp(l_tot) * (DROP ? a.drop.scale : 1.f) : 0.f;
@@ -734,7 +726,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 }
                 if (h == 0)
                     a.lse[(size_t)split * a.split_lse + (size_t)bh * N + qr] =
-                        lf_tot > 0.f ? (mc_run[r] + fast_log2(lf_tot)) * 0.69314718055994531f : -INFINITY;
+                        l_tot > 0.f ? (mc_run[r] + fast_log2(l_tot)) * 0.69314718055994531f : -INFINITY;
             }
         }
         // the next item reuses the LDS buffers (this wave's copies have
