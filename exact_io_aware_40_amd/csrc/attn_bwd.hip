@@ -11,9 +11,10 @@
 //
 // Two kernels, both deterministic (every output element is owned by one
 // lane of one wave, no atomics):
-//   dq_kernel   one workgroup per 128 query rows; streams K/V tiles.  It
-//               also stores -D_i and lse_i log2(e) of its rows in the
-//               workspace for the second kernel.
+//   dq_kernel   one workgroup per 128 query rows (under causal masking per
+//               pair of a heavy and a light block of one head); streams K/V
+//               tiles.  It also stores -D_i and lse_i log2(e) of its rows in
+//               the workspace for the second kernel.
 //   dkdv_kernel one workgroup per 128 keys; streams Q/dO tiles together
 //               with their D and lse values.
 // Tiles move global -> LDS with 16-byte direct copies into two stages
@@ -206,224 +207,248 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     const int s16 = lane & 15, grp = lane >> 4;
 
     const int L = xcd_remap(blockIdx.x, total);
-    // (wave-uniform: kept in scalar registers)
-    const int bh = __builtin_amdgcn_readfirstlane(L / nqb);
-    int qb = __builtin_amdgcn_readfirstlane(L - bh * nqb);
-    if (CAUSAL) qb = nqb - 1 - qb;     // heaviest query blocks first
-    const int q0 = qb * BQ;
-    const size_t head = (size_t)bh * N * D;
-    const T* __restrict__ Qh = (const T*)a.q + head;
-    const T* __restrict__ Gh = (const T*)a.dO + head;
-    const TO* __restrict__ Oh = (const TO*)a.o + head;
-    const unsigned head_bytes = (unsigned)N * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
-
-    const int qlo = q0 + 32 * w;
-    const int qrow = qlo + l32;
-    const bool live = qrow < N;
-
-    // Q and dO fragments of this lane's row (B operands), and D_i
-    i32x4 qf[DK], gf[DK];
-    float dpart = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-        i32x4 x = {0, 0, 0, 0}, g = {0, 0, 0, 0};
-        if (live) {
-            const size_t off = (size_t)qrow * D + 16 * kk + 8 * h;
-            x = *(const i32x4*)(Qh + off);
-            g = *(const i32x4*)(Gh + off);
-            dpart += RowDot<T, TO>::run(Gh, Oh, off);
-        }
-        qf[kk] = x;
-        gf[kk] = g;
+    // Work: one query block of one (batch, head); under causal masking the
+    // pair of blocks nqb-1-p and p of one head, one after the other, so that
+    // every workgroup streams about as many K/V tiles as any other and the
+    // grid has no tail of heavy blocks (wave-uniform: kept in scalar registers)
+    int bh, qb_first, qb_second = 0, nitems = 1;
+    if (CAUSAL) {
+        const int npairs = (nqb + 1) >> 1;
+        bh = L / npairs;
+        const int p = L - bh * npairs;
+        qb_first = nqb - 1 - p;
+        qb_second = p;
+        nitems = p != nqb - 1 - p ? 2 : 1;
+    } else {
+        bh = L / nqb;
+        qb_first = L - bh * nqb;
     }
-    // D_i, divided by the keep factor under dropout
-    const float delta = sum32(dpart) * (DROP ? 1.f / a.drop.scale : 1.f);
-    const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
-    f32x16 ndseed = {};
-    if constexpr (SEED) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ndseed[r] = -delta;
-    }
-    if (live && h == 0) {
-        a.ws[(size_t)bh * NP + qrow] = -delta;   // the dk/dv kernel starts its dP sums from it
-        a.ws[((size_t)a.BH + bh) * NP + qrow] = lse2;
-    }
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    qb_first = __builtin_amdgcn_readfirstlane(qb_first);
+    qb_second = __builtin_amdgcn_readfirstlane(qb_second);
+    nitems = __builtin_amdgcn_readfirstlane(nitems);
+    // One query block; every tile step ends with a wait for this wave's
+    // copies and a barrier, so a second block may refill the stages at once.
+    // (called once or twice: one copy of the code per call, so that each is
+    // allocated registers on its own)
+    auto block = [&](const int qb) __attribute__((always_inline)) {
+        const int q0 = qb * BQ;
+        const size_t head = (size_t)bh * N * D;
+        const T* __restrict__ Qh = (const T*)a.q + head;
+        const T* __restrict__ Gh = (const T*)a.dO + head;
+        const TO* __restrict__ Oh = (const TO*)a.o + head;
+        const unsigned head_bytes = (unsigned)N * ROWB;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
 
-    const int kend = CAUSAL ? min(N, q0 + BQ) : N;
-    const int ntiles = (kend + BKT - 1) / BKT;
+        const int qlo = q0 + 32 * w;
+        const int qrow = qlo + l32;
+        const bool live = qrow < N;
 
-    unsigned src_off[LOADS];
-    tile_sources<D, LOADS>(src_off, w, lane);
-    auto issue = [&](auto stg, int t) {
-        char* st = smem + decltype(stg)::value * 2 * TILE;
-        const unsigned base = (unsigned)t * TILE;
-#pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            dma16_async(krs, lds_addr(st + (p * 4 + w) * 1024), base + src_off[p]);
-            dma16_async(vrs, lds_addr(st + TILE + (p * 4 + w) * 1024), base + src_off[p]);
-        }
-    };
-
-    // K and V rows as A operands (16-byte reads, LDS byte addresses), K^T
-    // through transposing reads
-    unsigned roff[DK];
-    const unsigned lbase = lds_addr(smem);
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) roff[kk] = lbase + t_off<D>(l32, 2 * kk + h);
-    int toff[2][DB];
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-        const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-        const int r0 = 4 * h + (s16 >> 2);
-        toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
-        toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
-    }
-
-    const float c = a.c;
-    f32x16 acc[DB];
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-
-    auto tile = [&](auto stg, auto mask, int j0) {
-        constexpr int STG = decltype(stg)::value;
-        constexpr bool MASK = decltype(mask)::value;
-        const char* sK = smem + STG * 2 * TILE;
-        const char* sV = sK + TILE;
-        int nb = KB;
-        if (MASK) {
-            if (CAUSAL) {
-                const int lim = qlo + 31 - j0;
-                nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
+        // Q and dO fragments of this lane's row (B operands), and D_i
+        i32x4 qf[DK], gf[DK];
+        float dpart = 0.f;
+    #pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            i32x4 x = {0, 0, 0, 0}, g = {0, 0, 0, 0};
+            if (live) {
+                const size_t off = (size_t)qrow * D + 16 * kk + 8 * h;
+                x = *(const i32x4*)(Qh + off);
+                g = *(const i32x4*)(Gh + off);
+                dpart += RowDot<T, TO>::run(Gh, Oh, off);
             }
-            nb = min(nb, (N - j0 + 31) / 32);
+            qf[kk] = x;
+            gf[kk] = g;
         }
-        v8 dsb[KB][2], dsl[KB][2];
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            if (MASK && b >= nb) continue;
-            f32x16 s, dp;
-            // the row's generator call for this 32-key block: element r is
-            // byte r % 4 of word r / 4
-            unsigned ph[4];
-            if (DROP) {
-                ph[0] = (unsigned)qrow;
-                ph[1] = (unsigned)(2 * ((j0 >> 5) + b) + h);
-                ph[2] = (unsigned)bh;
-                ph[3] = a.drop.offset;
-#pragma unroll
-                for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
+        // D_i, divided by the keep factor under dropout
+        const float delta = sum32(dpart) * (DROP ? 1.f / a.drop.scale : 1.f);
+        const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+        f32x16 ndseed = {};
+        if constexpr (SEED) {
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) ndseed[r] = -delta;
+        }
+        if (live && h == 0) {
+            a.ws[(size_t)bh * NP + qrow] = -delta;   // the dk/dv kernel starts its dP sums from it
+            a.ws[((size_t)a.BH + bh) * NP + qrow] = lse2;
+        }
+
+        const int kend = CAUSAL ? min(N, q0 + BQ) : N;
+        const int ntiles = (kend + BKT - 1) / BKT;
+
+        unsigned src_off[LOADS];
+        tile_sources<D, LOADS>(src_off, w, lane);
+        auto issue = [&](auto stg, int t) {
+            char* st = smem + decltype(stg)::value * 2 * TILE;
+            const unsigned base = (unsigned)t * TILE;
+    #pragma unroll
+            for (int p = 0; p < LOADS; ++p) {
+                dma16_async(krs, lds_addr(st + (p * 4 + w) * 1024), base + src_off[p]);
+                dma16_async(vrs, lds_addr(st + TILE + (p * 4 + w) * 1024), base + src_off[p]);
             }
-            // S^T = K Q^T and dP^T = V dO^T alternate (step i is chain i % 2,
-            // k-step i / 2); each step's K or V fragment is read DSD steps
-            // ahead by inline assembly and waited for explicitly
-            constexpr int NSD = 2 * DK, DSD = 3;
-            i32x4 fr[DSD + 1];
-            auto rd = [&](int i) __attribute__((always_inline)) {
-                fr[i % (DSD + 1)] = lds_read_b128_asm(roff[i >> 1], STG * 2 * TILE + (i & 1) * TILE + 32 * b * ROWB);
-            };
-#pragma unroll
-            for (int i = 0; i < DSD; ++i) rd(i);
-#pragma unroll
-            for (int i = 0; i < NSD; ++i) {
-                WaitSel1<DSD - 1>::run(min(DSD - 1, NSD - 1 - i), fr[i % (DSD + 1)]);
-                const int kk = i >> 1;
-                if ((i & 1) == 0)
-                    s = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
-                else
-                    dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? ndseed : dp);
-                if (i + DSD < NSD) rd(i + DSD);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(s[r], c, -lse2));
-                if (MASK) {
-                    const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool ok = key < N && (!CAUSAL || key <= qrow);
-                    p = ok ? p : 0.f;
+        };
+
+        // K and V rows as A operands (16-byte reads, LDS byte addresses), K^T
+        // through transposing reads
+        unsigned roff[DK];
+        const unsigned lbase = lds_addr(smem);
+    #pragma unroll
+        for (int kk = 0; kk < DK; ++kk) roff[kk] = lbase + t_off<D>(l32, 2 * kk + h);
+        int toff[2][DB];
+    #pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+            const int r0 = 4 * h + (s16 >> 2);
+            toff[0][cb] = t_off<D>(r0, col >> 3) + (col & 7) * 2;
+            toff[1][cb] = t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2;
+        }
+
+        const float c = a.c;
+        f32x16 acc[DB];
+    #pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+        auto tile = [&](auto stg, auto mask, int j0) {
+            constexpr int STG = decltype(stg)::value;
+            constexpr bool MASK = decltype(mask)::value;
+            const char* sK = smem + STG * 2 * TILE;
+            const char* sV = sK + TILE;
+            int nb = KB;
+            if (MASK) {
+                if (CAUSAL) {
+                    const int lim = qlo + 31 - j0;
+                    nb = lim < 0 ? 0 : min(KB, lim / 32 + 1);
                 }
-                const bool kp = !DROP || drop_keep(ph[r >> 2], r & 3, a.drop.t);
-                if constexpr (SEED) s[r] = p * (kp ? dp[r] : -delta);   // dp holds dP - D
-                else s[r] = p * ((kp ? dp[r] : 0.f) - delta);
+                nb = min(nb, (N - j0 + 31) / 32);
             }
-            dsb[b][0] = pack8<T>(s, 0);
-            dsb[b][1] = pack8<T>(s, 1);
-            if (SPLIT) {
-                dsl[b][0] = pack8_lo<T>(s, 0, dsb[b][0]);
-                dsl[b][1] = pack8_lo<T>(s, 1, dsb[b][1]);
+            v8 dsb[KB][2], dsl[KB][2];
+    #pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                if (MASK && b >= nb) continue;
+                f32x16 s, dp;
+                // the row's generator call for this 32-key block: element r is
+                // byte r % 4 of word r / 4
+                unsigned ph[4];
+                if (DROP) {
+                    ph[0] = (unsigned)qrow;
+                    ph[1] = (unsigned)(2 * ((j0 >> 5) + b) + h);
+                    ph[2] = (unsigned)bh;
+                    ph[3] = a.drop.offset;
+    #pragma unroll
+                    for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
+                }
+                // S^T = K Q^T and dP^T = V dO^T alternate (step i is chain i % 2,
+                // k-step i / 2); each step's K or V fragment is read DSD steps
+                // ahead by inline assembly and waited for explicitly
+                constexpr int NSD = 2 * DK, DSD = 3;
+                i32x4 fr[DSD + 1];
+                auto rd = [&](int i) __attribute__((always_inline)) {
+                    fr[i % (DSD + 1)] = lds_read_b128_asm(roff[i >> 1], STG * 2 * TILE + (i & 1) * TILE + 32 * b * ROWB);
+                };
+    #pragma unroll
+                for (int i = 0; i < DSD; ++i) rd(i);
+    #pragma unroll
+                for (int i = 0; i < NSD; ++i) {
+                    WaitSel1<DSD - 1>::run(min(DSD - 1, NSD - 1 - i), fr[i % (DSD + 1)]);
+                    const int kk = i >> 1;
+                    if ((i & 1) == 0)
+                        s = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
+                    else
+                        dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? ndseed : dp);
+                    if (i + DSD < NSD) rd(i + DSD);
+                }
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(s[r], c, -lse2));
+                    if (MASK) {
+                        const int key = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const bool ok = key < N && (!CAUSAL || key <= qrow);
+                        p = ok ? p : 0.f;
+                    }
+                    const bool kp = !DROP || drop_keep(ph[r >> 2], r & 3, a.drop.t);
+                    if constexpr (SEED) s[r] = p * (kp ? dp[r] : -delta);   // dp holds dP - D
+                    else s[r] = p * ((kp ? dp[r] : 0.f) - delta);
+                }
+                dsb[b][0] = pack8<T>(s, 0);
+                dsb[b][1] = pack8<T>(s, 1);
+                if (SPLIT) {
+                    dsl[b][0] = pack8_lo<T>(s, 0, dsb[b][0]);
+                    dsl[b][1] = pack8_lo<T>(s, 1, dsb[b][1]);
+                }
             }
-        }
-        // dQ^T += K^T dS^T
-        if constexpr (MASK) {
-#pragma unroll
-            for (int cb = 0; cb < DB; ++cb) {
-#pragma unroll
-                for (int b = 0; b < KB; ++b) {
-                    if (b >= nb) continue;
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int ro = (32 * b + 16 * q) * ROWB;
-                        const v8 kt = join8<v8>(lds_read_tr16(sK, toff[0][cb] + ro),
-                                                lds_read_tr16(sK, toff[1][cb] + ro));
-                        acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
-                        if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
+            // dQ^T += K^T dS^T
+            if constexpr (MASK) {
+    #pragma unroll
+                for (int cb = 0; cb < DB; ++cb) {
+    #pragma unroll
+                    for (int b = 0; b < KB; ++b) {
+                        if (b >= nb) continue;
+    #pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int ro = (32 * b + 16 * q) * ROWB;
+                            const v8 kt = join8<v8>(lds_read_tr16(sK, toff[0][cb] + ro),
+                                                    lds_read_tr16(sK, toff[1][cb] + ro));
+                            acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
+                            if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
+                        }
                     }
                 }
+            } else {
+                // every key block: step i is column block i / (2 KB), key block
+                // (i / 2) % KB, half i % 2; its two transposing reads are issued
+                // DTR steps ahead by inline assembly and waited for explicitly
+                constexpr int NTR = DB * KB * 2, DTR = 2;
+                i32x2 ta[DTR + 1], tb[DTR + 1];
+                const unsigned kl = lds_addr(smem);
+                auto rdt = [&](int i) __attribute__((always_inline)) {
+                    const int cb = i / (2 * KB), b = (i >> 1) % KB, q = i & 1;
+                    const int imm = STG * 2 * TILE + (32 * b + 16 * q) * ROWB;
+                    ta[i % (DTR + 1)] = lds_read_tr16_asm(kl + toff[0][cb], imm);
+                    tb[i % (DTR + 1)] = lds_read_tr16_asm(kl + toff[1][cb], imm);
+                };
+    #pragma unroll
+                for (int i = 0; i < DTR; ++i) rdt(i);
+    #pragma unroll
+                for (int i = 0; i < NTR; ++i) {
+                    WaitSelT<DTR - 1>::run(min(DTR - 1, NTR - 1 - i), ta[i % (DTR + 1)], tb[i % (DTR + 1)]);
+                    const int cb = i / (2 * KB), b = (i >> 1) % KB, q = i & 1;
+                    const v8 kt = join8<v8>(bit_cast<i16x4>(ta[i % (DTR + 1)]), bit_cast<i16x4>(tb[i % (DTR + 1)]));
+                    acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
+                    if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
+                    if (i + DTR < NTR) rdt(i + DTR);
+                }
             }
-        } else {
-            // every key block: step i is column block i / (2 KB), key block
-            // (i / 2) % KB, half i % 2; its two transposing reads are issued
-            // DTR steps ahead by inline assembly and waited for explicitly
-            constexpr int NTR = DB * KB * 2, DTR = 2;
-            i32x2 ta[DTR + 1], tb[DTR + 1];
-            const unsigned kl = lds_addr(smem);
-            auto rdt = [&](int i) __attribute__((always_inline)) {
-                const int cb = i / (2 * KB), b = (i >> 1) % KB, q = i & 1;
-                const int imm = STG * 2 * TILE + (32 * b + 16 * q) * ROWB;
-                ta[i % (DTR + 1)] = lds_read_tr16_asm(kl + toff[0][cb], imm);
-                tb[i % (DTR + 1)] = lds_read_tr16_asm(kl + toff[1][cb], imm);
-            };
-#pragma unroll
-            for (int i = 0; i < DTR; ++i) rdt(i);
-#pragma unroll
-            for (int i = 0; i < NTR; ++i) {
-                WaitSelT<DTR - 1>::run(min(DTR - 1, NTR - 1 - i), ta[i % (DTR + 1)], tb[i % (DTR + 1)]);
-                const int cb = i / (2 * KB), b = (i >> 1) % KB, q = i & 1;
-                const v8 kt = join8<v8>(bit_cast<i16x4>(ta[i % (DTR + 1)]), bit_cast<i16x4>(tb[i % (DTR + 1)]));
-                acc[cb] = Elem<T>::mma(kt, dsb[b][q], acc[cb]);
-                if (SPLIT) acc[cb] = Elem<T>::mma(kt, dsl[b][q], acc[cb]);
-                if (i + DTR < NTR) rdt(i + DTR);
-            }
-        }
-    };
+        };
 
-    auto step = [&](auto stg, int t) {
-        constexpr int STG = decltype(stg)::value;
-        if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
-        const int j0 = t * BKT;
-        const bool need_mask = (j0 + BKT > N) || (CAUSAL && j0 + BKT - 1 > qlo);
-        if (need_mask)
-            tile(stg, std::true_type{}, j0);
-        else
-            tile(stg, std::false_type{}, j0);
+        auto step = [&](auto stg, int t) {
+            constexpr int STG = decltype(stg)::value;
+            if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
+            const int j0 = t * BKT;
+            const bool need_mask = (j0 + BKT > N) || (CAUSAL && j0 + BKT - 1 > qlo);
+            if (need_mask)
+                tile(stg, std::true_type{}, j0);
+            else
+                tile(stg, std::false_type{}, j0);
+            wait_vmem();
+            __syncthreads();
+        };
+
+        issue(IC<0>{}, 0);
         wait_vmem();
         __syncthreads();
+        int t = 0;
+        for (; t + 1 < ntiles; t += 2) {
+            step(IC<0>{}, t);
+            step(IC<1>{}, t + 1);
+        }
+        if (t < ntiles) step(IC<0>{}, t);
+
+        if (live) store_rows<TO, D>((TO*)a.dq + head + (size_t)qrow * D, acc, a.scale * (DROP ? a.drop.scale : 1.f), h);
     };
-
-    issue(IC<0>{}, 0);
-    wait_vmem();
-    __syncthreads();
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-        step(IC<0>{}, t);
-        step(IC<1>{}, t + 1);
-    }
-    if (t < ntiles) step(IC<0>{}, t);
-
-    if (live) store_rows<TO, D>((TO*)a.dq + head + (size_t)qrow * D, acc, a.scale * (DROP ? a.drop.scale : 1.f), h);
+    block(qb_first);
+    if (CAUSAL && nitems == 2) block(qb_second);
 }
 
 // --------------------------------------------------------------------------
@@ -731,7 +756,7 @@ template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 hipError_t launch(const BwdArgs& a, int which, hipStream_t stream) {
     if (which & 1) {
         const int nqb = (a.N + BQ - 1) / BQ;
-        const int tq = a.BH * nqb;
+        const int tq = a.BH * (CAUSAL ? (nqb + 1) / 2 : nqb);   // causal: pairs of query blocks
         hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL, DROP>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
