@@ -15,8 +15,9 @@
 //               pair of a heavy and a light block of one head); streams K/V
 //               tiles.  It also stores -D_i and lse_i log2(e) of its rows in
 //               the workspace for the second kernel.
-//   dkdv_kernel one workgroup per 128 keys; streams Q/dO tiles together
-//               with their D and lse values.
+//   dkdv_kernel one workgroup per 128 keys (under causal masking per pair of
+//               a heavy and a light block of one head); streams Q/dO tiles
+//               together with their D and lse values.
 // Tiles move global -> LDS with 16-byte direct copies into two stages
 // (one barrier per tile); loads past the end of the sequence read zeros,
 // which makes such rows contribute nothing (their dO, Q, lse and D are 0).
@@ -488,267 +489,293 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     const int s16 = lane & 15, grp = lane >> 4;
 
     const int L = xcd_remap(blockIdx.x, total);
-    // (wave-uniform: kept in scalar registers)
-    const int bh = __builtin_amdgcn_readfirstlane(L / nkb);
-    const int kblk = __builtin_amdgcn_readfirstlane(L - bh * nkb);   // ascending: most queries first under the mask
-    const int kb0 = kblk * BK;
-    const size_t head = (size_t)bh * N * D;
-    const unsigned head_bytes = (unsigned)N * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const T*)a.q + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t grs = make_rsrc((const T*)a.dO + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.ws + (size_t)bh * NP, (unsigned)N * 4);
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.ws + ((size_t)a.BH + bh) * NP, (unsigned)N * 4);
-
-    const int kw0 = kb0 + 32 * kg;      // this wave's first key
-    const int key = kw0 + l32;          // this lane's key
-
-    // LDS slot s of a [rows][D] region holds row s / (D/8), physical granule
-    // s % (D/8): the 16-byte piece at logical granule pg ^ key(row).
-    auto src_of = [&](int slot) {
-        const int row = slot / (D / 8), pg = slot % (D / 8);
-        return (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
-    };
-    // the block's K and V rows (rows past the end read as zeros)
-#pragma unroll
-    for (int p = 0; p < KLOADS; ++p) {
-        const int slot = (p * 8 + w) * 64 + lane;
-        const unsigned off = (unsigned)kb0 * ROWB + src_of(slot);
-        dma16_async(krs, lds_addr(smem + KOFF + (p * 8 + w) * 1024), off);
-        dma16_async(vrs, lds_addr(smem + KOFF + KVB + (p * 8 + w) * 1024), off);
+    // Work: one key block of one (batch, head); under causal masking the pair
+    // of blocks p (most queries) and nkb-1-p of one head, one after the
+    // other, so that every workgroup streams about as many Q/dO tiles as any
+    // other (wave-uniform: kept in scalar registers)
+    int bh, kb_first, kb_second = 0, nitems = 1;
+    if (CAUSAL) {
+        const int npairs = (nkb + 1) >> 1;
+        bh = L / npairs;
+        const int p = L - bh * npairs;
+        kb_first = p;
+        kb_second = nkb - 1 - p;
+        nitems = p != nkb - 1 - p ? 2 : 1;
+    } else {
+        bh = L / nkb;
+        kb_first = L - bh * nkb;
     }
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    kb_first = __builtin_amdgcn_readfirstlane(kb_first);
+    kb_second = __builtin_amdgcn_readfirstlane(kb_second);
+    nitems = __builtin_amdgcn_readfirstlane(nitems);
+    // One key block (called once or twice: one copy of the code per call, so
+    // that each is allocated registers on its own).
+    auto key_block = [&](const int kblk) __attribute__((always_inline)) {
+        const int kb0 = kblk * BK;
+        const size_t head = (size_t)bh * N * D;
+        const unsigned head_bytes = (unsigned)N * ROWB;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const T*)a.k + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const T*)a.v + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const T*)a.q + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc((const T*)a.dO + head, head_bytes);
+        const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.ws + (size_t)bh * NP, (unsigned)N * 4);
+        const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.ws + ((size_t)a.BH + bh) * NP, (unsigned)N * 4);
 
-    const int t0 = CAUSAL ? kb0 / BQT : 0;
-    const int ntiles = (N + BQT - 1) / BQT;
+        const int kw0 = kb0 + 32 * kg;      // this wave's first key
+        const int key = kw0 + l32;          // this lane's key
 
-    unsigned tsrc[TLOADS];
-#pragma unroll
-    for (int p = 0; p < TLOADS; ++p) tsrc[p] = src_of((p * 8 + w) * 64 + lane);
-    auto issue = [&](auto stg, int t) {
-        constexpr int STG = decltype(stg)::value;
-        char* st = smem + STG * STAGE;
-        const unsigned base = (unsigned)t * TILE;
-#pragma unroll
-        for (int p = 0; p < TLOADS; ++p) {
-            dma16_async(qrs, lds_addr(st + (p * 8 + w) * 1024), base + tsrc[p]);
-            dma16_async(grs, lds_addr(st + TILE + (p * 8 + w) * 1024), base + tsrc[p]);
-        }
-        // the tile's lse2 and D values: 64 floats each, 16 lanes of wave 0
-        if (w == 0 && lane < BQT / 4) {
-            const unsigned fo = (unsigned)(t * BQT + 4 * lane) * 4;
-            dma16_async(lrs, lds_addr(smem + LOFF + STG * 2 * BQT * 4), fo);
-            dma16_async(drs, lds_addr(smem + LOFF + STG * 2 * BQT * 4 + BQT * 4), fo);
-        }
-    };
-
-    // Per-lane LDS offsets; every read below adds only a compile-time
-    // immediate (stage, tensor, half tile) below 64 KiB.
-    // LDS byte addresses of this lane's Q (dO) and K (V) operand reads: rows l32
-    // (+ this wave's 32 rows) at granule 2kk + h; stage, tensor and V offsets
-    // are added as immediates
-    unsigned qaddr[DK], kaddr[DK];
-    const unsigned lbase = lds_addr(smem);
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
-        const int o = t_off<D>(l32, 2 * kk + h);
-        qaddr[kk] = lbase + o + 32 * qh * ROWB;
-        kaddr[kk] = lbase + o + 32 * kg * ROWB + KOFF;
-    }
-    // transposing reads (LDS byte addresses): rows 32qh + 4h + s16/4 (+8)
-    unsigned taddr[2][DB];
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-        const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
-        const int r0 = 4 * h + (s16 >> 2);
-        taddr[0][cb] = lbase + t_off<D>(r0, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
-        taddr[1][cb] = lbase + t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
-    }
-    const int laddr = LOFF + (32 * qh + 4 * h) * 4;   // lse2 / D of this lane's rows
-
-    const float c = a.c;   // signed exponent unit: no maximum is tracked here
-    f32x16 dk[DB], dv[DB];
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            dk[cb][r] = 0.f;
-            dv[cb][r] = 0.f;
-        }
-
-    // This wave's 32 queries of a staged tile.  MASK: the block straddles
-    // the causal diagonal of this wave's keys (only the first two tiles of a
-    // key block can; they run before the main loop).
-    auto block = [&](auto stg, auto mask, int i0) {
-        constexpr int STG = decltype(stg)::value;
-        constexpr bool MASK = decltype(mask)::value;
-        const char* sQ = smem + STG * STAGE;
-        const char* sG = sQ + TILE;
-        // S = Q K^T and dP = dO V^T: the two chains alternate (step i is
-        // chain i % 2, k-step i / 2), and each step's operand pair is read
-        // DSD steps ahead by inline assembly, waited for explicitly
-        constexpr int NSD = 2 * DK, DSD = 3;
-        f32x16 s, dp;
-        // the dP chain starts from -D of the lane's rows (the workspace holds
-        // -D; -D' under dropout), so that it ends at dP - D; element r of the
-        // accumulator is row 32 qh + 8(r/4) + 4h + r%4, as -D is laid out
-        f32x16 dinit;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 nd = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dinit[4 * rr + e] = nd[e];
-        }
-        i32x4 fa[DSD + 1], fb[DSD + 1];
-        auto rd = [&](int i) __attribute__((always_inline)) {
-            const int kk = i >> 1, g = i & 1;
-            fa[i % (DSD + 1)] = lds_read_b128_asm(qaddr[kk], STG * STAGE + g * TILE);
-            fb[i % (DSD + 1)] = lds_read_b128_asm(kaddr[kk], g * KVB);
+        // LDS slot s of a [rows][D] region holds row s / (D/8), physical granule
+        // s % (D/8): the 16-byte piece at logical granule pg ^ key(row).
+        auto src_of = [&](int slot) {
+            const int row = slot / (D / 8), pg = slot % (D / 8);
+            return (unsigned)(row * ROWB + (pg ^ lds_key<D>(row)) * 16);
         };
-#pragma unroll
-        for (int i = 0; i < DSD; ++i) rd(i);
-#pragma unroll
-        for (int i = 0; i < NSD; ++i) {
-            const int later = min(DSD - 1, NSD - 1 - i);   // pairs read after this one
-            WaitSel2<DSD - 1>::run(later, fa[i % (DSD + 1)], fb[i % (DSD + 1)]);
-            const int kk = i >> 1;
-            if ((i & 1) == 0)
-                s = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? f32x16{} : s);
-            else
-                dp = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? dinit : dp);
-            if (i + DSD < NSD) rd(i + DSD);
+        // the block's K and V rows (rows past the end read as zeros)
+    #pragma unroll
+        for (int p = 0; p < KLOADS; ++p) {
+            const int slot = (p * 8 + w) * 64 + lane;
+            const unsigned off = (unsigned)kb0 * ROWB + src_of(slot);
+            dma16_async(krs, lds_addr(smem + KOFF + (p * 8 + w) * 1024), off);
+            dma16_async(vrs, lds_addr(smem + KOFF + KVB + (p * 8 + w) * 1024), off);
         }
-        // Dropout: this lane runs the generator call of row 32 qh + l32 and
-        // lane half h, whose byte e % 4 of word e / 4 belongs to key
-        // 8(e/4) + 4h + e%4 of the wave's 32; the bytes pass through the
-        // wave's LDS area as [key][row], from which the lane reads, for its
-        // key, rows 8(r/4) + 4h .. + 3 as one word per r/4.
-        unsigned mw[4];
-        if (DROP) {
-            unsigned ph[4] = {(unsigned)(i0 + 32 * qh + l32), (unsigned)(2 * (kw0 >> 5) + h), (unsigned)bh,
-                              a.drop.offset};
-#pragma unroll
-            for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
-            unsigned char* mt = (unsigned char*)smem + MOFF + w * 1024;
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mt[(8 * g + 4 * h + e) * 32 + l32] = (unsigned char)(ph[g] >> (8 * e));
-#pragma unroll
-            for (int g = 0; g < 4; ++g) mw[g] = *(const unsigned*)(mt + l32 * 32 + 8 * g + 4 * h);
+
+        const int t0 = CAUSAL ? kb0 / BQT : 0;
+        const int ntiles = (N + BQT - 1) / BQT;
+
+        unsigned tsrc[TLOADS];
+    #pragma unroll
+        for (int p = 0; p < TLOADS; ++p) tsrc[p] = src_of((p * 8 + w) * 64 + lane);
+        auto issue = [&](auto stg, int t) {
+            constexpr int STG = decltype(stg)::value;
+            char* st = smem + STG * STAGE;
+            const unsigned base = (unsigned)t * TILE;
+    #pragma unroll
+            for (int p = 0; p < TLOADS; ++p) {
+                dma16_async(qrs, lds_addr(st + (p * 8 + w) * 1024), base + tsrc[p]);
+                dma16_async(grs, lds_addr(st + TILE + (p * 8 + w) * 1024), base + tsrc[p]);
+            }
+            // the tile's lse2 and D values: 64 floats each, 16 lanes of wave 0
+            if (w == 0 && lane < BQT / 4) {
+                const unsigned fo = (unsigned)(t * BQT + 4 * lane) * 4;
+                dma16_async(lrs, lds_addr(smem + LOFF + STG * 2 * BQT * 4), fo);
+                dma16_async(drs, lds_addr(smem + LOFF + STG * 2 * BQT * 4 + BQT * 4), fo);
+            }
+        };
+
+        // Per-lane LDS offsets; every read below adds only a compile-time
+        // immediate (stage, tensor, half tile) below 64 KiB.
+        // LDS byte addresses of this lane's Q (dO) and K (V) operand reads: rows l32
+        // (+ this wave's 32 rows) at granule 2kk + h; stage, tensor and V offsets
+        // are added as immediates
+        unsigned qaddr[DK], kaddr[DK];
+        const unsigned lbase = lds_addr(smem);
+    #pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            const int o = t_off<D>(l32, 2 * kk + h);
+            qaddr[kk] = lbase + o + 32 * qh * ROWB;
+            kaddr[kk] = lbase + o + 32 * kg * ROWB + KOFF;
         }
-        // rows of this block held by the lane: 32 qh + 8(r/4) + 4h + r%4
-        f32x16 p;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 l4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + 32 * rr);
-            f32x4 nd4 = {};   // -D' (dropout)
-            if (DROP) nd4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * rr + e;
-                float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
-                if (MASK) pv = (key <= i0 + 32 * qh + 8 * rr + 4 * h + e) ? pv : 0.f;
-                if (DROP) {
-                    const bool kp = drop_keep(mw[rr], e, a.drop.t);
-                    p[r] = kp ? pv : 0.f;                    // weights applied to dO (dV)
-                    s[r] = pv * (kp ? dp[r] : nd4[e]);   // dS / r (dp holds dP~ - D')
-                } else {
-                    p[r] = pv;
-                    s[r] = pv * dp[r];   // dS (dp holds dP - D)
+        // transposing reads (LDS byte addresses): rows 32qh + 4h + s16/4 (+8)
+        unsigned taddr[2][DB];
+    #pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+            const int col = 32 * cb + 16 * (grp & 1) + 4 * (s16 & 3);
+            const int r0 = 4 * h + (s16 >> 2);
+            taddr[0][cb] = lbase + t_off<D>(r0, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
+            taddr[1][cb] = lbase + t_off<D>(r0 + 8, col >> 3) + (col & 7) * 2 + 32 * qh * ROWB;
+        }
+        const int laddr = LOFF + (32 * qh + 4 * h) * 4;   // lse2 / D of this lane's rows
+
+        const float c = a.c;   // signed exponent unit: no maximum is tracked here
+        f32x16 dk[DB], dv[DB];
+    #pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dk[cb][r] = 0.f;
+                dv[cb][r] = 0.f;
+            }
+
+        // This wave's 32 queries of a staged tile.  MASK: the block straddles
+        // the causal diagonal of this wave's keys (only the first two tiles of a
+        // key block can; they run before the main loop).
+        auto block = [&](auto stg, auto mask, int i0) {
+            constexpr int STG = decltype(stg)::value;
+            constexpr bool MASK = decltype(mask)::value;
+            const char* sQ = smem + STG * STAGE;
+            const char* sG = sQ + TILE;
+            // S = Q K^T and dP = dO V^T: the two chains alternate (step i is
+            // chain i % 2, k-step i / 2), and each step's operand pair is read
+            // DSD steps ahead by inline assembly, waited for explicitly
+            constexpr int NSD = 2 * DK, DSD = 3;
+            f32x16 s, dp;
+            // the dP chain starts from -D of the lane's rows (the workspace holds
+            // -D; -D' under dropout), so that it ends at dP - D; element r of the
+            // accumulator is row 32 qh + 8(r/4) + 4h + r%4, as -D is laid out
+            f32x16 dinit;
+    #pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 nd = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) dinit[4 * rr + e] = nd[e];
+            }
+            i32x4 fa[DSD + 1], fb[DSD + 1];
+            auto rd = [&](int i) __attribute__((always_inline)) {
+                const int kk = i >> 1, g = i & 1;
+                fa[i % (DSD + 1)] = lds_read_b128_asm(qaddr[kk], STG * STAGE + g * TILE);
+                fb[i % (DSD + 1)] = lds_read_b128_asm(kaddr[kk], g * KVB);
+            };
+    #pragma unroll
+            for (int i = 0; i < DSD; ++i) rd(i);
+    #pragma unroll
+            for (int i = 0; i < NSD; ++i) {
+                const int later = min(DSD - 1, NSD - 1 - i);   // pairs read after this one
+                WaitSel2<DSD - 1>::run(later, fa[i % (DSD + 1)], fb[i % (DSD + 1)]);
+                const int kk = i >> 1;
+                if ((i & 1) == 0)
+                    s = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? f32x16{} : s);
+                else
+                    dp = Elem<T>::mma(bit_cast<v8>(fa[i % (DSD + 1)]), bit_cast<v8>(fb[i % (DSD + 1)]), kk == 0 ? dinit : dp);
+                if (i + DSD < NSD) rd(i + DSD);
+            }
+            // Dropout: this lane runs the generator call of row 32 qh + l32 and
+            // lane half h, whose byte e % 4 of word e / 4 belongs to key
+            // 8(e/4) + 4h + e%4 of the wave's 32; the bytes pass through the
+            // wave's LDS area as [key][row], from which the lane reads, for its
+            // key, rows 8(r/4) + 4h .. + 3 as one word per r/4.
+            unsigned mw[4];
+            if (DROP) {
+                unsigned ph[4] = {(unsigned)(i0 + 32 * qh + l32), (unsigned)(2 * (kw0 >> 5) + h), (unsigned)bh,
+                                  a.drop.offset};
+    #pragma unroll
+                for (int n = 0; n < 10; ++n) philox_round(ph, a.drop.seed0, a.drop.seed1, n);
+                unsigned char* mt = (unsigned char*)smem + MOFF + w * 1024;
+    #pragma unroll
+                for (int g = 0; g < 4; ++g)
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) mt[(8 * g + 4 * h + e) * 32 + l32] = (unsigned char)(ph[g] >> (8 * e));
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) mw[g] = *(const unsigned*)(mt + l32 * 32 + 8 * g + 4 * h);
+            }
+            // rows of this block held by the lane: 32 qh + 8(r/4) + 4h + r%4
+            f32x16 p;
+    #pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 l4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + 32 * rr);
+                f32x4 nd4 = {};   // -D' (dropout)
+                if (DROP) nd4 = *(const f32x4*)(smem + laddr + STG * 2 * BQT * 4 + BQT * 4 + 32 * rr);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rr + e;
+                    float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
+                    if (MASK) pv = (key <= i0 + 32 * qh + 8 * rr + 4 * h + e) ? pv : 0.f;
+                    if (DROP) {
+                        const bool kp = drop_keep(mw[rr], e, a.drop.t);
+                        p[r] = kp ? pv : 0.f;                    // weights applied to dO (dV)
+                        s[r] = pv * (kp ? dp[r] : nd4[e]);   // dS / r (dp holds dP~ - D')
+                    } else {
+                        p[r] = pv;
+                        s[r] = pv * dp[r];   // dS (dp holds dP - D)
+                    }
                 }
             }
-        }
-        const v8 pb0 = pack8<T>(p, 0), pb1 = pack8<T>(p, 1);
-        const v8 db0 = pack8<T>(s, 0), db1 = pack8<T>(s, 1);
-        v8 dl0 = db0, dl1 = db1;
-        if (SPLIT) {
-            dl0 = pack8_lo<T>(s, 0, db0);
-            dl1 = pack8_lo<T>(s, 1, db1);
-        }
-        // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles):
-        // step i is column block i / 4, half (i / 2) % 2, dV for even i and dK
-        // for odd i; its two reads are issued DTR steps ahead
-        constexpr int NTR = 4 * DB, DTR = 3;
-        i32x2 ta[DTR + 1], tb[DTR + 1];
-        auto rdt = [&](int i) __attribute__((always_inline)) {
-            const int cb = i >> 2, q = (i >> 1) & 1, isq = i & 1;
-            const int imm = STG * STAGE + (isq ? 0 : TILE) + 16 * q * ROWB;
-            ta[i % (DTR + 1)] = lds_read_tr16_asm(taddr[0][cb], imm);
-            tb[i % (DTR + 1)] = lds_read_tr16_asm(taddr[1][cb], imm);
-        };
-#pragma unroll
-        for (int i = 0; i < DTR; ++i) rdt(i);
-#pragma unroll
-        for (int i = 0; i < NTR; ++i) {
-            WaitSelT<DTR - 1>::run(min(DTR - 1, NTR - 1 - i), ta[i % (DTR + 1)], tb[i % (DTR + 1)]);
-            const int cb = i >> 2, q = (i >> 1) & 1;
-            const v8 op = join8<v8>(bit_cast<i16x4>(ta[i % (DTR + 1)]), bit_cast<i16x4>(tb[i % (DTR + 1)]));
-            if ((i & 1) == 0) {
-                dv[cb] = Elem<T>::mma(op, q ? pb1 : pb0, dv[cb]);
-            } else {
-                dk[cb] = Elem<T>::mma(op, q ? db1 : db0, dk[cb]);
-                if (SPLIT) dk[cb] = Elem<T>::mma(op, q ? dl1 : dl0, dk[cb]);
+            const v8 pb0 = pack8<T>(p, 0), pb1 = pack8<T>(p, 1);
+            const v8 db0 = pack8<T>(s, 0), db1 = pack8<T>(s, 1);
+            v8 dl0 = db0, dl1 = db1;
+            if (SPLIT) {
+                dl0 = pack8_lo<T>(s, 0, db0);
+                dl1 = pack8_lo<T>(s, 1, db1);
             }
-            if (i + DTR < NTR) rdt(i + DTR);
-        }
-    };
+            // dV^T += dO^T P,  dK^T += Q^T dS  (transposing reads of the tiles):
+            // step i is column block i / 4, half (i / 2) % 2, dV for even i and dK
+            // for odd i; its two reads are issued DTR steps ahead
+            constexpr int NTR = 4 * DB, DTR = 3;
+            i32x2 ta[DTR + 1], tb[DTR + 1];
+            auto rdt = [&](int i) __attribute__((always_inline)) {
+                const int cb = i >> 2, q = (i >> 1) & 1, isq = i & 1;
+                const int imm = STG * STAGE + (isq ? 0 : TILE) + 16 * q * ROWB;
+                ta[i % (DTR + 1)] = lds_read_tr16_asm(taddr[0][cb], imm);
+                tb[i % (DTR + 1)] = lds_read_tr16_asm(taddr[1][cb], imm);
+            };
+    #pragma unroll
+            for (int i = 0; i < DTR; ++i) rdt(i);
+    #pragma unroll
+            for (int i = 0; i < NTR; ++i) {
+                WaitSelT<DTR - 1>::run(min(DTR - 1, NTR - 1 - i), ta[i % (DTR + 1)], tb[i % (DTR + 1)]);
+                const int cb = i >> 2, q = (i >> 1) & 1;
+                const v8 op = join8<v8>(bit_cast<i16x4>(ta[i % (DTR + 1)]), bit_cast<i16x4>(tb[i % (DTR + 1)]));
+                if ((i & 1) == 0) {
+                    dv[cb] = Elem<T>::mma(op, q ? pb1 : pb0, dv[cb]);
+                } else {
+                    dk[cb] = Elem<T>::mma(op, q ? db1 : db0, dk[cb]);
+                    if (SPLIT) dk[cb] = Elem<T>::mma(op, q ? dl1 : dl0, dk[cb]);
+                }
+                if (i + DTR < NTR) rdt(i + DTR);
+            }
+        };
 
-    auto step = [&](auto stg, auto mask, int t) {
-        constexpr int STG = decltype(stg)::value;
-        if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
-        const int i0 = t * BQT;
-        const int ib = i0 + 32 * qh;        // first query of this wave's rows
-        const bool skip = ib >= N || (CAUSAL && ib + 31 < kw0);   // every query before every key
-        if (!skip) block(stg, mask, i0);
+        auto step = [&](auto stg, auto mask, int t) {
+            constexpr int STG = decltype(stg)::value;
+            if (t + 1 < ntiles) issue(IC<1 - STG>{}, t + 1);
+            const int i0 = t * BQT;
+            const int ib = i0 + 32 * qh;        // first query of this wave's rows
+            const bool skip = ib >= N || (CAUSAL && ib + 31 < kw0);   // every query before every key
+            if (!skip) block(stg, mask, i0);
+            wait_vmem();
+            __syncthreads();
+        };
+
+        if (t0 < ntiles) issue(IC<0>{}, t0);
         wait_vmem();
         __syncthreads();
-    };
+        int t = t0;
+        if (CAUSAL) {
+            // the key block spans queries kb0 .. kb0 + 127: tiles t0 and t0 + 1
+            if (t < ntiles) step(IC<0>{}, std::true_type{}, t++);
+            if (t < ntiles) step(IC<1>{}, std::true_type{}, t++);
+        }
+        for (; t + 1 < ntiles; t += 2) {
+            step(IC<0>{}, std::false_type{}, t);
+            step(IC<1>{}, std::false_type{}, t + 1);
+        }
+        if (t < ntiles) step(IC<0>{}, std::false_type{}, t);
 
-    if (t0 < ntiles) issue(IC<0>{}, t0);
-    wait_vmem();
-    __syncthreads();
-    int t = t0;
-    if (CAUSAL) {
-        // the key block spans queries kb0 .. kb0 + 127: tiles t0 and t0 + 1
-        if (t < ntiles) step(IC<0>{}, std::true_type{}, t++);
-        if (t < ntiles) step(IC<1>{}, std::true_type{}, t++);
-    }
-    for (; t + 1 < ntiles; t += 2) {
-        step(IC<0>{}, std::false_type{}, t);
-        step(IC<1>{}, std::false_type{}, t + 1);
-    }
-    if (t < ntiles) step(IC<0>{}, std::false_type{}, t);
-
-    // the two query halves of each key group: qh = 1 hands its partial sums
-    // to qh = 0 through LDS ([kg][accumulator quad][lane] of 16 bytes)
-    f32x4* red = (f32x4*)smem + kg * (2 * DB * 4) * 64;
-    if (qh == 1) {
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                red[((cb * 4 + g) * 2 + 0) * 64 + lane] = {dk[cb][4 * g], dk[cb][4 * g + 1], dk[cb][4 * g + 2], dk[cb][4 * g + 3]};
-                red[((cb * 4 + g) * 2 + 1) * 64 + lane] = {dv[cb][4 * g], dv[cb][4 * g + 1], dv[cb][4 * g + 2], dv[cb][4 * g + 3]};
-            }
-    }
-    __syncthreads();
-    if (qh == 0 && key < N) {
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 xk = red[((cb * 4 + g) * 2 + 0) * 64 + lane];
-                const f32x4 xv = red[((cb * 4 + g) * 2 + 1) * 64 + lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dk[cb][4 * g + e] += xk[e];
-                    dv[cb][4 * g + e] += xv[e];
+        // the two query halves of each key group: qh = 1 hands its partial sums
+        // to qh = 0 through LDS ([kg][accumulator quad][lane] of 16 bytes)
+        f32x4* red = (f32x4*)smem + kg * (2 * DB * 4) * 64;
+        if (qh == 1) {
+    #pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    red[((cb * 4 + g) * 2 + 0) * 64 + lane] = {dk[cb][4 * g], dk[cb][4 * g + 1], dk[cb][4 * g + 2], dk[cb][4 * g + 3]};
+                    red[((cb * 4 + g) * 2 + 1) * 64 + lane] = {dv[cb][4 * g], dv[cb][4 * g + 1], dv[cb][4 * g + 2], dv[cb][4 * g + 3]};
                 }
-            }
-        const float rs = DROP ? a.drop.scale : 1.f;
-        store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale * rs, h);
-        store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, rs, h);
+        }
+        __syncthreads();
+        if (qh == 0 && key < N) {
+    #pragma unroll
+            for (int cb = 0; cb < DB; ++cb)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 xk = red[((cb * 4 + g) * 2 + 0) * 64 + lane];
+                    const f32x4 xv = red[((cb * 4 + g) * 2 + 1) * 64 + lane];
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dk[cb][4 * g + e] += xk[e];
+                        dv[cb][4 * g + e] += xv[e];
+                    }
+                }
+            const float rs = DROP ? a.drop.scale : 1.f;
+            store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale * rs, h);
+            store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, rs, h);
+        }
+    };
+    key_block(kb_first);
+    if (CAUSAL && nitems == 2) {
+        __syncthreads();   // the last block's LDS reads (its reduction) are done
+        key_block(kb_second);
     }
 }
 
@@ -763,7 +790,7 @@ hipError_t launch(const BwdArgs& a, int which, hipStream_t stream) {
     }
     if (which & 2) {
         const int nkb = (a.N + BK - 1) / BK;
-        const int tk = a.BH * nkb;
+        const int tk = a.BH * (CAUSAL ? (nkb + 1) / 2 : nkb);   // causal: pairs of key blocks
         hipLaunchKernelGGL((dkdv_kernel<T, TO, D, CAUSAL, DROP>), dim3(tk), dim3(NTK), 0, stream, a, nkb, tk);
         return hipGetLastError();
     }
