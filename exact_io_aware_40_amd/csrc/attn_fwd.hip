@@ -36,8 +36,9 @@
 // Schedule.  Iteration t of a wave issues, interleaved: the softmax of tile
 // t (vector ALU), cut into pieces; the products for S of tile t+1 and for
 // P.V of tile t-1 (matrix cores), whose LDS operands are read four steps
-// ahead; and the direct-to-LDS copies of K(t+3) and V(t+1) into rings of
-// four buffers.  The copies and the operand reads are written as inline
+// ahead; and the direct-to-LDS copies of K(t+4) and V(t+2) into rings of
+// five buffers (all 160 KiB of LDS at two workgroups per CU), which lets one
+// barrier serve two iterations.  The copies and the operand reads are written as inline
 // assembly so that neither waits for the other (they never touch the same
 // buffer), with explicit waits where the data is consumed.  Every wave
 // walks every tile of its block: tiles past a wave's diagonal are masked
@@ -77,8 +78,8 @@ constexpr int OCC = 2;            // workgroups per CU
 // keys per K/V tile: 8 KiB tiles
 template <typename T, int D> constexpr int bc() { return 8192 / ((int)sizeof(T) * D); }
 // LDS buffers for K tiles, and as many for V tiles, within a workgroup's
-// share of the 160 KiB (an even count)
-constexpr int RING = ((160 * 1024 / OCC) / (2 * 8192)) & ~1;
+// share of the 160 KiB (five)
+constexpr int RING = (160 * 1024 / OCC) / (2 * 8192);
 
 // The exponent's reference point moves only when a row's maximum rises by
 // more than kTau binades, so P <= 2^kTau and most tiles skip the rescale of
@@ -164,6 +165,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     static_assert(!F8 || (D == 128 && !DROP), "the 8-bit forward is instantiated for d = 128 only");
     constexpr int BC = bc<T, D>();
     static_assert(RING >= 4, "the pipeline needs four buffers per tensor");
+    static_assert(RING <= 5, "the lead distances and the barrier rule are written for four or five buffers");
     constexpr int KLEAD = RING - 1;   // iteration t starts the copy of K(t + KLEAD) ...
     constexpr int VLEAD = RING - 3;   // ... and of V(t + VLEAD)
     constexpr int ROWB = D * (int)sizeof(T);   // bytes per tile row
@@ -579,20 +581,27 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         };
 
         // Iteration t (t = 0 .. te-tb; tile numbers below are relative to tb):
-        // copies of K(t+KLEAD) and V(t+VLEAD)
-        // start, into K buffer (t-1)%RING and V buffer (t-3)%RING, which last
-        // held K(t-1) and V(t-3), read in iteration t-2 at the latest; softmax of
-        // tile t (scores in sc, P to pc), S of tile t+1 (to sn, K buffer
-        // (t+1)%RING), P.V of tile t-1 (P in pp, V buffer (t-1)%RING; for t = 0
-        // both are zero); then this wave waits for its copies of K(t+2) and V(t),
-        // started in iteration t+2-KLEAD, and a barrier makes every wave's copies
-        // visible to iteration t+1, which reads them.  Tile te-tb is all masked
-        // and its P is zero.
+        // copies of K(t+KLEAD) and V(t+VLEAD) start, into K buffer
+        // (t+KLEAD)%RING and V buffer (t+VLEAD)%RING, which last held
+        // K(t+KLEAD-RING) and V(t+VLEAD-RING), read in iteration t-2 at the
+        // latest; softmax of tile t (scores in sc, P to pc), S of tile t+1 (to
+        // sn, K buffer (t+1)%RING), P.V of tile t-1 (P in pp, V buffer
+        // (t-1)%RING; for t = 0 both are zero).  With five buffers (KLEAD = 4,
+        // VLEAD = 2) a barrier follows every odd iteration t only: before it
+        // each wave waits for all its copies but those of iteration t, so that
+        // K(t+2), K(t+3), V(t) and V(t+1), which iterations t+1 and t+2 read,
+        // are complete and visible; and every buffer those two iterations
+        // overwrite was last read in iteration t or earlier.  (With four
+        // buffers, KLEAD = 3 and VLEAD = 1: a wait for all copies but those of
+        // iterations t-1 and t, and a barrier, after every iteration.)  Tile
+        // te-tb is all masked and its P is zero.
         constexpr int INFLIGHT = (KLEAD - 2) * 2 * LOADS;   // copies younger than those waited for
         static_assert(KLEAD - 2 == VLEAD, "K and V copies of one iteration are waited for together");
         static_assert(INFLIGHT < 64, "vmcnt is six bits");
+        constexpr bool PAIRB = RING >= 5;   // a barrier every second iteration
+        constexpr int WAIT_AT_BARRIER = PAIRB ? 2 * LOADS : INFLIGHT;
         auto iter = [&](auto J, int t, Scores& sc, Scores& sn, Probs& pp, Probs& pc) __attribute__((always_inline)) {
-            constexpr int j = decltype(J)::value;   // t % RING
+            constexpr int j = decltype(J)::value;   // t modulo the unrolled group (RING or 2 RING)
             const int j0 = (tb + t) * BC;
             tile_j0 = j0;
             const bool need_mask = (j0 + BC > klim) || (CAUSAL && j0 + BC - 1 > qlo + coff);
@@ -665,8 +674,10 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             for (int r = 0; r < QB; ++r) {
                 l_run[r] += st_l[r];
             }
-            wait_vmem_upto<INFLIGHT>();
-            barrier_only();
+            if (!PAIRB || j % 2 == 1) {
+                wait_vmem_upto<WAIT_AT_BARRIER>();
+                barrier_only();
+            }
         };
 
         // Prologue: copies of K(0), K(1), then K(t+KLEAD) and V(t+VLEAD) in the
@@ -683,12 +694,13 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
         for (int p = 0; p < LOADS; ++p)
             *(i32x4*)(smem + (2 * RING - 1) * TILE + (p * NW + w) * 1024 + 16 * lane) = i32x4{0, 0, 0, 0};
-        wait_vmem_upto<INFLIGHT>();   // Q, K(0) and K(1)
+        wait_vmem_upto<WAIT_AT_BARRIER>();   // Q and all but the copies of "iteration -1"
         __syncthreads();
     #pragma unroll
         for (int i = 0; i < NF; ++i) s_frag(0, i, sA);
 
-        // iterations in groups of RING (buffer indices are constants); scores and
+        // iterations in groups of RING, or 2 RING for an odd RING (buffer
+        // indices and the barrier parity are constants); scores and
         // probabilities alternate between the A and B sets
         int t = 0;
         auto one = [&](auto J) __attribute__((always_inline)) {
@@ -696,7 +708,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             else iter(J, t, sB, sA, pB, pA);
             return ++t <= te - tb;
         };
-        while (for_ring(one, std::make_integer_sequence<int, RING>{})) {
+        while (for_ring(one, std::make_integer_sequence<int, RING % 2 ? 2 * RING : RING>{})) {
         }
         wait_vmem();   // no copy may still be writing LDS when the workgroup ends
 
