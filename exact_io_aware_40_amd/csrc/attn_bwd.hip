@@ -315,7 +315,6 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
             constexpr int STG = decltype(stg)::value;
             constexpr bool MASK = decltype(mask)::value;
             const char* sK = smem + STG * 2 * TILE;
-            const char* sV = sK + TILE;
             int nb = KB;
             if (MASK) {
                 if (CAUSAL) {
@@ -603,8 +602,6 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
         auto block = [&](auto stg, auto mask, int i0) {
             constexpr int STG = decltype(stg)::value;
             constexpr bool MASK = decltype(mask)::value;
-            const char* sQ = smem + STG * STAGE;
-            const char* sG = sQ + TILE;
             // S = Q K^T and dP = dO V^T: the two chains alternate (step i is
             // chain i % 2, k-step i / 2), and each step's operand pair is read
             // DSD steps ahead by inline assembly, waited for explicitly

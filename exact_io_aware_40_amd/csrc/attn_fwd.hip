@@ -95,10 +95,9 @@ template <> constexpr float kTau<_Float16> = 15.f;
 template <> constexpr float kTau<fp8e4m3> = 8.f;
 template <typename T> constexpr float kShift = 0.f;
 template <> constexpr float kShift<fp8e4m3> = 4.f;
-// 2^kTau
+// 2^kTau (the bound of the 16-bit forward's lane-sum check)
 template <typename T> constexpr float kBound = 4294967296.f;
 template <> constexpr float kBound<_Float16> = 32768.f;
-template <> constexpr float kBound<fp8e4m3> = 256.f;
 
 template <int V> using IC = std::integral_constant<int, V>;
 
