@@ -607,6 +607,22 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             uint64_t upd_mask = 0;
             issue(kbase, tb + t + KLEAD, (j + KLEAD) % RING);
             issue(vbase, tb + t + VLEAD, RING + (j + VLEAD) % RING);
+            // Under the causal mask the tiles past this wave's last row are
+            // masked for all its rows.  Once tile t-1 is (and so t and t+1, and
+            // every later tile), the iteration's products and softmax add
+            // nothing: they are skipped, with P = 0 and its sum 0 (the copies
+            // and the barrier stay, for the other waves).
+            const bool dead = CAUSAL && j0 - BC > qlo + 32 * QB - 1 + coff;
+            if (dead) [[unlikely]] {
+    #pragma unroll
+                for (int r = 0; r < QB; ++r) {
+                    st_l[r] = 0.f;
+    #pragma unroll
+                    for (int jj = 0; jj < VK; ++jj)
+    #pragma unroll
+                        for (int wd = 0; wd < PWD; ++wd) pw[r][jj][wd] = 0u;
+                }
+            } else {
             if (need_mask) [[unlikely]] apply_mask(sc, j0);
             {
                 constexpr int kbuf = (j + 1) % RING, vbuf = (j + RING - 1) % RING;
@@ -631,6 +647,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
+            }
             }
             if constexpr (LAZY) {
                 // a lane whose sum of P is at most 2^kTau has every P within the
