@@ -610,9 +610,11 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             // Under the causal mask the tiles past this wave's last row are
             // masked for all its rows.  Once tile t-1 is (and so t and t+1, and
             // every later tile), the iteration's products and softmax add
-            // nothing: they are skipped, with P = 0 and its sum 0 (the copies
-            // and the barrier stay, for the other waves).
-            const bool dead = CAUSAL && j0 - BC > qlo + 32 * QB - 1 + coff;
+            // nothing; nor do they for a wave whose rows all lie past the end
+            // of the queries (in a decode step most waves of a block).  They
+            // are then skipped, with P = 0 and its sum 0 (the copies and the
+            // barrier stay, for the other waves).
+            const bool dead = (CAUSAL && j0 - BC > qlo + 32 * QB - 1 + coff) || qlo >= N;
             if (dead) [[unlikely]] {
     #pragma unroll
                 for (int r = 0; r < QB; ++r) {
