@@ -586,11 +586,14 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // latest; softmax of tile t (scores in sc, P to pc), S of tile t+1 (to
         // sn, K buffer (t+1)%RING), P.V of tile t-1 (P in pp, V buffer
         // (t-1)%RING; for t = 0 both are zero).  With five buffers (KLEAD = 4,
-        // VLEAD = 2) a barrier follows every odd iteration t only: before it
-        // each wave waits for all its copies but those of iteration t, so that
+        // VLEAD = 2) a barrier follows every odd iteration t: before it each
+        // wave waits for all its copies but those of iteration t, so that
         // K(t+2), K(t+3), V(t) and V(t+1), which iterations t+1 and t+2 read,
         // are complete and visible; and every buffer those two iterations
-        // overwrite was last read in iteration t or earlier.  (With four
+        // overwrite was last read in iteration t or earlier.  One more barrier
+        // follows iteration 0: iteration 1 refills K buffer 0, last read in the
+        // prologue (S of tile 0), and a wave that skips its products (below)
+        // would otherwise reach that copy while others still read K(0).  (With four
         // buffers, KLEAD = 3 and VLEAD = 1: a wait for all copies but those of
         // iterations t-1 and t, and a barrier, after every iteration.)  Tile
         // te-tb is all masked and its P is zero.
@@ -694,6 +697,10 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             }
             if (!PAIRB || j % 2 == 1) {
                 wait_vmem_upto<WAIT_AT_BARRIER>();
+                barrier_only();
+            } else if (t == 0) {
+                // iteration 1 refills K buffer 0, whose K(0) every wave reads
+                // in the prologue: all waves must be past that first
                 barrier_only();
             }
         };
