@@ -723,6 +723,15 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         __syncthreads();
     #pragma unroll
         for (int i = 0; i < NF; ++i) s_frag(0, i, sA);
+        if constexpr (LAZY) {
+            // the reference from tile 0's (masked) row maximum, so that its P
+            // already stay within the bound and the first iteration needs no
+            // second pass (iteration 0 masks the tile again, to the same values)
+            const int j00 = tb * BC;
+            if ((j00 + BC > klim) || (CAUSAL && j00 + BC - 1 > qlo + coff)) apply_mask(sA, j00);
+    #pragma unroll
+            for (int r = 0; r < QB; ++r) move_ref(r, sA);
+        }
 
         // iterations in groups of RING, or 2 RING for an odd RING (buffer
         // indices and the barrier parity are constants); scores and
