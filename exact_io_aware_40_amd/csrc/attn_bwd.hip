@@ -378,8 +378,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
                     dsl[b][1] = pack8_lo<T>(s, 1, dsb[b][1]);
                 }
             }
-            // dQ^T += K^T dS^T
-            if constexpr (MASK) {
+            // dQ^T += K^T dS^T (a masked tile whose key blocks this wave all
+            // sees takes the pipelined loop below)
+            if (MASK && nb < KB) {
     #pragma unroll
                 for (int cb = 0; cb < DB; ++cb) {
     #pragma unroll
