@@ -460,7 +460,8 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         // as it stands.  After the tile's products every lane compares its
         // share of the tile's l with 2^kTau: a lane at or below it has all its
         // P within the bound; a lane above it may hold a P above the bound or
-        // an infinite one (always so on the first tile), and then the wave
+        // an infinite one (the prologue sets the reference from tile 0, so
+        // the first tile passes), and then the wave
         // takes the row maximum, moves the reference where that asks for it
         // and forms the tile's probabilities again.  A probability piece
         // forms two probabilities, their packed pair and their share of l
@@ -628,37 +629,37 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                         for (int wd = 0; wd < PWD; ++wd) pw[r][jj][wd] = 0u;
                 }
             } else {
-            if (need_mask) [[unlikely]] apply_mask(sc, j0);
-            {
-                constexpr int kbuf = (j + 1) % RING, vbuf = (j + RING - 1) % RING;
-                constexpr int NS = 2 * QB;   // products per step
-                Frag f[DIST + 1];
+                if (need_mask) [[unlikely]] apply_mask(sc, j0);
+                {
+                    constexpr int kbuf = (j + 1) % RING, vbuf = (j + RING - 1) % RING;
+                    constexpr int NS = 2 * QB;   // products per step
+                    Frag f[DIST + 1];
     #pragma unroll
-                for (int k = 0; k < DIST; ++k) load_frag(kbuf, vbuf, k, f[k]);
+                    for (int k = 0; k < DIST; ++k) load_frag(kbuf, vbuf, k, f[k]);
     #pragma unroll
-                for (int k = 0; k < NF; ++k) {
-                    Frag& cur = f[k % (DIST + 1)];
-                    const int later = min(DIST - 1, NF - 1 - k);   // steps read after this one
-                    if constexpr (F8) WaitSel6<DIST - 1>::run(later, cur.k, cur.k1, cur.v0, cur.v1, cur.v2, cur.v3);
-                    else WaitSel3<DIST - 1>::run(later, cur.k, cur.v0, cur.v1);
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int m = 0; m < NS; ++m) {
-                        const int slot = k * NS + m;
-                        product(k, m, cur, sn, pp);
-                        if (m == 0 && k + DIST < NF) load_frag(kbuf, vbuf, k + DIST, f[(k + DIST) % (DIST + 1)]);
-    #pragma unroll
-                        for (int p = slot * NP / NMM; p < (slot + 1) * NP / NMM; ++p) piece(p, sc, upd_mask);
+                    for (int k = 0; k < NF; ++k) {
+                        Frag& cur = f[k % (DIST + 1)];
+                        const int later = min(DIST - 1, NF - 1 - k);   // steps read after this one
+                        if constexpr (F8) WaitSel6<DIST - 1>::run(later, cur.k, cur.k1, cur.v0, cur.v1, cur.v2, cur.v3);
+                        else WaitSel3<DIST - 1>::run(later, cur.k, cur.v0, cur.v1);
                         __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                        for (int m = 0; m < NS; ++m) {
+                            const int slot = k * NS + m;
+                            product(k, m, cur, sn, pp);
+                            if (m == 0 && k + DIST < NF) load_frag(kbuf, vbuf, k + DIST, f[(k + DIST) % (DIST + 1)]);
+    #pragma unroll
+                            for (int p = slot * NP / NMM; p < (slot + 1) * NP / NMM; ++p) piece(p, sc, upd_mask);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
                 }
             }
-            }
             if constexpr (LAZY) {
                 // a lane whose sum of P is at most 2^kTau has every P within the
-                // bound; otherwise (a P above it or infinite, as on the first
-                // tile) the wave moves the reference where the row maximum asks
-                // for it and forms the tile's probabilities again
+                // bound; otherwise (a P above it or infinite) the wave moves the
+                // reference where the row maximum asks for it and forms the
+                // tile's probabilities again
                 bool over = false;
     #pragma unroll
                 for (int r = 0; r < QB; ++r) over |= st_l[r] > kBound<T>;
