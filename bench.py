@@ -51,22 +51,36 @@ from exact_io_aware_40_amd import inputs  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16/fp16 matrix peak
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 matrix peak
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["exact_io_aware_40_amd/csrc/attn_fwd.hip",
-                  "exact_io_aware_40_amd/csrc/attn_bwd.hip",
-                  "exact_io_aware_40_amd/csrc/attn_common.h"]
+# the sources each kernel is built from: the fused kernels' and the
+# materialised baseline's counter data are keyed separately
+KERNEL_SOURCES = {
+    "fused": ["exact_io_aware_40_amd/csrc/attn_fwd.hip",
+              "exact_io_aware_40_amd/csrc/attn_bwd.hip",
+              "exact_io_aware_40_amd/csrc/attn_common.h"],
+    "standard": ["exact_io_aware_40_amd/csrc/attn_std.hip",
+                 "exact_io_aware_40_amd/csrc/attn_common.h"],
+}
 
 
-def source_hash() -> str:
-    """Hash of the kernel sources with comments removed and whitespace
-    collapsed: it keys the committed counter data, which stays valid across
-    edits of comments and layout only."""
+def _family(kernel: str) -> str:
+    return "standard" if kernel.startswith("std_") else "fused"
+
+
+def source_hash(family: str = "fused") -> str:
+    """Hash of a kernel family's sources with comments removed and
+    whitespace collapsed, and of the compiler flags they are built with: it
+    keys the committed counter data, which stays valid across edits of
+    comments and layout only."""
+    from exact_io_aware_40_amd.csrc import build as hip_build
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
         h.update(" ".join(text.split()).encode())
+    flags = [f for f in hip_build.FLAGS if not f.startswith(ROOT) and f != "-I"]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
@@ -100,10 +114,20 @@ def parse():
                          "decode step (attn_fwd_decode_fp8)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output dirs")
+    ap.add_argument("--counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/counters.json from rocprofv3 --pmc output dirs")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the forward and step timings of the other workloads")
+    ap.add_argument("--other-steps", type=int, default=10,
+                    help="timed steps of each other workload")
+    ap.add_argument("--standard", action="store_true",
+                    help="time the materialised standard attention (S and P written to HBM) "
+                         "against the fused forward on the workload (default: the GPT-2-medium shape)")
     return ap.parse_args()
 
 
-KERNELS = ("fwd_kernel", "dq_kernel", "dkdv_kernel")
+KERNELS = ("fwd_kernel", "dq_kernel", "dkdv_kernel", "std_scores_kernel", "std_softmax_kernel",
+           "std_pv_kernel")
 COPY_BYTES = 512 << 20
 
 
@@ -140,12 +164,12 @@ def write_traffic(fetch_dir, write_dir, workload):
                 e[counter.lower() + "_bytes"] = factor * sum(per[k]) / len(per[k])
     for k, e in res.items():
         e["bytes"] = e.get("fetch_size_bytes", 0.0) + e.get("write_size_bytes", 0.0)
-        e["source_hash"] = source_hash()
+        e["source_hash"] = source_hash(_family(k))
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = {}
     if os.path.exists(path):
         rec = json.load(open(path))
-    rec[workload] = res
+    rec.setdefault(workload, {}).update(res)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps(rec[workload], indent=1))
@@ -193,9 +217,19 @@ def cpu_baseline(w, t, scale, budget_s, gpu_out=None):
         if w.dtype != "bf16":
             ex = np.maximum(ex, -14)   # fp16 subnormal spacing
         tol = 1.5e-2 if w.dtype == "bf16" else 2e-3
-        excess = np.abs(og - o_ref) - (tol + np.ldexp(0.5, (ex - mant).astype(np.int64)))
-        parity = {"rows": int(len(rows)), "max_abs_o": float(np.abs(og - o_ref).max()),
+        err = np.abs(og - o_ref)
+        excess = err - (tol + np.ldexp(0.5, (ex - mant).astype(np.int64)))
+        # the exact values' own rounding to the output type: elements that no
+        # output of that type can bring within the literal tolerance
+        own = np.abs(torch.from_numpy(o_ref).to(w.torch_dtype).double().numpy() - o_ref)
+        beyond = err > tol
+        parity = {"rows": int(len(rows)), "max_abs_o": float(err.max()),
                   "max_abs_lse": float(np.abs(lg - l_ref).max()), "tol_o": tol, "tol_lse": 1e-3,
+                  "o_elements": int(err.size),
+                  "o_elements_beyond_tol": int(beyond.sum()),
+                  "o_exact_values_beyond_tol_by_own_rounding": int((own > tol).sum()),
+                  "o_beyond_tol_where_own_rounding_is_beyond_tol": int((beyond & (own > tol)).sum()),
+                  "o_beyond_tol_within_tol_plus_half_ulp": int((beyond & (excess <= 0)).sum()),
                   "max_excess_o_over_tol_plus_half_ulp": float(excess.max())}
     i = rows % N
     keys = (i + 1) if w.causal else np.full_like(i, N)
@@ -356,6 +390,396 @@ def bench_fp8(args):
     print(json.dumps(out), flush=True)
 
 
+class StepRunner:
+    """The step's launches on one workload, inputs resident on the GPU: the
+    forward (attn_fwd), then the backward's two kernels (attn_bwd_dq,
+    attn_bwd_dkdv), or their dropout forms."""
+
+    def __init__(self, w, dev, dropout=None, t=None):
+        self.w = w
+        self.scale = 1.0 / math.sqrt(w.d)
+        if t is None:
+            t = inputs.make_inputs(w)
+        if "dO" not in t:
+            t["dO"] = inputs.normal((w.B, w.H, w.N, w.d), w.seed, inputs.TENSOR_IDS["dO"],
+                                    w.torch_dtype)
+        self.t = t
+        q, k, v, dO = (t[x].to(dev) for x in ("q", "k", "v", "dO"))
+        B, H, N, d = w.B, w.H, w.N, w.d
+        code = attn.ATTN_BF16 if w.dtype == "bf16" else attn.ATTN_F16
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(max(256, attn.attn_bwd_workspace_size(B, H, N, d, code)), dtype=torch.uint8,
+                         device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        sp = self.stream.cuda_stream
+        causal = int(w.causal)
+        scale = self.scale
+        nb = ws.numel()
+        self.o, self.lse = o, lse
+        self.bufs = (q, k, v, dO, o, lse, dq, dk, dv, ws)
+
+        def fwd():
+            st = attn.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, scale, causal, code, code, sp)
+            if st:
+                raise attn.AttnError(st, "attn_fwd")
+
+        def bwd_dq():
+            st = attn.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  dO.data_ptr(), lse.data_ptr(), dq.data_ptr(), ws.data_ptr(),
+                                  nb, B, H, N, d, scale, causal, code, code, sp)
+            if st:
+                raise attn.AttnError(st, "attn_bwd_dq")
+
+        def bwd_dkdv():
+            st = attn.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(),
+                                    dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nb, B, H, N,
+                                    d, scale, causal, code, code, sp)
+            if st:
+                raise attn.AttnError(st, "attn_bwd_dkdv")
+
+        self.drop = drop = None if dropout is None else (dropout,) + DROP_STATE
+
+        def fwd_drop():
+            st = attn.attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr(), B, H, N, d, scale, causal, drop[0], drop[1],
+                                       drop[2], code, code, sp)
+            if st:
+                raise attn.AttnError(st, "attn_fwd_dropout")
+
+        def bwd_drop():
+            st = attn.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       dO.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), ws.data_ptr(), nb, B, H, N, d, scale,
+                                       causal, drop[0], drop[1], drop[2], code, code, sp)
+            if st:
+                raise attn.AttnError(st, "attn_bwd_dropout")
+
+        half = 0.5 if w.causal else 1.0
+        unit = B * H * N * N * d * half
+        self.f_fwd = 4.0 * unit
+        self.f_bwd = 2.5 * self.f_fwd                 # credited: five N^2 d products
+        self.algo = {"fwd_kernel": 4.0 * unit, "dq_kernel": 6.0 * unit, "dkdv_kernel": 8.0 * unit,
+                     "bwd_kernels": 14.0 * unit}
+        if drop is None:
+            self.calls = {"step": [("fwd_kernel", fwd), ("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)],
+                          "fwd": [("fwd_kernel", fwd)],
+                          "bwd": [("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)]}
+        else:
+            self.calls = {"step": [("fwd_kernel", fwd_drop), ("bwd_kernels", bwd_drop)],
+                          "fwd": [("fwd_kernel", fwd_drop)],
+                          "bwd": [("bwd_kernels", bwd_drop)]}
+        self.fwd = fwd_drop if drop is not None else fwd
+
+    def time(self, phase, steps, warmup):
+        """Warm up, then time `steps` passes of the phase's launches, an event
+        after every call on the launch stream.  Returns (wall ms per step,
+        kernels, phases, credited FLOPs per step)."""
+        calls = self.calls[phase]
+        if phase == "bwd":
+            self.fwd()
+        for _ in range(warmup):
+            for _, fn in calls:
+                fn()
+        torch.cuda.synchronize()
+        nc = len(calls)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nc + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for st_ in range(steps):
+            ev[st_][0].record(self.stream)
+            for j_, (_, fn) in enumerate(calls):
+                fn()
+                ev[st_][j_ + 1].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per = np.array([[ev[s_][j_].elapsed_time(ev[s_][j_ + 1]) for j_ in range(nc)]
+                        for s_ in range(steps)])  # ms
+        algo = self.algo
+        kernels = {}
+        for j_, (nm, _) in enumerate(calls):
+            m = float(per[:, j_].mean())
+            kernels[nm] = {"ms_mean": m, "ms_min": float(per[:, j_].min()),
+                           "algorithmic_tflop": algo[nm] / 1e12,
+                           "tflops": algo[nm] / (m * 1e-3) / 1e12,
+                           "frac_of_peak": algo[nm] / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        phases = {}
+        if "fwd_kernel" in kernels:
+            m = kernels["fwd_kernel"]["ms_mean"]
+            phases["fwd"] = {"ms_mean": m, "tflops": self.f_fwd / (m * 1e-3) / 1e12,
+                             "frac_of_peak": self.f_fwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        if "dq_kernel" in kernels or "bwd_kernels" in kernels:
+            m = (kernels["bwd_kernels"]["ms_mean"] if "bwd_kernels" in kernels
+                 else kernels["dq_kernel"]["ms_mean"] + kernels["dkdv_kernel"]["ms_mean"])
+            phases["bwd"] = {"ms_mean": m, "tflops": self.f_bwd / (m * 1e-3) / 1e12,
+                             "frac_of_peak": self.f_bwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                             "flops": "credited 2.5x forward"}
+        flops_step = {"step": self.f_fwd + self.f_bwd, "fwd": self.f_fwd, "bwd": self.f_bwd}[phase]
+        return wall * 1e3 / steps, kernels, phases, flops_step
+
+
+def algorithmic_bytes(w):
+    """HBM bytes each kernel must move at least (inputs read once, outputs
+    written once), split into reads and writes."""
+    e = 2
+    BH, N, d = w.B * w.H, w.N, w.d
+    t = BH * N * d * e
+    r = BH * N * 4
+    return {"fwd_kernel": {"read": 3 * t, "write": t + r},
+            "dq_kernel": {"read": 5 * t + r, "write": t + 2 * r},
+            "dkdv_kernel": {"read": 4 * t + 2 * r, "write": 2 * t}}
+
+
+def _counter_rows(dirs):
+    rows = []
+    for d in dirs:
+        rows += _pmc_rows(d)
+    return rows
+
+
+SIMDS = 256 * 4   # MI355X: 256 compute units of four SIMDs
+
+
+def _num_xcc(dirs):
+    """XCDs of the profiled GPU (rocprofv3's agent info), default 8."""
+    import csv
+    import glob
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Agent_Type") == "GPU" and r.get("Num_Xcc"):
+                    return int(r["Num_Xcc"])
+    return 8
+
+
+def write_counters(dirs, workload):
+    """profiles/counters.json from rocprofv3 --pmc output dirs (any counter
+    set per dir): per kernel, every counter averaged over its dispatches
+    (each value summed over the GPU's blocks), plus derived figures:
+      - the dispatch's duration and the shader clock GRBM_GUI_ACTIVE implies
+        (it counts on every XCD, so it is divided by their number);
+      - the matrix pipes' busy fraction: busy cycles summed over SIMDs over
+        (active cycles per XCD x SIMDs), rocprofv3's MfmaUtil;
+      - the products' FLOPs by the MOPS counters (x 512), their rate, and
+        that rate against 2.5 PFLOP/s and against the peak at the clock the
+        dispatch ran at (1024 FLOP per clock per SIMD);
+      - LDS and other vector instructions per product."""
+    xcc = _num_xcc(dirs)
+    per, dur = {}, {}
+    for r in _counter_rows(dirs):
+        name = r["Kernel_Name"]
+        key = next((k for k in KERNELS if k in name), None)
+        if key is None:
+            continue
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        dur.setdefault(key, {})[(d_id := (r.get("Dispatch_Id"), r.get("Start_Timestamp")))] = (
+            float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    res = {}
+    for k, cs in per.items():
+        e = {c: sum(v) / len(v) for c, v in cs.items()}
+        e["dispatches"] = max(len(v) for v in cs.values())
+        ns = sorted(dur[k].values())
+        e["duration_ns_median"] = ns[len(ns) // 2]
+        g = e.get("GRBM_GUI_ACTIVE")
+        if g:
+            e["num_xcc"] = xcc
+            e["active_cycles_per_xcd"] = g / xcc
+            e["clock_ghz"] = g / xcc / e["duration_ns_median"]
+        if g and "SQ_VALU_MFMA_BUSY_CYCLES" in e:
+            e["mfma_busy_frac"] = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (g / xcc * SIMDS)
+        mops = e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + e.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        if mops:
+            f = mops * 512.0
+            e["mfma_flop_by_mops"] = f
+            e["mfma_tflops_by_mops"] = f / (e["duration_ns_median"] * 1e-9) / 1e12
+            e["mfma_frac_of_2500_tflops"] = e["mfma_tflops_by_mops"] / PEAK_BF16_TFLOPS
+            if "clock_ghz" in e:
+                e["mfma_frac_of_clock_peak"] = (e["mfma_tflops_by_mops"] * 1e12
+                                                / (e["clock_ghz"] * 1e9 * SIMDS * 1024.0))
+        nmf = e.get("SQ_INSTS_VALU_MFMA_BF16", 0.0) + e.get("SQ_INSTS_VALU_MFMA_F16", 0.0)
+        if nmf and "SQ_INSTS_LDS" in e:
+            e["lds_insts_per_mfma"] = e["SQ_INSTS_LDS"] / nmf
+        if nmf and "SQ_INSTS_VALU" in e:
+            e["valu_insts_per_mfma"] = (e["SQ_INSTS_VALU"] - nmf) / nmf
+        e["source_hash"] = source_hash(_family(k))
+        res[k] = e
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec.setdefault(workload, {}).update(res)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec[workload], indent=1))
+
+
+def _committed(name, workload, kernel):
+    """A kernel's entry of profiles/<name>.json if taken with the current
+    sources and flags, else None."""
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        entry = json.load(open(path)).get(workload, {}).get(kernel)
+    except (ValueError, OSError):
+        return None
+    if entry and entry.get("source_hash") == source_hash(_family(kernel)):
+        return entry
+    return None
+
+
+def attach_counters(w, kernels):
+    """Per kernel: HBM bytes from the committed FETCH/WRITE counters against
+    the algorithmic bytes (and the GB/s they mean at the live launch time),
+    whether any N x N traffic reached HBM, and the matrix pipes' counter
+    utilisation.  Entries taken with other sources or flags are left out."""
+    alg = algorithmic_bytes(w)
+    n2 = w.B * w.H * w.N * w.N * 2 * (0.5 if w.causal else 1.0)   # one S (or P) in 16 bits
+    for k, kern in kernels.items():
+        tr = _committed("traffic.json", w.name, k)
+        if tr and k in alg:
+            rd, wr = tr.get("fetch_size_bytes", 0.0), tr.get("write_size_bytes", 0.0)
+            a = alg[k]
+            kern["hbm"] = {
+                "read_bytes": rd, "write_bytes": wr,
+                "algorithmic_read_bytes": a["read"], "algorithmic_write_bytes": a["write"],
+                "read_ratio": rd / a["read"], "write_ratio": wr / a["write"],
+                "gbs": (rd + wr) / (kern["ms_mean"] * 1e-3) / 1e9,
+                "frac_of_hbm_peak": (rd + wr) / (kern["ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "n2_matrix_bytes": n2,
+                # writes within 10% of the outputs, and reads far below one
+                # N x N matrix: nothing of size N x N reaches HBM
+                "no_n2_traffic": bool(wr <= 1.1 * a["write"] and rd < 0.5 * n2),
+            }
+        c = _committed("counters.json", w.name, k)
+        if c:
+            kern["counters"] = {x: c[x] for x in ("mfma_busy_frac", "mfma_flop_by_mops",
+                                                  "mfma_frac_of_clock_peak", "clock_ghz",
+                                                  "lds_insts_per_mfma", "valu_insts_per_mfma",
+                                                  "SQ_LDS_BANK_CONFLICT") if x in c}
+            if "mfma_flop_by_mops" in c:
+                kern["counters"]["mfma_tflops_by_mops"] = (c["mfma_flop_by_mops"]
+                                                           / (kern["ms_mean"] * 1e-3) / 1e12)
+
+
+OTHER_WORKLOADS = ("gpt2_medium_fwd", "long_context_fwd", "recompute_bwd")
+
+
+def bench_standard(args):
+    """The materialised standard attention (attn_std_scores, attn_std_softmax,
+    attn_std_pv: S and P written to HBM in full and read back) against the
+    fused forward (attn_fwd) on the same inputs, one pass of each per step.
+    Default workload: the GPT-2-medium shape of the pages' comparison.
+    Algorithmic HBM bytes per head: the standard passes move S (fp32)
+    written and read, P (16-bit) written and read -- the explainer's 4 N^2
+    elements -- plus Q, K, V read and O, lse written; the fused forward only
+    the latter.  Their FETCH/WRITE counters go to profiles/traffic.json
+    under the workload's name with --copy-calibration and --traffic."""
+    dev = torch.device("cuda:0")
+    name = args.workload if args.workload != "llama7b_layer_fwd" else "gpt2_medium_fwd"
+    w = inputs.WORKLOADS[name]
+    t = inputs.make_inputs(w)
+    q, k, v = (t[x].to(dev) for x in ("q", "k", "v"))
+    B, H, N, d = w.B, w.H, w.N, w.d
+    BH = B * H
+    code = attn.ATTN_BF16 if w.dtype == "bf16" else attn.ATTN_F16
+    scale = 1.0 / math.sqrt(d)
+    causal = int(w.causal)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    o2 = torch.empty_like(q)
+    lse2 = torch.empty_like(lse)
+    need = attn.attn_std_workspace_size(B, H, N, d, code)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    sbytes = (BH * N * N * 4 + 255) // 256 * 256
+    sp_ = ws.data_ptr()
+    pp_ = sp_ + sbytes
+    stream = torch.cuda.current_stream(dev)
+    st_ = stream.cuda_stream
+
+    def ck(st, nm):
+        if st:
+            raise attn.AttnError(st, nm)
+
+    calls = [
+        ("std_scores_kernel", lambda: ck(attn.attn_std_scores(q.data_ptr(), k.data_ptr(), sp_, B, H, N, d,
+                                                              scale, code, st_), "attn_std_scores")),
+        ("std_softmax_kernel", lambda: ck(attn.attn_std_softmax(sp_, pp_, lse2.data_ptr(), B, H, N, causal,
+                                                                code, st_), "attn_std_softmax")),
+        ("std_pv_kernel", lambda: ck(attn.attn_std_pv(pp_, v.data_ptr(), o2.data_ptr(), B, H, N, d, code,
+                                                      code, st_), "attn_std_pv")),
+        ("fwd_kernel", lambda: ck(attn.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                lse.data_ptr(), B, H, N, d, scale, causal, code, code,
+                                                st_), "attn_fwd")),
+    ]
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    nc = len(calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nc + 1)] for _ in range(args.steps)]
+    for st in range(args.steps):
+        ev[st][0].record(stream)
+        for j, (_, fn) in enumerate(calls):
+            fn()
+            ev[st][j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[ev[s_][j].elapsed_time(ev[s_][j + 1]) for j in range(nc)]
+                    for s_ in range(args.steps)])
+    e = 2
+    io = BH * N * d * e
+    alg = {"std_scores_kernel": {"read": 2 * io, "write": BH * N * N * 4},
+           "std_softmax_kernel": {"read": BH * N * N * 4, "write": BH * N * N * e + BH * N * 4},
+           "std_pv_kernel": {"read": BH * N * N * e + io, "write": io},
+           "fwd_kernel": {"read": 3 * io, "write": io + BH * N * 4}}
+    kern = {}
+    for j, (nm, _) in enumerate(calls):
+        m = float(per[:, j].mean())
+        b = alg[nm]["read"] + alg[nm]["write"]
+        kern[nm] = {"ms_mean": m, "ms_min": float(per[:, j].min()),
+                    "algorithmic_read_bytes": alg[nm]["read"], "algorithmic_write_bytes": alg[nm]["write"],
+                    "algorithmic_gbs": b / (m * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": b / (m * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        tr = _committed("traffic.json", w.name, nm)
+        if tr:
+            kern[nm]["counter_read_bytes"] = tr.get("fetch_size_bytes")
+            kern[nm]["counter_write_bytes"] = tr.get("write_size_bytes")
+    std_ms = sum(kern[n]["ms_mean"] for n in ("std_scores_kernel", "std_softmax_kernel", "std_pv_kernel"))
+    fused_ms = kern["fwd_kernel"]["ms_mean"]
+    std_bytes = sum(alg[n]["read"] + alg[n]["write"] for n in ("std_scores_kernel", "std_softmax_kernel",
+                                                                 "std_pv_kernel"))
+    fused_bytes = alg["fwd_kernel"]["read"] + alg["fwd_kernel"]["write"]
+    flops = 4.0 * BH * N * N * d * (0.5 if w.causal else 1.0)
+    out = {
+        "metric": "materialised standard attention vs fused forward: ms and HBM bytes at 1 GPU",
+        "value": std_ms / fused_ms, "unit": "x (standard time / fused time)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}; standard = attn_std_scores + "
+                               f"attn_std_softmax + attn_std_pv (S fp32, P {w.dtype} in HBM); "
+                               f"fused = attn_fwd"},
+        "standard_ms": std_ms, "fused_ms": fused_ms,
+        "standard_algorithmic_bytes": std_bytes, "fused_algorithmic_bytes": fused_bytes,
+        "byte_ratio": std_bytes / fused_bytes,
+        "standard_tflops": flops / (std_ms * 1e-3) / 1e12, "fused_tflops": flops / (fused_ms * 1e-3) / 1e12,
+        "elements_per_head_standard": 4 * N * N + 4 * N * d, "elements_per_head_fused": 4 * N * d,
+        "roofline": {"bound": "hbm", "kernel": "std_softmax_kernel",
+                     "achieved": kern["std_softmax_kernel"]["algorithmic_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kern["std_softmax_kernel"]["frac_of_hbm_peak"],
+                     "traffic": None},
+        "kernels": kern,
+    }
+    tr = _committed("traffic.json", w.name, "std_softmax_kernel")
+    if tr:
+        out["roofline"]["traffic"] = tr.get("bytes")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -366,93 +790,25 @@ def main():
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.workload)
         return
+    if args.counters:
+        write_counters(args.counters, args.workload)
+        return
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
     if args.decode is not None or args.fp8:
-        if not torch.cuda.is_available():
-            print("no GPU visible", file=sys.stderr)
-            sys.exit(1)
         if args.decode is None:
             bench_fp8(args)
         else:
             bench_decode(args)
         return
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
+    if args.standard:
+        bench_standard(args)
+        return
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
-    scale = 1.0 / math.sqrt(w.d)
-    scale32 = float(np.float32(scale))
-    t = inputs.make_inputs(w)
-    if "dO" not in t:
-        t["dO"] = inputs.normal((w.B, w.H, w.N, w.d), w.seed, inputs.TENSOR_IDS["dO"], w.torch_dtype)
-    q, k, v, dO = (t[x].to(dev) for x in ("q", "k", "v", "dO"))
-    B, H, N, d = w.B, w.H, w.N, w.d
-    code = attn.ATTN_BF16 if w.dtype == "bf16" else attn.ATTN_F16
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(max(256, attn.attn_bwd_workspace_size(B, H, N, d, code)), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    causal = int(w.causal)
-
-    nbytes_ws = ws.numel()
-
-    def fwd():
-        st = attn.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                           B, H, N, d, scale, causal, code, code, sp)
-        if st:
-            raise attn.AttnError(st, "attn_fwd")
-
-    def bwd_dq():
-        st = attn.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              dO.data_ptr(), lse.data_ptr(), dq.data_ptr(), ws.data_ptr(),
-                              nbytes_ws, B, H, N, d, scale, causal, code, code, sp)
-        if st:
-            raise attn.AttnError(st, "attn_bwd_dq")
-
-    def bwd_dkdv():
-        st = attn.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(),
-                                dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), nbytes_ws, B, H, N,
-                                d, scale, causal, code, code, sp)
-        if st:
-            raise attn.AttnError(st, "attn_bwd_dkdv")
-
-    drop = None if args.dropout is None else (args.dropout,) + DROP_STATE
-
-    def fwd_drop():
-        st = attn.attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                   lse.data_ptr(), B, H, N, d, scale, causal, drop[0], drop[1],
-                                   drop[2], code, code, sp)
-        if st:
-            raise attn.AttnError(st, "attn_fwd_dropout")
-
-    def bwd_drop():
-        st = attn.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                   dO.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                   dv.data_ptr(), ws.data_ptr(), nbytes_ws, B, H, N, d, scale,
-                                   causal, drop[0], drop[1], drop[2], code, code, sp)
-        if st:
-            raise attn.AttnError(st, "attn_bwd_dropout")
-
-    half = 0.5 if w.causal else 1.0
-    unit = B * H * N * N * d * half
-    f_fwd = 4.0 * unit
-    f_bwd = 2.5 * f_fwd                      # credited: five N^2 d products
-    algo = {"fwd_kernel": 4.0 * unit, "dq_kernel": 6.0 * unit, "dkdv_kernel": 8.0 * unit,
-            "bwd_kernels": 14.0 * unit}
-    if drop is None:
-        calls = {"step": [("fwd_kernel", fwd), ("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)],
-                 "fwd": [("fwd_kernel", fwd)],
-                 "bwd": [("dq_kernel", bwd_dq), ("dkdv_kernel", bwd_dkdv)]}[args.phase]
-    else:
-        fwd = fwd_drop
-        calls = {"step": [("fwd_kernel", fwd), ("bwd_kernels", bwd_drop)],
-                 "fwd": [("fwd_kernel", fwd)],
-                 "bwd": [("bwd_kernels", bwd_drop)]}[args.phase]
-    if args.phase == "bwd":
-        fwd()
-    flops_step = {"step": f_fwd + f_bwd, "fwd": f_fwd, "bwd": f_bwd}[args.phase]
+    run = StepRunner(w, dev, dropout=args.dropout)
+    drop = run.drop
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -462,63 +818,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        for _, fn in calls:
-            fn()
-    torch.cuda.synchronize()
-
-    # timed region: an event after every call, all on the launch stream
-    nc = len(calls)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nc + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for st_ in range(args.steps):
-        ev[st_][0].record(stream)
-        for j_, (_, fn) in enumerate(calls):
-            fn()
-            ev[st_][j_ + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per = np.array([[ev[s_][j_].elapsed_time(ev[s_][j_ + 1]) for j_ in range(nc)]
-                    for s_ in range(args.steps)])  # ms
-    ms_step = wall * 1e3 / args.steps
+    ms_step, kernels, phases, flops_step = run.time(args.phase, args.steps, args.warmup)
     value = flops_step / (ms_step * 1e-3) / 1e12
-
-    kernels = {}
-    for j_, (nm, _) in enumerate(calls):
-        m = float(per[:, j_].mean())
-        kernels[nm] = {"ms_mean": m, "ms_min": float(per[:, j_].min()),
-                       "algorithmic_tflop": algo[nm] / 1e12,
-                       "tflops": algo[nm] / (m * 1e-3) / 1e12,
-                       "frac_of_peak": algo[nm] / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    phases = {}
-    if "fwd_kernel" in kernels:
-        m = kernels["fwd_kernel"]["ms_mean"]
-        phases["fwd"] = {"ms_mean": m, "tflops": f_fwd / (m * 1e-3) / 1e12,
-                         "frac_of_peak": f_fwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    if "dq_kernel" in kernels or "bwd_kernels" in kernels:
-        m = (kernels["bwd_kernels"]["ms_mean"] if "bwd_kernels" in kernels
-             else kernels["dq_kernel"]["ms_mean"] + kernels["dkdv_kernel"]["ms_mean"])
-        phases["bwd"] = {"ms_mean": m, "tflops": f_bwd / (m * 1e-3) / 1e12,
-                         "frac_of_peak": f_bwd / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         "flops": "credited 2.5x forward"}
+    if drop is None:
+        attach_counters(w, kernels)
 
     # roofline of the dominant kernel (longest mean launch)
     dom = max(kernels, key=lambda k_: kernels[k_]["ms_mean"])
-    traffic = None
-    tp = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tp) and drop is None:   # counters were taken on the plain kernels
-        try:
-            entry = json.load(open(tp)).get(w.name, {}).get(dom)
-            if entry and entry.get("source_hash") == source_hash():
-                traffic = entry.get("bytes")
-        except (ValueError, OSError):
-            traffic = None
+    traffic = kernels[dom].get("hbm", {})
+    traffic = traffic.get("read_bytes", 0.0) + traffic.get("write_bytes", 0.0) if traffic else None
     achieved = kernels[dom]["tflops"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "flops_per_launch": algo[dom], "launch_ms": kernels[dom]["ms_mean"]}
-    names = [nm for nm, _ in calls]
+                "flops_per_launch": run.algo[dom], "launch_ms": kernels[dom]["ms_mean"]}
+    names = [nm for nm, _ in run.calls[args.phase]]
+    B, H, N, d = w.B, w.H, w.N, w.d
 
     out = {
         "metric": "attention fwd/bwd TFLOP/s at 1 GPU + % of bf16 MFMA peak",
@@ -535,10 +849,31 @@ def main():
         "roofline": roofline,
         "kernel_source_hash": source_hash(),
     }
+    o, lse = run.o, run.lse
     if not args.no_cpu_baseline and drop is None:
         torch.cuda.synchronize()
-        out["cpu_baseline"] = cpu_baseline(w, t, scale32, args.cpu_seconds,
+        out["cpu_baseline"] = cpu_baseline(w, run.t, float(np.float32(run.scale)), args.cpu_seconds,
                                            gpu_out=None if args.no_parity else (o, lse))
+    if not args.no_other_workloads and drop is None and args.phase == "step":
+        # the other workloads' forward alone and whole step, for context (not the headline)
+        del run
+        others = {}
+        for name in OTHER_WORKLOADS:
+            if name == w.name:
+                continue
+            wo = inputs.WORKLOADS[name]
+            r = StepRunner(wo, dev)
+            fms, fk, fph, ff = r.time("fwd", args.other_steps, 3)
+            sms, sk, sph, sf = r.time("step", args.other_steps, 3)
+            attach_counters(wo, sk)
+            others[name] = {"workload": wo.describe(), "steps": args.other_steps, "warmup": 3,
+                            "fwd_alone_ms": fms, "fwd_alone_tflops": ff / (fms * 1e-3) / 1e12,
+                            "step_ms": sms, "step_tflops": sf / (sms * 1e-3) / 1e12,
+                            "step_frac_of_peak": sf / (sms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                            "phases_in_step": sph, "kernels_in_step": sk}
+            del r
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 

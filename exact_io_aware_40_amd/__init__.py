@@ -9,10 +9,13 @@ Low level (same names and argument order as the C ABI, raw integers and
 device pointers):  :func:`attn_fwd`, :func:`attn_fwd_split`,
 :func:`attn_fwd_split_workspace_size`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
 :func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`, :func:`attn_fwd_fp8`,
-:func:`attn_fwd_decode_fp8`, :func:`attn_status_str`.
+:func:`attn_fwd_decode_fp8`, :func:`attn_std_fwd`, :func:`attn_std_scores`,
+:func:`attn_std_softmax`, :func:`attn_std_pv`, :func:`attn_std_workspace_size`,
+:func:`attn_status_str`.
 
 Tensor level:  :func:`forward`, :func:`forward_split`, :func:`forward_decode`,
-:func:`forward_fp8`, :func:`forward_decode_fp8` and :func:`backward`.
+:func:`forward_fp8`, :func:`forward_decode_fp8` and :func:`backward`;
+:func:`forward_standard` is the materialised (unfused) baseline.
 """
 from __future__ import annotations
 
@@ -27,6 +30,8 @@ __all__ = [
     "attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_size",
     "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
     "attn_fwd_fp8", "attn_fwd_decode_fp8", "attn_status_str",
+    "attn_std_fwd", "attn_std_scores", "attn_std_softmax", "attn_std_pv", "attn_std_workspace_size",
+    "forward_standard",
     "forward", "forward_split", "forward_decode", "forward_fp8", "forward_decode_fp8", "backward", "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "library_path",
 ]
 
@@ -91,6 +96,16 @@ def _load():
     lib.attn_fwd_decode_fp8.restype = i32
     lib.attn_fwd_decode_fp8.argtypes = [vp] * 6 + [sz, i64, i64, i64, i64, i64, f32, f32, f32, f32,
                                                    i32, i32, i32, vp]
+    lib.attn_std_workspace_size.restype = sz
+    lib.attn_std_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_std_fwd.restype = i32
+    lib.attn_std_fwd.argtypes = [vp] * 6 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_std_scores.restype = i32
+    lib.attn_std_scores.argtypes = [vp] * 3 + [i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_std_softmax.restype = i32
+    lib.attn_std_softmax.argtypes = [vp] * 3 + [i64, i64, i64, i32, i32, vp]
+    lib.attn_std_pv.restype = i32
+    lib.attn_std_pv.argtypes = [vp] * 3 + [i64, i64, i64, i64, i32, i32, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -179,6 +194,32 @@ def attn_fwd_decode_fp8(q: int, k: int, v: int, o: int, lse: int, workspace: int
     return _load().attn_fwd_decode_fp8(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d,
                                        scale, q_descale, k_descale, v_descale, causal, out_dtype,
                                        nsplit, stream)
+
+
+def attn_std_workspace_size(B: int, H: int, N: int, d: int, dtype: int) -> int:
+    return _load().attn_std_workspace_size(B, H, N, d, dtype)
+
+
+def attn_std_fwd(q: int, k: int, v: int, o: int, lse: int, workspace: int, workspace_bytes: int,
+                 B: int, H: int, N: int, d: int, scale: float, causal: int, dtype: int,
+                 out_dtype: int, stream: int) -> int:
+    return _load().attn_std_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                                causal, dtype, out_dtype, stream)
+
+
+def attn_std_scores(q: int, k: int, s: int, B: int, H: int, N: int, d: int, scale: float,
+                    dtype: int, stream: int) -> int:
+    return _load().attn_std_scores(q, k, s, B, H, N, d, scale, dtype, stream)
+
+
+def attn_std_softmax(s: int, p: int, lse: int, B: int, H: int, N: int, causal: int, dtype: int,
+                     stream: int) -> int:
+    return _load().attn_std_softmax(s, p, lse, B, H, N, causal, dtype, stream)
+
+
+def attn_std_pv(p: int, v: int, o: int, B: int, H: int, N: int, d: int, dtype: int,
+                out_dtype: int, stream: int) -> int:
+    return _load().attn_std_pv(p, v, o, B, H, N, d, dtype, out_dtype, stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -441,7 +482,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = (torch.empty(q.shape, dtype=od, device=q.device) for _ in range(3))
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel())
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size())
     if dropout is None:
         st = attn_bwd(*ptrs, B, H, N, d, float(scale), int(bool(causal)), code, _OUT_CODE[od],
                       _stream(q))
@@ -453,3 +495,46 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if st != 0:
         raise AttnError(st, "attn_bwd" if dropout is None else "attn_bwd_dropout")
     return dq, dk, dv
+
+
+def forward_standard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                     scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                     workspace: Optional[torch.Tensor] = None, return_sp: bool = False):
+    """The materialised standard attention (attn_std_fwd): S = scale Q K^T
+    written to device memory in full (fp32), P = softmax(S) written in full
+    (q's dtype), then O = P V.  Same result as :func:`forward` up to
+    rounding, at N x N traffic per head; it exists as the baseline the fused
+    path is measured against.  Returns (o, lse), and with return_sp also
+    (s [B, H, N, N] float32, p [B, H, N, N] q.dtype), views of the workspace
+    (a uint8 device tensor of at least attn_std_workspace_size bytes,
+    allocated when not given)."""
+    _check(q, "q")
+    _check(k, "k", q)
+    _check(v, "v", q)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"dtype must be float16 or bfloat16, got {q.dtype}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    od = _out_dtype(q, out_dtype)
+    code = _DTYPE_CODE[q.dtype]
+    o = torch.empty(q.shape, dtype=od, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = attn_std_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = attn_std_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                      B, H, N, d, float(scale), int(bool(causal)), code, _OUT_CODE[od], _stream(q))
+    if st != 0:
+        raise AttnError(st, "attn_std_fwd")
+    if not return_sp:
+        return o, lse
+    nel = B * H * N * N
+    sbytes = (nel * 4 + 255) // 256 * 256
+    raw = workspace.view(torch.uint8).reshape(-1)
+    s = raw[:nel * 4].view(torch.float32).reshape(B, H, N, N)
+    p = raw[sbytes:sbytes + nel * 2].view(q.dtype).reshape(B, H, N, N)
+    return o, lse, s, p

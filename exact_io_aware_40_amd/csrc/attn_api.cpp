@@ -468,3 +468,124 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, v
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shapes the standard (materialised) passes accept: the common checks, N at
+// most ATTN_STD_MAX_N, B * H * N * N elements addressable, and every grid
+// within 2^31 - 1 workgroups.
+int std_check(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+              int out_dtype, bool* empty) {
+    const int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, empty);
+    if (st != ATTN_OK || *empty) return st;
+    if (N > ATTN_STD_MAX_N) return ATTN_ERR_SHAPE;
+    const int64_t BH = B * H;
+    if (BH > (int64_t(1) << 62) / (N * N)) return ATTN_ERR_SHAPE;
+    const int64_t nb = (N + 127) / 128;
+    if (BH * nb * nb > 0x7fffffff || (BH * N + 3) / 4 > 0x7fffffff) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+size_t std_s_bytes(int64_t BH, int64_t N) { return (size_t(BH * N * N) * 4 + 255) & ~size_t(255); }
+
+int std_scores(const void* q, const void* k, float* s, int64_t B, int64_t H, int64_t N, int64_t d,
+               float scale, int dtype, void* stream) {
+    bool empty = false;
+    const int st = std_check(B, H, N, d, scale, 0, dtype, dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!q || !k || !s) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(s)) return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const size_t tbytes = size_t(BH * N * d) * 2;
+    const Range rs = range(s, size_t(BH * N * N) * 4);
+    if (overlap(rs, range(q, tbytes)) || overlap(rs, range(k, tbytes))) return ATTN_ERR_ALIAS;
+    const hipError_t e = attn::launch_std_scores(q, k, s, BH, int(N), int(d), scale, dtype,
+                                                 (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int std_softmax(const float* s, void* p, float* lse, int64_t B, int64_t H, int64_t N, int causal,
+                int dtype, void* stream) {
+    bool empty = false;
+    const int st = std_check(B, H, N, 64, 1.f, causal, dtype, dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!s || !p || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(s) || !aligned16(p) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const Range rs = range(s, size_t(BH * N * N) * 4), rp = range(p, size_t(BH * N * N) * 2),
+                rl = range(lse, size_t(BH * N) * 4);
+    if (overlap(rp, rs) || overlap(rl, rs) || overlap(rp, rl)) return ATTN_ERR_ALIAS;
+    const hipError_t e = attn::launch_std_softmax(s, p, lse, BH, int(N), causal, dtype,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int std_pv(const void* p, const void* v, void* o, int64_t B, int64_t H, int64_t N, int64_t d,
+           int dtype, int out_dtype, void* stream) {
+    bool empty = false;
+    const int st = std_check(B, H, N, d, 1.f, 0, dtype, out_dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!p || !v || !o) return ATTN_ERR_NULL;
+    if (!aligned16(p) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const Range ro = range(o, size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2));
+    if (overlap(ro, range(p, size_t(BH * N * N) * 2)) || overlap(ro, range(v, size_t(BH * N * d) * 2)))
+        return ATTN_ERR_ALIAS;
+    const hipError_t e = attn::launch_std_pv(p, v, o, BH, int(N), int(d), dtype, out_dtype == ATTN_F32,
+                                             (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_std_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    bool empty = false;
+    if (std_check(B, H, N, d, 1.f, 0, dtype, dtype, &empty) != ATTN_OK || empty) return 0;
+    return std_s_bytes(B * H, N) + size_t(B * H * N * N) * 2;
+}
+
+int attn_std_scores(const void* q, const void* k, float* s, int64_t B, int64_t H, int64_t N,
+                    int64_t d, float scale, int dtype, void* stream) {
+    return std_scores(q, k, s, B, H, N, d, scale, dtype, stream);
+}
+
+int attn_std_softmax(const float* s, void* p, float* lse, int64_t B, int64_t H, int64_t N,
+                     int causal, int dtype, void* stream) {
+    return std_softmax(s, p, lse, B, H, N, causal, dtype, stream);
+}
+
+int attn_std_pv(const void* p, const void* v, void* o, int64_t B, int64_t H, int64_t N, int64_t d,
+                int dtype, int out_dtype, void* stream) {
+    return std_pv(p, v, o, B, H, N, d, dtype, out_dtype, stream);
+}
+
+int attn_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 int causal, int dtype, int out_dtype, void* stream) {
+    bool empty = false;
+    int st = std_check(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_ALIGN;
+    const int64_t BH = B * H;
+    const size_t sb = std_s_bytes(BH, N), need = sb + size_t(BH * N * N) * 2;
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    const size_t tbytes = size_t(BH * N * d) * 2;
+    const size_t obytes = size_t(BH * N * d) * (out_dtype == ATTN_F32 ? 4 : 2);
+    const Range ro = range(o, obytes), rl = range(lse, size_t(BH * N) * 4), rw = range(workspace, need);
+    const Range in[3] = {range(q, tbytes), range(k, tbytes), range(v, tbytes)};
+    for (const Range& r : in)
+        if (overlap(ro, r) || overlap(rl, r) || overlap(rw, r)) return ATTN_ERR_ALIAS;
+    if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw)) return ATTN_ERR_ALIAS;
+    float* s = static_cast<float*>(workspace);
+    void* p = static_cast<char*>(workspace) + sb;
+    if ((st = std_scores(q, k, s, B, H, N, d, scale, dtype, stream)) != ATTN_OK) return st;
+    if ((st = std_softmax(s, p, lse, B, H, N, causal, dtype, stream)) != ATTN_OK) return st;
+    return std_pv(p, v, o, B, H, N, d, dtype, out_dtype, stream);
+}
+
+}  // extern "C"

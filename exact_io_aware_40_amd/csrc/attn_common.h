@@ -337,9 +337,6 @@ template <> __device__ __forceinline__ void store4<_Float16>(_Float16* p, f32x4 
 }
 template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 x) { *(f32x4*)p = x; }
 
-// Workgroup id -> logical work item, so that consecutive logical items land
-// on the same XCD.  The dispatcher hands workgroup ids to the 8 XCDs in
-// round-robin order; XCD x receives logical items [base(x), base(x)+count(x)).
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011), the generator of the dropout mask.  A round
 // maps the counter (c0, c1, c2, c3) under key (k0, k1) to
@@ -362,6 +359,9 @@ __device__ __forceinline__ bool drop_keep(unsigned word, int byte, unsigned t) {
     return ((word >> (8 * byte)) & 0xFFu) >= t;
 }
 
+// Workgroup id -> logical work item, so that consecutive logical items land
+// on the same XCD.  The dispatcher hands workgroup ids to the 8 XCDs in
+// round-robin order; XCD x receives logical items [base(x), base(x)+count(x)).
 __device__ __forceinline__ int xcd_remap(int id, int total) {
     const int per = total >> 3, rem = total & 7, x = id & 7;
     return x * per + (x < rem ? x : rem) + (id >> 3);

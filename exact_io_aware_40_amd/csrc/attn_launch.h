@@ -79,4 +79,13 @@ size_t bwd_workspace_bytes(int64_t BH, int64_t N);
 hipError_t launch_bwd(const BwdArgs& a, int which, int dtype, bool out_f32, int d, int causal,
                       hipStream_t stream);
 
+// Materialised standard attention: S = scale Q K^T (fp32, [BH][N][N]),
+// P = softmax(S) (dtype, masked entries 0) with lse, O = P V.
+hipError_t launch_std_scores(const void* q, const void* k, float* s, int64_t BH, int N, int d,
+                             float scale, int dtype, hipStream_t stream);
+hipError_t launch_std_softmax(const float* s, void* p, float* lse, int64_t BH, int N, int causal,
+                              int dtype, hipStream_t stream);
+hipError_t launch_std_pv(const void* p, const void* v, void* o, int64_t BH, int N, int d, int dtype,
+                         bool out_f32, hipStream_t stream);
+
 }  // namespace attn

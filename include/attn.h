@@ -317,6 +317,51 @@ int attn_fwd_decode_fp8(const void* q, const void* k, const void* v, void* o, fl
                         float k_descale, float v_descale, int causal, int out_dtype, int nsplit,
                         void* stream);
 
+/*
+ * Materialised standard attention -- the unfused baseline the pages measure
+ * the fused kernel against ("FlashAttention" explainer, Step 2 "Standard
+ * Attention": S = Q K^T written to HBM, read back for P = softmax(S), P
+ * written and read back for O = P V; "13% more FLOPs, 5.7x faster",
+ * introduction).  Same result as attn_fwd up to rounding, but S and P are
+ * real [B, H, N, N] arrays in device memory: 4 N^2 elements of traffic per
+ * head beside the 4 N d of Q, K, V and O.  It exists to measure that
+ * traffic; attn_fwd is the path to use.
+ *
+ * Conventions as above, plus: N <= ATTN_STD_MAX_N, and the caller provides
+ * the N x N arrays.
+ *   s : [B, H, N, N] float, s_ij = scale * q_i . k_j for every i, j (the mask
+ *       is not applied to s)
+ *   p : [B, H, N, N] of `dtype`, p_ij = exp(s_ij - m_i) / l_i over j in A(i),
+ *       0 for masked j, normalised in fp32 and rounded once to nearest even
+ *   lse : [B, H, N] float, m_i + ln(l_i), as attn_fwd writes it
+ */
+#define ATTN_STD_MAX_N 32768
+
+/* Bytes of the workspace attn_std_fwd takes: s (fp32) and then p (`dtype`),
+ * B * H * N * N * 6 (s rounded up to a multiple of 256 bytes).  0 for
+ * invalid arguments or when there is nothing to do. */
+size_t attn_std_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/* The three passes in order, with s and p in `workspace` (s at its start, p
+ * after it); o and lse as for attn_fwd.  The workspace holds s and p
+ * afterwards. */
+int attn_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                 int64_t d, float scale, int causal, int dtype, int out_dtype, void* stream);
+
+/* Pass 1: s = scale * q k^T for every (i, j), fp32, on the matrix cores. */
+int attn_std_scores(const void* q, const void* k, float* s, int64_t B, int64_t H, int64_t N,
+                    int64_t d, float scale, int dtype, void* stream);
+
+/* Pass 2: p and lse from s, row by row (the mask applied here). */
+int attn_std_softmax(const float* s, void* p, float* lse, int64_t B, int64_t H, int64_t N,
+                     int causal, int dtype, void* stream);
+
+/* Pass 3: o = p v over every key, fp32 accumulation on the matrix cores,
+ * o of `out_dtype` (`dtype` or ATTN_F32) rounded once. */
+int attn_std_pv(const void* p, const void* v, void* o, int64_t B, int64_t H, int64_t N,
+                int64_t d, int dtype, int out_dtype, void* stream);
+
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);
 

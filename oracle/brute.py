@@ -23,11 +23,17 @@ def _mask(N, causal):
     return np.tril(np.ones((N, N), dtype=bool))
 
 
+def scores(q, k, scale):
+    """The full score matrix S = scale * Q K^T, [..., N, N] fp64 (no mask)."""
+    q, k = (np.asarray(t, np.float64) for t in (q, k))
+    return scale * (q @ np.swapaxes(k, -1, -2))
+
+
 def fwd(q, k, v, scale, causal=False):
     """q, k, v: [..., N, d] fp64.  Returns (o, lse, p)."""
     q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
     N = q.shape[-2]
-    s = scale * (q @ np.swapaxes(k, -1, -2))
+    s = scores(q, k, scale)
     keep = _mask(N, causal)
     s = np.where(keep, s, -np.inf)
     m = s.max(axis=-1, keepdims=True)

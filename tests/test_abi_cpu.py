@@ -33,7 +33,9 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dropout",
                                     "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode", "attn_fwd_decode_fp8",
                                     "attn_fwd_dropout", "attn_fwd_fp8", "attn_fwd_split",
-                                    "attn_fwd_split_workspace_size", "attn_status_str"]
+                                    "attn_fwd_split_workspace_size", "attn_status_str", "attn_std_fwd",
+                                    "attn_std_pv", "attn_std_scores", "attn_std_softmax",
+                                    "attn_std_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -350,3 +352,61 @@ def test_fwd_decode_fp8_rejects(kw, code):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(Nq=0, q=0, ws=0)])
 def test_fwd_decode_fp8_empty_is_noop(kw):
     assert fwd_decode_fp8(**kw) == OK
+
+
+# ---------------------------------------------------------------------------
+# materialised standard attention (validation only)
+# ---------------------------------------------------------------------------
+
+def std_fwd(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], ws=P[5], wsb=None, B=2, H=3, N=100,
+             d=128, scale=0.1, causal=0, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    wsb = a["wsb"]
+    if wsb is None:
+        wsb = attn.attn_std_workspace_size(a["B"], a["H"], a["N"], a["d"], a["dtype"])
+    return attn.attn_std_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], wsb, a["B"], a["H"],
+                             a["N"], a["d"], a["scale"], a["causal"], a["dtype"], od, a["stream"])
+
+
+def test_std_workspace_size():
+    # s in fp32 rounded up to 256 bytes, then p in 16 bits
+    n = 2 * 3 * 100 * 100
+    assert attn.attn_std_workspace_size(2, 3, 100, 128, 1) == (n * 4 + 255) // 256 * 256 + n * 2
+    assert attn.attn_std_workspace_size(2, 3, 100, 64, 0) == (n * 4 + 255) // 256 * 256 + n * 2
+    assert attn.attn_std_workspace_size(0, 3, 100, 64, 0) == 0
+    assert attn.attn_std_workspace_size(1, 1, 40000, 64, 0) == 0      # N above ATTN_STD_MAX_N
+    assert attn.attn_std_workspace_size(1, 1, 100, 96, 0) == 0        # bad d
+    assert attn.attn_std_workspace_size(1, 1, 100, 64, 2) == 0        # fp32 is not an input type
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), E_NULL), (dict(lse=0), E_NULL), (dict(ws=0), E_WS),
+    (dict(wsb=1000), E_WS), (dict(d=96), E_HD), (dict(dtype=2), E_DT), (dict(out_dtype=0), E_DT),
+    (dict(N=40000), E_SHAPE), (dict(N=-1), E_SHAPE), (dict(causal=2), E_CAUSAL),
+    (dict(scale=float("inf")), E_SCALE), (dict(o=P[3] + 8), E_ALIGN), (dict(ws=P[5] + 8), E_ALIGN),
+    (dict(o=P[1]), E_ALIAS), (dict(ws=P[3]), E_ALIAS), (dict(lse=P[5] + 256), E_ALIAS),
+])
+def test_std_fwd_rejects(kw, code):
+    assert std_fwd(**kw) == code
+
+
+def test_std_fwd_empty_is_noop():
+    assert std_fwd(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, wsb=0) == OK
+    assert std_fwd(N=0, q=0, ws=0, wsb=0) == OK
+
+
+def test_std_passes_reject():
+    assert attn.attn_std_scores(0, P[1], P[2], 2, 3, 100, 128, 0.1, 1, 0) == E_NULL
+    assert attn.attn_std_scores(P[0], P[1], P[2] + 4, 2, 3, 100, 128, 0.1, 1, 0) == E_ALIGN
+    assert attn.attn_std_scores(P[0], P[1], P[0], 2, 3, 100, 128, 0.1, 1, 0) == E_ALIAS
+    assert attn.attn_std_scores(P[0], P[1], P[2], 2, 3, 100, 80, 0.1, 1, 0) == E_HD
+    assert attn.attn_std_softmax(P[0], 0, P[2], 2, 3, 100, 0, 1, 0) == E_NULL
+    assert attn.attn_std_softmax(P[0], P[0], P[2], 2, 3, 100, 0, 1, 0) == E_ALIAS
+    assert attn.attn_std_softmax(P[0], P[1], P[2], 2, 3, 100, 3, 1, 0) == E_CAUSAL
+    assert attn.attn_std_softmax(P[0], P[1], P[2], 2, 3, 40000, 0, 1, 0) == E_SHAPE
+    assert attn.attn_std_pv(P[0], P[1], 0, 2, 3, 100, 64, 1, 1, 0) == E_NULL
+    assert attn.attn_std_pv(P[0], P[1], P[0], 2, 3, 100, 64, 1, 1, 0) == E_ALIAS
+    assert attn.attn_std_pv(P[0], P[1], P[2], 2, 3, 100, 64, 1, 0, 0) == E_DT
+    assert attn.attn_std_pv(P[0], P[1], P[2], 0, 3, 100, 64, 1, 1, 0) == OK

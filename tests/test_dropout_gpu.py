@@ -17,7 +17,8 @@ import torch
 import exact_io_aware_40_amd as attn
 import oracle
 from exact_io_aware_40_amd import inputs
-from tests._util import LSE_TOL, TOL, announce, f64, randn, report, report_rounded
+from tests._util import (LSE_TOL, TOL, announce, f64, randn, report, report_rounded, rounded,
+                         stored_o_allowance)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -103,30 +104,44 @@ def gpu_fwd_bwd(q, k, v, dO, causal, scale, drop, out_dtype=None):
     o, lse = attn.forward(qd, kd, vd, causal=causal, scale=scale, out_dtype=out_dtype, dropout=drop)
     dq, dk, dv = attn.backward(qd, kd, vd, o, lse, gd, causal=causal, scale=scale, dropout=drop)
     torch.cuda.synchronize()
-    return dq, dk, dv, o
+    return dq, dk, dv
 
 
 def bwd_compare(q, k, v, dO, causal, scale, drop, tag, heads=None):
-    """fp32 gradients against the definition; 16-bit gradients against the
-    oracle given the stored o (the backward's contract), within the tolerance
-    plus half an ulp.  heads: restrict the oracle to the first `heads` heads
-    of batch 0 (their head index, which the mask depends on, is unchanged)."""
+    """fp32 gradients against the definition; 16-bit gradients (a) from the
+    oracle's own o rounded to the input type and its lse, against the oracle
+    given that o (the backward's contract), within the tolerance plus half an
+    ulp, and (b) through the whole 16-bit pipeline against the plain
+    definition, with the allowance for the rounded o derived from oracle
+    quantities.  heads: restrict the oracle to the first `heads` heads of
+    batch 0 (their head index, which the mask depends on, is unchanged).  No
+    GPU output is passed to the oracle."""
     announce(f"dropout bwd {tag} shape={tuple(q.shape)} {q.dtype} causal={causal} drop={drop}")
-    H, N, d = q.shape[1], q.shape[2], q.shape[3]
-    sel = (lambda x: f64(x)) if heads is None else (lambda x: f64(x[0, :heads]))
-    tol = TOL[q.dtype]
-    _, _, rq, rk, rv = oracle.bwd(sel(q), sel(k), sel(v), sel(dO), s32(scale), causal, dropout=drop)
-    dq, dk, dv, _ = gpu_fwd_bwd(q, k, v, dO, causal, scale, drop, out_dtype=torch.float32)
+    part = (lambda x: x) if heads is None else (lambda x: x[:1, :heads].contiguous())
+    sel = lambda x: f64(part(x))  # noqa: E731
+    tol, dt = TOL[q.dtype], q.dtype
+    Q, K, V, G = (sel(x) for x in (q, k, v, dO))
+    o_ref, lse_ref, rq, rk, rv = oracle.bwd(Q, K, V, G, s32(scale), causal, dropout=drop)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, dO, causal, scale, drop, out_dtype=torch.float32)
     report(f"{tag} dq(fp32 out)", sel(dq), rq, tol)
     report(f"{tag} dk(fp32 out)", sel(dk), rk, tol)
     report(f"{tag} dv(fp32 out)", sel(dv), rv, tol)
     del dq, dk, dv
-    hq, hk, hv, ho = gpu_fwd_bwd(q, k, v, dO, causal, scale, drop)
-    _, _, sq, sk, sv = oracle.bwd(sel(q), sel(k), sel(v), sel(dO), s32(scale), causal, o_in=sel(ho),
-                                  dropout=drop)
-    report_rounded(f"{tag} dq", sel(hq), sq, tol, q.dtype)
-    report_rounded(f"{tag} dk", sel(hk), sk, tol, q.dtype)
-    report_rounded(f"{tag} dv", sel(hv), sv, tol, q.dtype)
+    o_st = rounded(o_ref, dt)
+    lse_st = torch.from_numpy(lse_ref).float()
+    dev = [x.to(DEV) for x in (part(q), part(k), part(v), o_st, lse_st, part(dO))]
+    hq, hk, hv = attn.backward(*dev, causal=causal, scale=scale, dropout=drop)
+    torch.cuda.synchronize()
+    _, _, sq, sk, sv = oracle.bwd(Q, K, V, G, s32(scale), causal, o_in=f64(o_st), dropout=drop)
+    report_rounded(f"{tag} dq(stored o)", f64(hq), sq, tol, dt)
+    report_rounded(f"{tag} dk(stored o)", f64(hk), sk, tol, dt)
+    report_rounded(f"{tag} dv(stored o)", f64(hv), sv, tol, dt)
+    del hq, hk, hv, dev
+    hq, hk, hv = gpu_fwd_bwd(q, k, v, dO, causal, scale, drop)
+    aq, ak = stored_o_allowance(Q, K, G, o_ref, lse_ref, s32(scale), causal, dt)
+    report_rounded(f"{tag} dq(pipeline)", sel(hq), rq, tol, dt, extra=aq)
+    report_rounded(f"{tag} dk(pipeline)", sel(hk), rk, tol, dt, extra=ak)
+    report_rounded(f"{tag} dv(pipeline)", sel(hv), rv, tol, dt)
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])

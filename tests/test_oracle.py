@@ -293,6 +293,32 @@ def test_backward_with_stored_output(causal):
     np.testing.assert_allclose(dq3 - dq, -0.5 * dD[..., None] * (p @ k), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_stored_o_allowance(causal, dtype):
+    """The GPU tests' allowance for a backward fed a 16-bit o: the oracle's
+    gradients from o rounded to the type, and from o moved by a whole ulp
+    against the sign of dO (the largest change of D the bound admits), stay
+    within it; the second reaches it (the bound is tight, not vacuous)."""
+    from tests._util import stored_o_allowance, ulp
+    shape = (2, 3, 40, 16)
+    q, k, v, dO = (rand(shape, s) for s in (70, 71, 72, 73))
+    o, lse, dq, dk, dv = oracle.bwd(q, k, v, dO, 0.3, causal)
+    aq, ak = stored_o_allowance(q, k, dO, o, lse, 0.3, causal, dtype)
+    o16 = torch.from_numpy(o).to(dtype).double().numpy()
+    worst = o - ulp(o, dtype) * np.sign(dO)
+    for o_in, tight in ((o16, False), (worst, True)):
+        _, _, dq2, dk2, dv2 = oracle.bwd(q, k, v, dO, 0.3, causal, o_in=o_in)
+        np.testing.assert_array_equal(dv2, dv)
+        assert np.all(np.abs(dq2 - dq) <= aq * (1 + 1e-9) + 1e-15)
+        assert np.all(np.abs(dk2 - dk) <= ak * (1 + 1e-9) + 1e-15)
+        if tight:
+            # dq_i's change is -scale e_i sum_j P_ij k_j: the bound uses |k|
+            # inside the sum, so it is reached where one key dominates; the
+            # sum over heads and rows reaches a fair fraction of it
+            assert (np.abs(dq2 - dq).sum() / aq.sum()) > 0.2
+
+
 def test_backward_single_key():
     """N = 1: P = 1 so dq = dk = 0 and dv = dO."""
     q, k, v, dO = (rand((3, 1, 8), s) for s in (44, 45, 46, 47))
