@@ -7,7 +7,8 @@ memory and the current stream.
 
 Low level (same names and argument order as the C ABI, raw integers and
 device pointers):  :func:`attn_fwd`, :func:`attn_fwd_split`,
-:func:`attn_fwd_split_workspace_size`, :func:`attn_bwd`, :func:`attn_bwd_dq`,
+:func:`attn_fwd_split_workspace_size`, :func:`attn_bwd`, :func:`attn_bwd_noalloc`,
+:func:`attn_bwd_dq`,
 :func:`attn_bwd_dkdv`, :func:`attn_bwd_workspace_size`, :func:`attn_fwd_fp8`,
 :func:`attn_fwd_decode_fp8`, :func:`attn_std_fwd`, :func:`attn_std_scores`,
 :func:`attn_std_softmax`, :func:`attn_std_pv`, :func:`attn_std_workspace_size`,
@@ -28,7 +29,7 @@ import torch
 
 __all__ = [
     "attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_size",
-    "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
+    "attn_bwd", "attn_bwd_noalloc", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_workspace_size",
     "attn_fwd_fp8", "attn_fwd_decode_fp8", "attn_status_str",
     "attn_std_fwd", "attn_std_scores", "attn_std_softmax", "attn_std_pv", "attn_std_workspace_size",
     "forward_standard",
@@ -81,6 +82,8 @@ def _load():
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_bwd.restype = i32
     lib.attn_bwd.argtypes = [vp] * 10 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_bwd_noalloc.restype = i32
+    lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.attn_bwd_dq.restype = i32
     lib.attn_bwd_dq.argtypes = [vp] * 8 + [sz, i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.attn_bwd_dkdv.restype = i32
@@ -148,6 +151,13 @@ def attn_bwd(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, dk: int
              scale: float, causal: int, dtype: int, out_dtype: int, stream: int) -> int:
     return _load().attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes,
                             B, H, N, d, scale, causal, dtype, out_dtype, stream)
+
+
+def attn_bwd_noalloc(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, dk: int, dv: int,
+                     B: int, H: int, N: int, d: int, scale: float, causal: int, dtype: int,
+                     out_dtype: int, stream: int) -> int:
+    return _load().attn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                                    dtype, out_dtype, stream)
 
 
 def attn_bwd_dq(q: int, k: int, v: int, o: int, dO: int, lse: int, dq: int, workspace: int,

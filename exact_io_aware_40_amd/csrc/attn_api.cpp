@@ -352,12 +352,16 @@ size_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int d
 namespace {
 
 // Shared by attn_bwd (which = 3), attn_bwd_dq (1) and attn_bwd_dkdv (2).
+// check_only: validate everything but the workspace and return (nothing is
+// launched); *empty is then set when there is nothing to compute.
 int bwd_common(int which, const void* q, const void* k, const void* v, const void* o,
                const void* dO, const float* lse, void* dq, void* dk, void* dv, const void* ws,
                size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-               int causal, int dtype, int out_dtype, const attn::DropArgs& drop, void* stream) {
+               int causal, int dtype, int out_dtype, const attn::DropArgs& drop, void* stream,
+               bool check_only = false, bool* empty_out = nullptr) {
     bool empty = false;
     int st = check_common(B, H, N, d, scale, causal, dtype, out_dtype, &empty);
+    if (empty_out) *empty_out = empty;
     if (st != ATTN_OK || empty) return st;
     const bool want_dq = which & 1, want_dkdv = which & 2;
     if (!q || !k || !v || !dO) return ATTN_ERR_NULL;
@@ -369,8 +373,12 @@ int bwd_common(int which, const void* q, const void* k, const void* v, const voi
         if (!aligned16(p)) return ATTN_ERR_ALIGN;
     const int64_t BH = B * H;
     const size_t need = attn::bwd_workspace_bytes(BH, N);
-    if (!ws || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    if (!aligned16(ws)) return ATTN_ERR_ALIGN;
+    if (check_only) {
+        if (need > attn::kBwdScratchBytes) return ATTN_ERR_WORKSPACE;
+    } else {
+        if (!ws || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+        if (!aligned16(ws)) return ATTN_ERR_ALIGN;
+    }
     if (BH > 0x7fffffff / ((N + 63) / 64)) return ATTN_ERR_SHAPE;
 
     // outputs may overlap neither the inputs nor each other
@@ -388,9 +396,9 @@ int bwd_common(int which, const void* q, const void* k, const void* v, const voi
         ins[ni++] = range(o, obytes);
         ins[ni++] = range(lse, size_t(BH * N) * 4);
         outs[no++] = range(dq, obytes);
-        outs[no++] = range(ws, need);           // written by the dq half
-    } else {
-        ins[ni++] = range(ws, need);            // read by the dk/dv half
+        if (!check_only) outs[no++] = range(ws, need);   // written by the dq half
+    } else if (!check_only) {
+        ins[ni++] = range(ws, need);                     // read by the dk/dv half
     }
     if (want_dkdv) {
         outs[no++] = range(dk, obytes);
@@ -402,6 +410,7 @@ int bwd_common(int which, const void* q, const void* k, const void* v, const voi
         for (int j = i + 1; j < no; ++j)
             if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
     }
+    if (check_only) return ATTN_OK;
 
     attn::BwdArgs a;
     a.q = q;
@@ -436,6 +445,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
              int causal, int dtype, int out_dtype, void* stream) {
     return bwd_common(3, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                      scale, causal, dtype, out_dtype, no_drop(), stream);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
+                     void* stream) {
+    // every argument is checked (and the workspace's size against the fixed
+    // per-GPU scratch) before the first HIP call
+    bool empty = false;
+    int st = bwd_common(3, q, k, v, o, dO, lse, dq, dk, dv, nullptr, 0, B, H, N, d, scale, causal,
+                        dtype, out_dtype, no_drop(), stream, true, &empty);
+    if (st != ATTN_OK || empty) return st;
+    void* ws = nullptr;
+    if (attn::bwd_scratch(&ws) != hipSuccess) return ATTN_ERR_LAUNCH;
+    return bwd_common(3, q, k, v, o, dO, lse, dq, dk, dv, ws, attn::kBwdScratchBytes, B, H, N, d,
                       scale, causal, dtype, out_dtype, no_drop(), stream);
 }
 

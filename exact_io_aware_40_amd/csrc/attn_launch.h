@@ -75,6 +75,10 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(int64_t BH, int64_t N);
+// The fixed per-GPU workspace of attn_bwd_noalloc: its size, and its device
+// address on the current device (looked up on the first call per device).
+constexpr size_t kBwdScratchBytes = size_t(16) << 20;
+hipError_t bwd_scratch(void** ptr);
 // which: 1 = dq kernel only, 2 = dk/dv kernel only, 3 = both in order
 hipError_t launch_bwd(const BwdArgs& a, int which, int dtype, bool out_f32, int d, int causal,
                       hipStream_t stream);

@@ -35,7 +35,8 @@
  *    status means nothing was launched and no output was touched, except
  *    ATTN_ERR_LAUNCH, which reports a failed kernel launch
  *    (hipGetLastError) after enqueueing.
- *  - There is no global mutable state; calls are thread-safe.
+ *  - There is no global mutable state apart from attn_bwd_noalloc's fixed
+ *    per-GPU workspace (see there); every other call is thread-safe.
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H
@@ -200,6 +201,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* workspace, size_t workspace_bytes,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, int out_dtype, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Arguments, results and
+ * kernels are those of attn_bwd; the workspace is a fixed array the library
+ * holds in every GPU's memory (ATTN_BWD_SCRATCH_BYTES, 16 MiB) until the
+ * process ends, so the call allocates and frees nothing.
+ *  - attn_bwd_workspace_size(B, H, N, d, dtype) must not exceed
+ *    ATTN_BWD_SCRATCH_BYTES (B * H * ceil(N / 64) * 64 <= 2^21 rows), else
+ *    ATTN_ERR_WORKSPACE and nothing is launched.
+ *  - The array is looked up on the current device (hipGetDevice) at the
+ *    first call there; `stream` must belong to that device.
+ *  - Every call on one GPU uses the same array: calls that overlap in time
+ *    on one GPU (on two streams, or from two threads without ordering) race
+ *    and give wrong gradients.  Calls on one stream are ordered and safe.
+ *    Nothing in the array needs clearing between calls: each call writes the
+ *    rows it reads.
+ */
+#define ATTN_BWD_SCRATCH_BYTES (16u << 20)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, float scale, int causal, int dtype, int out_dtype,
+                     void* stream);
 
 /*
  * attn_bwd_dq, attn_bwd_dkdv -- the two halves of attn_bwd, callable on

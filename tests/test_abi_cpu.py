@@ -31,6 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dropout",
+                                    "attn_bwd_noalloc",
                                     "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode", "attn_fwd_decode_fp8",
                                     "attn_fwd_dropout", "attn_fwd_fp8", "attn_fwd_split",
                                     "attn_fwd_split_workspace_size", "attn_status_str", "attn_std_fwd",
@@ -410,3 +411,33 @@ def test_std_passes_reject():
     assert attn.attn_std_pv(P[0], P[1], P[0], 2, 3, 100, 64, 1, 1, 0) == E_ALIAS
     assert attn.attn_std_pv(P[0], P[1], P[2], 2, 3, 100, 64, 1, 0, 0) == E_DT
     assert attn.attn_std_pv(P[0], P[1], P[2], 0, 3, 100, 64, 1, 1, 0) == OK
+
+
+# ---------------------------------------------------------------------------
+# backward without a workspace argument (validation only)
+# ---------------------------------------------------------------------------
+
+def bwd_noalloc(**kw):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8],
+             B=2, H=3, N=100, d=128, scale=0.1, causal=1, dtype=1, out_dtype=None, stream=0)
+    a.update(kw)
+    od = a["dtype"] if a["out_dtype"] is None else a["out_dtype"]
+    return attn.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["dO"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                 a["causal"], a["dtype"], od, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), E_NULL), (dict(dv=0), E_NULL), (dict(d=80), E_HD), (dict(dtype=3), E_DT),
+    (dict(causal=5), E_CAUSAL), (dict(scale=float("nan")), E_SCALE), (dict(dk=P[7] + 4), E_ALIGN),
+    (dict(dq=P[0]), E_ALIAS),
+    # workspace rows past the fixed 16 MiB scratch: B*H*ceil(N/64)*64 > 2^21
+    (dict(B=1, H=1, N=(1 << 21) + 1, d=64), E_WS), (dict(B=33, H=1, N=65536, d=64), E_WS),
+])
+def test_bwd_noalloc_rejects(kw, code):
+    assert bwd_noalloc(**kw) == code
+
+
+def test_bwd_noalloc_empty_is_noop():
+    assert bwd_noalloc(B=0, q=0, k=0) == OK
+    assert bwd_noalloc(N=0, dq=0) == OK
