@@ -78,15 +78,17 @@ def error_bound_values(q, k, v, scale, causal=False, rows=None, out_rel=0.0):
     fp64 inputs q [..., Nq, d] and k, v [..., Nk, d] (the values the codes
     stand for; under the causal mask query i sees keys 0 .. i + Nk - Nq).
 
-    With w_j the exact softmax weights of a row and v_j its visible V rows:
-    rounding P_j to nearest in E4M3 changes it by at most 2^-4 P_j while P_j
-    is in E4M3's normal range, and by at most 2^-10 (half the subnormal
-    spacing 2^-9) below it.  The method keeps every P of a row within
-    (0, 2^8] (below E4M3's largest value, 448) and the row's largest P at
-    least 2^4 relative to the reference point the row's sum is taken at, so
-    the row sum is at least 2^4 and a subnormal error weighs at most 2^-14
-    times the largest weight, in units of the normalised output.  Hence, per
-    output element c,
+    The reading of the method's scaling (FlashAttention-3's low-precision
+    forward scales P into the format's range; the pages fix no more): each
+    probability is rounded at some scale -- P_j = sigma_j w_j, one scale per
+    key or shared by many -- under which no P exceeds 2^8 (below E4M3's
+    largest value, 448) and the row's largest weight (among the keys summed
+    with it) maps to at least 2^4.  With w_j the exact softmax weights of a
+    row and v_j its visible V rows: rounding P_j to nearest in E4M3 changes
+    it by at most 2^-4 P_j while P_j is in E4M3's normal range, and by at
+    most 2^-10 (half the subnormal spacing 2^-9) below it, which in units of
+    the normalised output is at most 2^-14 times the largest weight.  Hence,
+    per output element c,
         |dO_c| <= 2^-4 sum_j w_j |v_jc| + 2^-14 max_j w_j sum_j |v_jc|
                   + 2^-10 sum_j w_j |v_jc| + out_rel |O_c| + 1e-6,
     the third term a generous allowance for fp32 accumulation over up to

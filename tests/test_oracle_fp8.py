@@ -4,11 +4,17 @@
   for all 256 codes, and against values the format's definition fixes.
 * The definition (decode, descale, exact attention in the C oracle) against
   the materialised NumPy attention on the same decoded values.
-* The error bound: an emulation written here of the method as the oracle's
-  reading states it (64-key tiles, a reference point kept within the stated
-  range, P rounded to nearest even E4M3 by torch, P.V and sums in fp64) stays
-  within the bound on random and outlier inputs, and plausible mistakes (V
-  paired with the neighbouring key, a missed rescale) break it.
+* The error bound, from the reading alone (no tiling of the kernel's): the
+  oracle's exact softmax weights w_j (the materialised NumPy attention) are
+  scaled and rounded to nearest even E4M3 by torch at every scale the
+  reading admits -- each key j at a scale sigma_j with the row's largest
+  weight mapped to at least 2^4 and sigma_j w_j at most 2^8 -- one scale for
+  the whole row at offsets across [2^4, 2^8], and independent per-key
+  scales drawn over the whole admissible range (which covers any order in
+  which a reference can move).  The output those rounded weights give stays
+  within the bound everywhere and comes within a factor of ten of it
+  somewhere; planted mistakes (V paired with the neighbouring key, a
+  missed rescale, equal merge weights for split chunks) break it.
 """
 import math
 
@@ -72,74 +78,94 @@ def _e4m3_round(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).double().numpy()
 
 
-def _emulate(q, k, v, scale, causal, mistake=None):
-    """The method as read: 64-key tiles per row; reference r (binades) moved
-    to (tile max - 4) when the tile max exceeds r + 8; P = 2^(s log2e - r)
-    rounded to E4M3 for P.V; l and lse from unrounded P."""
-    BH, N, d = q.shape
-    o = np.zeros((BH, N, d))
-    for bh in range(BH):
-        s = scale * (q[bh] @ k[bh].T) * math.log2(math.e)
-        for i in range(N):
-            kend = i + 1 if causal else N
-            ref, l, acc = -np.inf, 0.0, np.zeros(d)
-            for j0 in range(0, kend, 64):
-                x = s[i, j0:min(kend, j0 + 64)]
-                tmax = x.max()
-                if tmax > ref + 8:
-                    alpha = 0.0 if ref == -np.inf else 2.0 ** (ref - (tmax - 4))
-                    if mistake != "no_rescale":
-                        acc *= alpha
-                        l *= alpha
-                    ref = tmax - 4
-                p = np.exp2(x - ref)
-                assert p.max() <= 256.0
-                pr = _e4m3_round(p)
-                vv = v[bh, j0:j0 + x.size]
-                if mistake == "shift_v":
-                    vv = v[bh, np.minimum(np.arange(j0, j0 + x.size) + 1, N - 1)]
-                acc += pr @ vv
-                l += p.sum()
-            o[bh, i] = acc / l
-    return o
+def _rounded_weights(w, mode, rng):
+    """Weights of one softmax (w: [rows, keys], each row summing to one,
+    masked keys 0) as the reading uses them: w_j scaled by sigma_j, rounded
+    to E4M3, scaled back.  mode: a number a -- one scale per row, mapping the
+    row's largest weight to 2^a (4 <= a <= 8); "random" -- each key its own
+    scale, log2 sigma_j uniform over [4 - log2 max w, 8 - log2 w_j]; "low" /
+    "high" -- each key at the lower / upper end of that range."""
+    wmax = w.max(axis=1, keepdims=True)
+    pos = w > 0
+    lw = np.log2(np.where(pos, w, 1.0))
+    lo = 4.0 - np.log2(wmax) + np.zeros_like(w)
+    hi = 8.0 - lw
+    if mode == "random":
+        e = lo + rng.random(w.shape) * (hi - lo)
+    elif mode == "low":
+        e = lo
+    elif mode == "high":
+        e = hi
+    else:
+        e = float(mode) - np.log2(wmax) + np.zeros_like(w)
+    sig = np.exp2(e)
+    assert np.all(sig * w <= 256.0 * (1 + 1e-12))
+    return np.where(pos, _e4m3_round(sig * w) / sig, 0.0)
+
+
+MODES = [4.0, 5.5, 6.3, 7.0, 8.0, "low", "high", "random", "random"]
+
+
+def _weights_and_values(x, ds, causal):
+    scale = 1 / math.sqrt(128)
+    q, k, v = (ofp8.dequantize(x[n].numpy(), d) for n, d in zip("qkv", ds))
+    o, _, w = brute.fwd(q, k, v, scale, causal)
+    return w, v, o
 
 
 @pytest.mark.parametrize("outliers", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bound_holds_for_emulated_method(outliers, causal):
+def test_bound_covers_every_admissible_rounding(outliers, causal):
     name = "llama7b_layer_fwd" if outliers else "long_context_fwd"
-    w = WORKLOADS[name]
-    x, ds = make_fp8_inputs(w, seed=12, shape=(1, 2, 200, 128))
+    x, ds = make_fp8_inputs(WORKLOADS[name], seed=12, shape=(1, 2, 200, 128))
     scale = 1 / math.sqrt(128)
-    q, k, v = (ofp8.dequantize(x[n].numpy(), d).reshape(2, 200, 128) for n, d in zip("qkv", ds))
-    o_ref, _ = ofp8.fwd_fp8(x["q"], x["k"], x["v"], scale, ds, causal)
+    w, v, o = _weights_and_values(x, ds, causal)
     bound = ofp8.error_bound(x["q"], x["k"], x["v"], scale, ds, causal)
-    o_emu = _emulate(q, k, v, scale, causal)
-    err = np.abs(o_emu - o_ref.reshape(2, 200, 128))
-    assert np.all(err <= bound.reshape(2, 200, 128))
-    # the bound is not vacuous: somewhere the rounding comes within a
-    # factor of ten of it
-    assert (err / bound.reshape(2, 200, 128)).max() > 0.1
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for mode in MODES:
+        wh = np.stack([_rounded_weights(w[0, h], mode, rng) for h in range(2)])[None]
+        err = np.abs(wh @ v - o)
+        assert np.all(err <= bound), (mode, float((err / bound).max()))
+        worst = max(worst, float((err / bound).max()))
+    # the bound is not vacuous: some rounding comes within a factor of ten of it
+    assert worst > 0.1
+
+
+def test_bound_needs_the_lower_scale_limit():
+    """Outside the reading -- the row's largest weight mapped far below 2^4,
+    so that most weights fall into E4M3's subnormals -- the rounding breaks
+    the bound: its subnormal term relies on the lower limit."""
+    x, ds = make_fp8_inputs(WORKLOADS["long_context_fwd"], seed=12, shape=(1, 1, 200, 128))
+    scale = 1 / math.sqrt(128)
+    w, v, o = _weights_and_values(x, ds, False)
+    bound = ofp8.error_bound(x["q"], x["k"], x["v"], scale, ds, False)
+    wmax = w[0, 0].max(axis=1, keepdims=True)
+    sig = 2.0**-4 / wmax
+    wh = _e4m3_round(sig * w[0, 0]) / sig
+    assert np.any(np.abs(wh @ v[0, 0] - o[0, 0]) > bound[0, 0])
 
 
 @pytest.mark.parametrize("mistake", ["shift_v", "no_rescale"])
 def test_bound_catches_mistakes(mistake):
-    w = WORKLOADS["llama7b_layer_fwd"]
-    x, ds = make_fp8_inputs(w, seed=13, shape=(1, 1, 200, 128))
+    x, ds = make_fp8_inputs(WORKLOADS["llama7b_layer_fwd"], seed=13, shape=(1, 1, 200, 128))
     scale = 1 / math.sqrt(128)
-    q, k, v = (ofp8.dequantize(x[n].numpy(), d).reshape(1, 200, 128) for n, d in zip("qkv", ds))
-    if mistake == "no_rescale":
-        # key 150 scores far above every earlier key for each row that sees
-        # it, so the reference moves in the row's third tile
-        u = np.full(128, 0.5)
-        q = q + u
-        k[0, 150] = 10 * u
-    o_ref = brute.fwd(q, k, v, scale, True)[0]
-    bound = ofp8.error_bound_values(q, k, v, scale, True)
-    o_ok = _emulate(q, k, v, scale, True)
-    assert np.all(np.abs(o_ok - o_ref) <= bound)
-    o_bad = _emulate(q, k, v, scale, True, mistake=mistake)
-    assert np.any(np.abs(o_bad - o_ref) > bound)
+    w, v, o = _weights_and_values(x, ds, True)
+    w, v, o = w[0, 0], v[0, 0], o[0, 0]
+    bound = ofp8.error_bound(x["q"], x["k"], x["v"], scale, ds, True)[0, 0]
+    rng = np.random.default_rng(6)
+    wh = _rounded_weights(w, "random", rng)
+    assert np.all(np.abs(wh @ v - o) <= bound)
+    if mistake == "shift_v":
+        # each weight applied to the next key's V row
+        bad = wh @ np.concatenate([v[1:], v[-1:]])
+    else:
+        # the first half of the keys keeps the weight of a reference that
+        # later moved up by 4 binades: the accumulated output and sum both
+        # miss the factor 2^-4
+        f = np.where(np.arange(w.shape[1]) < w.shape[1] // 2, 16.0, 1.0)
+        bad = ((wh * f) @ v) / (w * f).sum(axis=1, keepdims=True)
+    assert np.any(np.abs(bad - o) > bound)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -158,58 +184,64 @@ def test_fwd_fp8_rect_equals_materialised(causal):
     assert np.abs(lse - lse2).max() <= 1e-12
 
 
-def _emulate_split(q, k, v, scale, causal, tiles_per_chunk, mistake=None):
-    """Nq queries against Nk keys in chunks of whole 64-key tiles: per chunk
-    and row the method as in _emulate (own reference, P rounded to E4M3,
-    normalised by the chunk's fp32 sum), then the exact logsumexp merge.
-    Rows that see no key get 0."""
-    BH, Nq, d = q.shape
-    Nk = k.shape[1]
-    o = np.zeros((BH, Nq, d))
-    for bh in range(BH):
-        s = scale * (q[bh] @ k[bh].T) * math.log2(math.e)
-        for i in range(Nq):
-            kend = min(Nk, i + 1 + Nk - Nq) if causal else Nk
-            parts = []
-            for c0 in range(0, max(kend, 0), 64 * tiles_per_chunk):
-                ref, l, acc = -np.inf, 0.0, np.zeros(d)
-                for j0 in range(c0, min(kend, c0 + 64 * tiles_per_chunk), 64):
-                    x = s[i, j0:min(kend, j0 + 64)]
-                    tmax = x.max()
-                    if tmax > ref + 8:
-                        alpha = 0.0 if ref == -np.inf else 2.0 ** (ref - (tmax - 4))
-                        acc *= alpha
-                        l *= alpha
-                        ref = tmax - 4
-                    p = np.exp2(x - ref)
-                    acc += _e4m3_round(p) @ v[bh, j0:j0 + x.size]
-                    l += p.sum()
-                parts.append((acc / l, (ref + math.log2(l)) * math.log(2)))
-            if not parts:
-                continue
-            lses = np.array([lc for _, lc in parts])
-            wts = np.exp(lses - lses.max())
-            if mistake == "equal_weights":
-                wts = np.ones_like(wts)
-            o[bh, i] = sum(wc * oc for wc, (oc, _) in zip(wts, parts)) / wts.sum()
-    return o
+def _chunked_rounded(q, k, v, scale, causal, bounds, rng, mistake=None):
+    """Nq queries against Nk keys, the keys cut at `bounds`: per chunk and
+    row the exact softmax over the chunk's visible keys, its weights rounded
+    as in _rounded_weights (mode "random", the chunk's own largest weight
+    mapped to at least 2^4), the chunk's partial output; then the exact
+    logsumexp merge of the chunks.  Rows that see no key get 0."""
+    Nq, Nk = q.shape[-2], k.shape[-2]
+    s = scale * (q @ k.T)
+    vis = (np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)) if causal else np.ones((Nq, Nk), bool)
+    out = np.zeros((Nq, q.shape[-1]))
+    parts_o, parts_l = [], []
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        inside = vis.copy()
+        inside[:, :c0] = False
+        inside[:, c1:] = False
+        sc = np.where(inside, s, -np.inf)
+        m = sc.max(axis=1, keepdims=True)
+        seen = np.isfinite(m)
+        e = np.where(inside, np.exp(sc - np.where(seen, m, 0.0)), 0.0)
+        l = e.sum(axis=1, keepdims=True)
+        w = e / np.where(seen, l, 1.0)
+        wh = np.zeros_like(w)
+        if seen.any():
+            rws = seen[:, 0]
+            wh[rws] = _rounded_weights(w[rws], "random", rng)
+        parts_o.append(wh @ v)
+        parts_l.append(np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf))
+    L = np.concatenate(parts_l, axis=1)
+    top = L.max(axis=1, keepdims=True)
+    seen = np.isfinite(top)
+    wts = np.where(np.isfinite(L), np.exp(L - np.where(seen, top, 0.0)), 0.0)
+    if mistake == "equal_weights":
+        wts = np.where(np.isfinite(L), 1.0, 0.0)
+    wts = wts / np.where(seen, wts.sum(axis=1, keepdims=True), 1.0)
+    for c, oc in enumerate(parts_o):
+        out += wts[:, c:c + 1] * oc
+    return out
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("Nq,Nk,tpc", [(1, 700, 2), (4, 300, 1), (16, 16, 1), (40, 20, 1), (130, 500, 3)])
-def test_bound_holds_for_chunked_rect(Nq, Nk, tpc, causal):
+@pytest.mark.parametrize("Nq,Nk,cuts", [(1, 700, [0, 128, 256, 640, 700]), (4, 300, [0, 64, 300]),
+                                        (16, 16, [0, 16]), (40, 20, [0, 8, 20]),
+                                        (130, 500, [0, 192, 384, 500])])
+def test_bound_holds_for_chunks(Nq, Nk, cuts, causal):
     w = WORKLOADS["llama7b_layer_fwd"]
     xq, ds = make_fp8_inputs(w, seed=16, shape=(1, 1, Nq, 128))
     xk, dk = make_fp8_inputs(w, seed=17, shape=(1, 1, Nk, 128))
     desc = (ds[0], dk[1], dk[2])
     scale = 1 / math.sqrt(128)
-    q = ofp8.dequantize(xq["q"].numpy(), desc[0]).reshape(1, Nq, 128)
-    k = ofp8.dequantize(xk["k"].numpy(), desc[1]).reshape(1, Nk, 128)
-    v = ofp8.dequantize(xk["v"].numpy(), desc[2]).reshape(1, Nk, 128)
+    q = ofp8.dequantize(xq["q"].numpy(), desc[0]).reshape(Nq, 128)
+    k = ofp8.dequantize(xk["k"].numpy(), desc[1]).reshape(Nk, 128)
+    v = ofp8.dequantize(xk["v"].numpy(), desc[2]).reshape(Nk, 128)
     o_ref, _ = ofp8.fwd_fp8_rect(xq["q"], xk["k"], xk["v"], scale, desc, causal)
-    bound = ofp8.error_bound(xq["q"], xk["k"], xk["v"], scale, desc, causal).reshape(1, Nq, 128)
-    o_emu = _emulate_split(q, k, v, scale, causal, tpc)
-    assert np.all(np.abs(o_emu - o_ref.reshape(1, Nq, 128)) <= bound)
+    bound = ofp8.error_bound(xq["q"], xk["k"], xk["v"], scale, desc, causal).reshape(Nq, 128)
+    rng = np.random.default_rng(7)
+    for _ in range(3):
+        o_c = _chunked_rounded(q, k, v, scale, causal, cuts, rng)
+        assert np.all(np.abs(o_c - o_ref.reshape(Nq, 128)) <= bound)
 
 
 def test_bound_catches_wrong_merge():
@@ -218,10 +250,13 @@ def test_bound_catches_wrong_merge():
     xk, dk = make_fp8_inputs(w, seed=19, shape=(1, 1, 640, 128))
     desc = (ds[0], dk[1], dk[2])
     scale = 1 / math.sqrt(128)
-    q = ofp8.dequantize(xq["q"].numpy(), desc[0]).reshape(1, 2, 128)
-    k = ofp8.dequantize(xk["k"].numpy(), desc[1]).reshape(1, 640, 128)
-    v = ofp8.dequantize(xk["v"].numpy(), desc[2]).reshape(1, 640, 128)
+    q = ofp8.dequantize(xq["q"].numpy(), desc[0]).reshape(2, 128)
+    k = ofp8.dequantize(xk["k"].numpy(), desc[1]).reshape(640, 128)
+    v = ofp8.dequantize(xk["v"].numpy(), desc[2]).reshape(640, 128)
     o_ref, _ = ofp8.fwd_fp8_rect(xq["q"], xk["k"], xk["v"], scale, desc, False)
-    bound = ofp8.error_bound(xq["q"], xk["k"], xk["v"], scale, desc, False).reshape(1, 2, 128)
-    o_bad = _emulate_split(q, k, v, scale, False, 2, mistake="equal_weights")
-    assert np.any(np.abs(o_bad - o_ref.reshape(1, 2, 128)) > bound)
+    bound = ofp8.error_bound(xq["q"], xk["k"], xk["v"], scale, desc, False).reshape(2, 128)
+    rng = np.random.default_rng(8)
+    cuts = [0, 128, 640]
+    assert np.all(np.abs(_chunked_rounded(q, k, v, scale, False, cuts, rng) - o_ref.reshape(2, 128)) <= bound)
+    o_bad = _chunked_rounded(q, k, v, scale, False, cuts, rng, mistake="equal_weights")
+    assert np.any(np.abs(o_bad - o_ref.reshape(2, 128)) > bound)
