@@ -138,8 +138,17 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     a.coff = 0;
     const int br = attn::fwd_block_rows();
     a.nqb = int((N + br - 1) / br);
-    // causal: one workgroup per pair of query blocks (a heavy and a light one)
-    const int64_t total = BH * (causal ? (a.nqb + 1) / 2 : a.nqb);
+    // causal: when B*H is a multiple of 8, one workgroup per query block in
+    // each XCD's heaviest-first order over groups of heads (the largest of 4,
+    // 3, 2, 1 that divides an XCD's B*H/8 heads); otherwise one per pair of
+    // query blocks (a heavy and a light one)
+    const int64_t per_xcd = BH / 8;
+    int64_t hg = 0;
+    if (causal && BH % 8 == 0)
+        for (hg = 4; per_xcd % hg != 0; --hg) {
+        }
+    a.hgroup = int(hg);
+    const int64_t total = a.hgroup ? BH * a.nqb : BH * (causal ? (a.nqb + 1) / 2 : a.nqb);
     if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
     a.total = int(total);
     a.c = exponent_unit(scale);
@@ -210,6 +219,7 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
     a.coff = 0;
     const int br = attn::fwd_block_rows();
     a.nqb = int((N + br - 1) / br);
+    a.hgroup = 0;
     const int64_t total = BH * (causal ? (a.nqb + 1) / 2 : a.nqb);
     if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
     a.total = int(total);
@@ -301,6 +311,7 @@ int fwd_split_common(const void* q, const void* k, const void* v, void* o, float
     a.c = exponent_unit(scale);
     a.negate = scale < 0.f;
     a.nsplit = nsplit;
+    a.hgroup = 0;
     a.split_o = split_o;
     a.split_lse = split_lse;
     a.drop = no_drop();

@@ -153,14 +153,17 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     // fp32 sum of the tile's P, formed with the current reference (see the
     // softmax pieces); 8-bit: from the tile's row maximum, computed first.
     constexpr bool LAZY = !F8;
-    // The row normaliser l (it divides O and gives lse) is one sum per row.
-    // fp16: the sum of P as rounded for the P.V product, so that O's weights
-    // sum to one exactly as used (P's rounding, 2^-11 relative, would
-    // otherwise reach the fp16 output bound on rows dominated by one key),
-    // and lse is within 2^-11 relative of l's exact value.  bf16 and 8-bit:
-    // the fp32 sum of P (their P rounding, 2^-9 and 2^-4 relative, would move
-    // lse too far); O then carries that rounding, at most 2^-9 max|v| for bf16.
+    // The row normalisers.  O is divided by the sum of P as rounded for the
+    // P.V product, so that O's weights sum to one exactly as used: P's
+    // rounding (2^-11 relative for fp16, 2^-8 for bf16) would otherwise move
+    // a row dominated by one key by that much of its V row, which reaches the
+    // output bound (bf16: 2^-8 of a V element of 4 is 1.6e-2).  lse needs the
+    // exact sum to 1e-3: fp16 takes the rounded sum for it too (2^-11
+    // relative); bf16 keeps a second, fp32 sum of P for lse (OSUM); 8-bit
+    // operands use the fp32 sum for both (their error bound accounts for
+    // P's rounding, 2^-4 relative).
     constexpr bool RSUM = std::is_same_v<T, _Float16>;
+    constexpr bool OSUM = std::is_same_v<T, __bf16>;
     static_assert(!F8 || (D == 128 && !DROP), "the 8-bit forward is instantiated for d = 128 only");
     constexpr int BC = bc<T, D>();
     static_assert(RING >= 4, "the pipeline needs four buffers per tensor");
@@ -194,10 +197,18 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
 
-    // Work: one query block of one (batch, head); under causal masking the
-    // pair of blocks nqb-1-p and p of one head, one after the other, so that
-    // every workgroup streams about as many tiles as any other (heavy and
-    // light blocks together) and the grid has no tail of heavy blocks.
+    // Work: one query block of one (batch, head).  Under causal masking the
+    // blocks differ in length (block b sees b + 1 blocks of keys), so the grid
+    // is ordered for the dispatcher, which hands workgroup i to XCD i % 8 and
+    // then to whichever of that XCD's slots frees first:
+    //  - hgroup > 0 (B*H a multiple of 8): XCD x takes the heads congruent to
+    //    x modulo 8, hgroup heads at a time, and each group's blocks heaviest
+    //    first; the light blocks of a group then fill the slots the heavy ones
+    //    free, only the last group's lightest blocks form the kernel's tail,
+    //    and an XCD streams the K/V of about hgroup heads at once (its L2);
+    //  - otherwise one workgroup takes the pair of blocks nqb-1-p and p of one
+    //    head, one after the other, so that every workgroup streams about as
+    //    many tiles as any other.
     // (the divisions by run-time counts are vector code; their results are
     // the same in every lane and are moved to scalar registers, so that they
     // and everything derived from them take no vector registers in the loop)
@@ -212,6 +223,13 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         const int qbi = rem / a.nsplit;
         split = rem - qbi * a.nsplit;
         qb_first = CAUSAL ? a.nqb - 1 - qbi : qbi;
+    } else if (CAUSAL && a.hgroup > 0) {
+        const int i = (int)blockIdx.x, x = i & 7, m = i >> 3;   // m-th workgroup of XCD x
+        const int per = a.hgroup * a.nqb;                        // workgroups of one group
+        const int g = m / per, rem = m - g * per;
+        const int r = rem / a.hgroup, u = rem - r * a.hgroup;
+        bh = 8 * (g * a.hgroup + u) + x;
+        qb_first = a.nqb - 1 - r;
     } else if (CAUSAL) {
         const int npairs = (a.nqb + 1) >> 1;
         bh = L / npairs;
@@ -331,11 +349,11 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 for (int e = 0; e < 16; ++e) oacc[r][cb][e] = 0.f;
         // per row: exponent reference (scaled units), and this lane's share of
         // the row's normaliser l
-        float mc_run[QB], l_run[QB];
+        float mc_run[QB], l_run[QB], lo_run[QB];   // lo_run: bf16's rounded sum (divides O)
         // (the reference starts at the lowest finite value: the first tile, whose
         // key 0 every row sees, always moves it, with alpha = 0)
     #pragma unroll
-        for (int r = 0; r < QB; ++r) mc_run[r] = -FLT_MAX, l_run[r] = 0.f;
+        for (int r = 0; r < QB; ++r) mc_run[r] = -FLT_MAX, l_run[r] = 0.f, lo_run[r] = 0.f;
 
         typedef f32x16 Scores[QB][KB];   // S^T of one tile, per row block and 32-key block
         typedef v8 Probs[QB][VK];        // P of one tile packed as B operands, per k-step
@@ -476,7 +494,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         constexpr int NPD = DROP ? 10 * KB : 0;
         constexpr int NP_ROW = NPD + (LAZY ? 8 * KB : 10 * KB + 1);
         constexpr int NP = QB * NP_ROW;
-        float st_mt[QB], st_mold[QB], st_l[QB];
+        float st_mt[QB], st_mold[QB], st_l[QB], st_lo[QB];
         constexpr int PWD = (int)sizeof(raw) / 4;   // words of one P operand
         unsigned pw[QB][VK][PWD];
         unsigned ph[QB][KB][4];   // generator state, then the call's four words
@@ -501,6 +519,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 }
             } else {
                 const unsigned pr = Elem<T>::cvt2(x0, x1);
+                if constexpr (OSUM) st_lo[r] = Elem<T>::sum2(pr, q == 0 ? 0.f : st_lo[r]);
                 if constexpr (RSUM) {
                     st_l[r] = Elem<T>::sum2(pr, q == 0 ? 0.f : st_l[r]);
                 } else if (q == 0) {
@@ -623,6 +642,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
                 for (int r = 0; r < QB; ++r) {
                     st_l[r] = 0.f;
+                    st_lo[r] = 0.f;
     #pragma unroll
                     for (int jj = 0; jj < VK; ++jj)
     #pragma unroll
@@ -679,6 +699,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
                         for (int e = 0; e < 16; ++e) oacc[r][cb][e] *= alpha;
                     l_run[r] *= alpha;
+                    lo_run[r] *= alpha;
                 }
             }
     #pragma unroll
@@ -695,6 +716,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     #pragma unroll
             for (int r = 0; r < QB; ++r) {
                 l_run[r] += st_l[r];
+                if constexpr (OSUM) lo_run[r] += st_lo[r];
             }
             if (!PAIRB || j % 2 == 1) {
                 wait_vmem_upto<WAIT_AT_BARRIER>();
@@ -752,9 +774,10 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < QB; ++r) {
             // (8-bit: O is also scaled by V's descale)
             const float l_tot = sum32(l_run[r]);
+            const float lo_tot = OSUM ? sum32(lo_run[r]) : l_tot;   // divides O
             // a row that sees no key of its chunk (split K/V only) gets O = 0 and
             // lse = -inf, which weigh nothing in the merge
-            float inv = l_tot > 0.f ? fast_rcp(l_tot) * (DROP ? a.drop.scale : 1.f) : 0.f;
+            float inv = l_tot > 0.f ? fast_rcp(lo_tot) * (DROP ? a.drop.scale : 1.f) : 0.f;
             if constexpr (F8) inv *= a.oscale;
             // (the row index passes through an empty asm statement so that
             // its 64-bit offset is formed here, not kept live through the loop)

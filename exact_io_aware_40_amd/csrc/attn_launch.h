@@ -39,6 +39,8 @@ struct FwdArgs {
     size_t split_lse;  // elements between their partial lse
     DropArgs drop;
     float oscale;      // 8-bit inputs only: factor applied to O (V's descale)
+    int hgroup;        // causal whole blocks, B*H a multiple of 8: heads per group in
+                       // each XCD's heaviest-first order (total = B*H*nqb); 0: pairs
 };
 
 int fwd_block_rows();

@@ -181,7 +181,7 @@ def test_workload_full_size():
     scale = 1 / math.sqrt(w.d)
     announce(f"bwd workload {w.describe()}")
     BH = w.B * w.H
-    heads = [0, 37, 90, BH - 1]
+    heads = [0, 19, 37, 64, 90, 101, 117, BH - 1]
     sel = lambda x: f64(x.reshape(BH, w.N, w.d)[heads]).reshape(1, len(heads), w.N, w.d)  # noqa: E731
     tol = TOL[w.torch_dtype]
     rq, rk, rv = check_16bit(t["q"], t["k"], t["v"], t["dO"], w.causal, scale, "full", heads=heads)

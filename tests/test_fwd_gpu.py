@@ -73,6 +73,24 @@ def test_causal_block_pairs(N):
     run_and_compare(q, k, v, True, 1 / math.sqrt(64), f"pairs N={N}")
 
 
+@pytest.mark.parametrize("B,H,N", [(2, 4, 300), (2, 8, 257), (4, 8, 129), (1, 24, 200), (3, 16, 385)])
+def test_causal_head_groups(B, H, N):
+    """With B*H a multiple of 8 the causal grid runs one query block per
+    workgroup in each XCD's heaviest-first order over groups of heads
+    (groups of 1, 2, 4, 3 and 3 heads here, ragged tails): every (batch,
+    head, block) is computed exactly once, and the result equals the paired
+    grid's (the same per-block computation) bit for bit."""
+    q, k, v = (randn((B, H, N, 64), torch.bfloat16, 140 + N + i) for i in range(3))
+    o, lse = run_and_compare(q, k, v, True, 1 / math.sqrt(64), f"head groups B={B} H={H}")
+    # the same heads plus one more (B*H + 1, not a multiple of 8) take the paired grid
+    q2, k2, v2 = (torch.cat([x.reshape(B * H, N, 64), x.reshape(B * H, N, 64)[:1]]).reshape(1, B * H + 1, N, 64)
+                  for x in (q, k, v))
+    o2, lse2 = attn.forward(q2.to(DEV), k2.to(DEV), v2.to(DEV), causal=True, scale=1 / math.sqrt(64))
+    torch.cuda.synchronize()
+    assert torch.equal(o2[0, :B * H].reshape(o.shape), o)
+    assert torch.equal(lse2[0, :B * H].reshape(lse.shape), lse)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.9])
 def test_zero_negative_and_large_scale(scale):
     q, k, v = (randn((1, 2, 200, 64), torch.float16, 60 + i) for i in range(3))
@@ -246,7 +264,10 @@ def test_workload_full_size(name):
     if B * H * N <= 1024:
         rows = np.arange(B * H * N)
     else:
-        rows = sample_rows(B, H, N, n_heads=6, per_head=48, seed=w.seed)
+        # about 32,768 rows from up to 64 heads (the first and last rows of
+        # each among them), element by element against the oracle
+        nh = min(B * H, 64)
+        rows = sample_rows(B, H, N, n_heads=nh, per_head=max(48, 32768 // nh), seed=w.seed)
     o_ref, lse_ref = oracle_fwd(t["q"], t["k"], t["v"], s32(scale), w.causal, rows=rows)
     of = o32.view(-1, d)[torch.from_numpy(rows).to(DEV)]
     lf = lse.view(-1)[torch.from_numpy(rows).to(DEV)]
