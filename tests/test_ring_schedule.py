@@ -48,10 +48,13 @@ def kernel_schedule():
     vlead = ring - int(re.search(r"constexpr int VLEAD = RING - (\d+);", text).group(1))
     pairb = "constexpr bool PAIRB = RING >= 5;" in text
     t0_barrier = re.search(r"else if \(t == 0\) \{[^}]*barrier_only\(\);", text, flags=re.S) is not None
-    return dict(ring=ring, klead=klead, vlead=vlead, pairb=pairb, t0_barrier=t0_barrier)
+    # after the loop: the wave's own copies waited for, then a barrier, before
+    # the epilogue stages O through the rings' LDS
+    epi = re.search(r"\n        wait_vmem\(\);\n        __syncthreads\(\);\n", text) is not None
+    return dict(ring=ring, klead=klead, vlead=vlead, pairb=pairb, t0_barrier=t0_barrier, epi_barrier=epi)
 
 
-def wave_events(ring, klead, vlead, pairb, t0_barrier, ntiles, skip_from, items=1):
+def wave_events(ring, klead, vlead, pairb, t0_barrier, ntiles, skip_from, items=1, epi_barrier=True):
     """The event list of one wave.  Events: ("copy", tensor, tile, buffer),
     ("wait", n) -- all but the n youngest copies complete --, ("barrier",),
     ("read", tensor, tile, buffer).  skip_from: first iteration whose
@@ -62,8 +65,10 @@ def wave_events(ring, klead, vlead, pairb, t0_barrier, ntiles, skip_from, items=
     for S of tile 0.  Iteration t = 0 .. ntiles: copies K(t + klead) and
     V(t + vlead) (only tiles < ntiles exist; a copy past the end is a
     zero-length copy that still counts), reads K(t + 1) and V(t - 1) unless
-    skipped, then the barrier rule.  Between items: wait for everything,
-    barrier."""
+    skipped, then the barrier rule.  After the loop: wait for everything,
+    the epilogue barrier (when the kernel has it), ("stage",) -- the wave
+    writes its O tile over the rings' LDS and reads it back --, and between
+    items a barrier."""
     ev = []
     per_iter_wait = 2 if pairb else 2 * (klead - 2)   # copies younger than those waited for
     for item in range(items):
@@ -95,6 +100,9 @@ def wave_events(ring, klead, vlead, pairb, t0_barrier, ntiles, skip_from, items=
             elif t == 0 and t0_barrier:
                 ev.append(("barrier",))
         ev.append(("wait", 0))
+        if epi_barrier:
+            ev.append(("barrier",))
+        ev.append(("stage", item))
         if item + 1 < items:
             ev.append(("barrier",))
     return ev
@@ -141,6 +149,24 @@ def check(waves):
                 rec[1][wi] = ep
                 # a plain store completes at once (program order); a copy when waited
                 rec[2][wi] = ep if e[0] == "store" else done_at[idx]
+    # staging: every copy of the item (zero-length ones included) complete in
+    # every wave before any wave stages O over the rings, and the next item's
+    # copies start after every wave has staged
+    for wi, (evs, done_at) in enumerate(info):
+        for idx, (e, ep) in enumerate(evs):
+            if e[0] != "stage":
+                continue
+            item = e[1]
+            for wj, (evj, dj) in enumerate(info):
+                for jdx, (e2, ep2) in enumerate(evj):
+                    if e2[0] == "copy" and e2[2][0] == item:
+                        d = dj[jdx]
+                        assert d is not None and d < ep, (
+                            f"wave {wi} stages O in epoch {ep} while wave {wj}'s copy of {e2[1]}{e2[2]} "
+                            f"may still be writing LDS (complete in epoch {d})")
+                    if e2[0] in ("copy", "store") and e2[2][0] > item:
+                        assert ep2 > ep, (f"wave {wj} starts {e2[1]}{e2[2]} in epoch {ep2} while wave {wi} "
+                                          f"stages O of item {item} (epoch {ep})")
     # reads: find the generation a read sees and check it
     for wi, (evs, _) in enumerate(info):
         for e, ep in evs:
@@ -157,6 +183,13 @@ def check(waves):
                 assert d is not None and (d < ep), (
                     f"wave {wi} reads {e[1]}({e[2]}) in epoch {ep} before wave {wj}'s share of it is "
                     f"complete and past a barrier (completed in epoch {d})")
+            # the epilogue's staging of O overwrites the rings: every wave's
+            # staging of this item must come after the read
+            for wj, (evj, _) in enumerate(info):
+                for e2, ep2 in evj:
+                    if e2[0] == "stage" and e2[1] == e[2][0]:
+                        assert ep2 > ep, (f"wave {wj} stages O over the rings in epoch {ep2} while wave "
+                                          f"{wi} may still read {e[1]}({e[2]}) (epoch {ep})")
             nxt = glist.get(g + 1)
             if nxt is not None:
                 for wj in range(n):
@@ -167,7 +200,7 @@ def check(waves):
 
 def run(sched, ntiles, skips, items=1):
     waves = [wave_events(sched["ring"], sched["klead"], sched["vlead"], sched["pairb"],
-                         sched["t0_barrier"], ntiles, s, items) for s in skips]
+                         sched["t0_barrier"], ntiles, s, items, sched.get("epi_barrier", True)) for s in skips]
     check(waves)
 
 
@@ -182,6 +215,15 @@ def test_kernel_schedule_is_read():
     s = kernel_schedule()
     assert s["ring"] in (4, 5)
     assert s["klead"] == s["ring"] - 1
+    assert s["epi_barrier"]
+
+
+def test_epilogue_without_its_barrier_is_a_race():
+    """Staging O over the rings right after the wave's own loop: another wave
+    may still read its last tiles, or its last copies may still land."""
+    s = dict(kernel_schedule(), epi_barrier=False)
+    with pytest.raises(AssertionError, match="stages O"):
+        run(s, 6, (7, 7, 7, 7))
 
 
 @pytest.mark.parametrize("ntiles", [1, 2, 3, 4, 5, 6, 9, 12])
