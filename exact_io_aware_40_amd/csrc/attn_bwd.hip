@@ -131,7 +131,9 @@ template <typename T> struct SplitDS { static constexpr bool value = false; };
 template <> struct SplitDS<_Float16> { static constexpr bool value = true; };
 
 // Store a 32-row x D accumulator set in "lane = row, 16 columns per block"
-// layout (the C layout of a product whose n index is the row), times f.
+// layout (the C layout of a product whose n index is the row), times f,
+// straight from the registers (the dq kernel, at its register limit, keeps
+// this form; the dk/dv kernel stages its rows through LDS).
 template <typename TO, int D>
 __device__ __forceinline__ void store_rows(TO* __restrict__ row_ptr, const f32x16* acc, float f, int h) {
 #pragma unroll
@@ -752,7 +754,9 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
                 }
         }
         __syncthreads();
-        if (qh == 0 && key < N) {
+        // (the whole wave takes part: the staged store below writes rows by
+        // lane other than the lanes' own keys; rows past N are not written)
+        if (qh == 0) {
     #pragma unroll
             for (int cb = 0; cb < DB; ++cb)
     #pragma unroll
@@ -766,8 +770,13 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
                     }
                 }
             const float rs = DROP ? a.drop.scale : 1.f;
-            store_rows<TO, D>((TO*)a.dk + head + (size_t)key * D, dk, a.scale * rs, h);
-            store_rows<TO, D>((TO*)a.dv + head + (size_t)key * D, dv, rs, h);
+            // dK and dV leave through LDS as whole rows, staged in this key
+            // group's part of the reduction area (only this wave reads or
+            // writes it after the barrier; its reads above complete first)
+            char* const stg = (char*)red;
+            store_rows_staged<TO, D>(stg, (TO*)a.dk + head + (size_t)kw0 * D, N - kw0, dk, a.scale * rs, lane);
+            store_rows_staged<TO, D>(stg + 32 * D * (int)sizeof(TO), (TO*)a.dv + head + (size_t)kw0 * D,
+                                     N - kw0, dv, rs, lane);
         }
     };
     key_block(kb_first);

@@ -337,6 +337,42 @@ template <> __device__ __forceinline__ void store4<_Float16>(_Float16* p, f32x4 
 }
 template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 x) { *(f32x4*)p = x; }
 
+// Store a wave's 32-row x D accumulator set, times f, through LDS.  In the
+// layout of a product whose n index is the row (lane l holds row l % 32,
+// four consecutive columns 32 cb + 8 g + 4 (l / 32) .. + 3 per quad g of
+// block cb), a direct store writes 64 rows x 8 bytes per instruction.
+// Instead the rounded rows go to `stage` (this wave's own 32 * D *
+// sizeof(TO) bytes of LDS, 16-byte aligned; each row's 16-byte granules
+// XOR-permuted by the row, so that the lanes' rows fall on distinct banks)
+// and come back as 16-byte row pieces: each store instruction then writes
+// 1 KiB (16-bit) of consecutive rows.  Rows base + r * D for r < rows_left
+// are written (rows_left may be <= 0: nothing).  The caller makes sure no
+// other wave uses `stage` meanwhile.
+template <typename TO, int D>
+__device__ __forceinline__ void store_rows_staged(char* stage, TO* __restrict__ base, int rows_left,
+                                                  const f32x16* acc, float f, int lane) {
+    constexpr int GPR = D * (int)sizeof(TO) / 16;   // 16-byte granules per row
+    static_assert((GPR & (GPR - 1)) == 0 && 32 * GPR % 64 == 0, "");
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 x = {acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f, acc[cb][4 * g + 2] * f,
+                       acc[cb][4 * g + 3] * f};
+            const int byte = (32 * cb + 8 * g + 4 * h) * (int)sizeof(TO);
+            const int gi = (byte >> 4) ^ (l32 & (GPR - 1));
+            store4<TO>((TO*)(stage + l32 * (GPR * 16) + gi * 16 + (byte & 15)), x);
+        }
+    }
+#pragma unroll 1
+    for (int i = 0; i < 32 * GPR / 64; ++i) {
+        const int gi = i * 64 + lane, row = gi / GPR, col = gi % GPR;
+        const i32x4 y = *(const i32x4*)(stage + row * (GPR * 16) + ((col ^ (row & (GPR - 1))) * 16));
+        if (row < rows_left) *(i32x4*)((char*)(base + (size_t)row * D) + col * 16) = y;
+    }
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011), the generator of the dropout mask.  A round
 // maps the counter (c0, c1, c2, c3) under key (k0, k1) to

@@ -786,38 +786,12 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
             // its 64-bit offset is formed here, not kept live through the loop)
             int qr = qrow[r];
             __asm__ volatile("" : "+v"(qr));
-            // O leaves through LDS: a lane holds four consecutive columns of
-            // its row per accumulator quad, so storing straight from the
-            // accumulators writes 64 rows x 8 bytes per instruction; instead
-            // each wave writes its 32 x D tile, rounded, to its own region of
-            // the idle rings (16-byte granules of a row XOR-permuted by the
-            // row, so that the lanes' rows fall on distinct banks) and reads it
-            // back as 16-byte row pieces, so that every store instruction
-            // writes 1 KiB of consecutive rows.
-            {
-                constexpr int GPR = D * (int)sizeof(TO) / 16;   // 16-byte granules per row
-                char* const ot = smem + w * (32 * D * (int)sizeof(TO));
-    #pragma unroll
-                for (int cb = 0; cb < DB; ++cb) {
-    #pragma unroll
-                    for (int gg = 0; gg < 4; ++gg) {
-                        f32x4 x = {oacc[r][cb][4 * gg] * inv, oacc[r][cb][4 * gg + 1] * inv,
-                                   oacc[r][cb][4 * gg + 2] * inv, oacc[r][cb][4 * gg + 3] * inv};
-                        // columns 32 cb + 8 gg + 4 h .. + 3 of row l32
-                        const int byte = (32 * cb + 8 * gg + 4 * h) * (int)sizeof(TO);
-                        const int g = (byte >> 4) ^ (l32 & (GPR - 1));
-                        store4<TO>((TO*)(ot + l32 * (GPR * 16) + g * 16 + (byte & 15)), x);
-                    }
-                }
-                const int rows_left = N - (qlo + 32 * r);   // rows of this block at or past qlo + 32 r
-                TO* __restrict__ obase = (TO*)a.o + (size_t)split * a.split_o + head + (size_t)(qlo + 32 * r) * D;
-    #pragma unroll 1
-                for (int i = 0; i < 32 * GPR / 64; ++i) {
-                    const int gi = i * 64 + lane, row = gi / GPR, col = gi % GPR;
-                    const i32x4 y = *(const i32x4*)(ot + row * (GPR * 16) + ((col ^ (row & (GPR - 1))) * 16));
-                    if (row < rows_left) *(i32x4*)((char*)(obase + (size_t)row * D) + col * 16) = y;
-                }
-            }
+            // O leaves through LDS as whole rows (a direct store from the
+            // accumulators would write 64 rows x 8 bytes per instruction),
+            // staged in this wave's own region of the idle rings
+            store_rows_staged<TO, D>(smem + w * (32 * D * (int)sizeof(TO)),
+                                     (TO*)a.o + (size_t)split * a.split_o + head + (size_t)(qlo + 32 * r) * D,
+                                     N - (qlo + 32 * r), oacc[r], inv, lane);
             if (qr < N) {
                 if (h == 0)
                     a.lse[(size_t)split * a.split_lse + (size_t)bh * N + qr] =
