@@ -281,6 +281,40 @@ def test_workload_full_size(name):
     assert err <= TOL[w.torch_dtype], err
 
 
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", [
+    (1, 64, 2048, 128, torch.bfloat16, True),      # head groups of 4, 16 blocks per head
+    (2, 64, 1024, 64, torch.float16, False),       # 1024 blocks, two rounds of workgroups
+    (1, 13, 4096, 128, torch.bfloat16, True),      # 13 heads: causal pairs
+    (3, 7, 2560, 64, torch.bfloat16, True),        # 21 heads, pairs
+    (4, 64, 777, 128, torch.float16, False),       # 1792 blocks, ragged tail
+    (8, 16, 1153, 64, torch.bfloat16, True),       # odd block count (10), head groups
+])
+def test_many_blocks(B, H, N, d, dtype, causal):
+    """Grids of several rounds of workgroups over many heads and blocks:
+    head counts that are and are not multiples of 8 (head groups or causal
+    pairs), odd block counts, ragged tails: sampled rows of fp32 O and lse
+    against the oracle, the 16-bit O equal to RNE(fp32 O) everywhere, and a
+    column of ones in V reproduced in every row."""
+    tag = f"many blocks B={B} H={H} N={N} d={d}"
+    announce(f"fwd {tag} {dtype} causal={causal}")
+    q, k, v = (randn((B, H, N, d), dtype, 300 + N + d + i) for i in range(3))
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o32, lse32 = attn.forward(qd, kd, vd, causal=causal, scale=scale, out_dtype=torch.float32)
+    o, lse = attn.forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o32.to(dtype)) and torch.equal(lse, lse32)
+    rows = sample_rows(B, H, N, n_heads=min(B * H, 24), per_head=160, seed=N + d)
+    o_ref, lse_ref = oracle_fwd(q, k, v, s32(scale), causal, rows=rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    report(f"{tag} O(fp32 out)", f64(o32.view(-1, d)[idx]), o_ref, TOL[dtype])
+    report(f"{tag} lse", f64(lse32.view(-1)[idx]), lse_ref, LSE_TOL)
+    vd[..., 0] = 1
+    o1, _ = attn.forward(qd, kd, vd, causal=causal, scale=scale, out_dtype=torch.float32)
+    err = (o1[..., 0] - 1).abs().max().item()
+    assert err <= TOL[dtype], err
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_heads(causal):
     """16,384 (batch, head) pairs of 40 rows: a grid far larger than the chip,
