@@ -205,11 +205,11 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];   // [stage][K | V]
 
     const int N = a.N, NP = padded_rows(N);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = tid_x(), lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
 
-    const int L = xcd_remap(blockIdx.x, total);
+    const int L = xcd_remap(wg_x(), total);
     // Work: one query block of one (batch, head); under causal masking the
     // pair of blocks nqb-1-p and p of one head, one after the other, so that
     // every workgroup streams about as many K/V tiles as any other and the
@@ -484,13 +484,13 @@ __global__ __launch_bounds__(NTK, 1) void dkdv_kernel(BwdArgs a, int nkb, int to
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int N = a.N, NP = padded_rows(N);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = tid_x(), lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = w & 3, qh = w >> 2;
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
 
-    const int L = xcd_remap(blockIdx.x, total);
+    const int L = xcd_remap(wg_x(), total);
     // Work: one key block of one (batch, head); under causal masking the pair
     // of blocks p (most queries) and nkb-1-p of one head, one after the
     // other, so that every workgroup streams about as many Q/dO tiles as any

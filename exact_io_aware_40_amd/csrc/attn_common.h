@@ -51,6 +51,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                              0x00020000);
 }
 
+// Work-item, workgroup and grid indices (x) read with the hardware
+// builtins.  HIP's threadIdx, blockIdx and gridDim go through device-library
+// functions that are not inlined under this build's floating-point flags:
+// each use would be a call whose entry waits for every outstanding memory
+// operation of the wave.
+__device__ __forceinline__ int tid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int wg_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int num_wg_x() {
+    return (int)(__builtin_amdgcn_grid_size_x() / __builtin_amdgcn_workgroup_size_x());
+}
+
 // Byte address in LDS of a pointer into a __shared__ array.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

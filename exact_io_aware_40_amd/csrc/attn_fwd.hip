@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     const int N = a.N;                  // query rows per head
     const int Nk = a.Nk;                // keys per head
     const int coff = a.coff;            // causal: row i sees keys 0 .. i + coff
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = tid_x(), lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int l32 = lane & 31, h = lane >> 5;
     const int s16 = lane & 15, grp = lane >> 4;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
     // (the divisions by run-time counts are vector code; their results are
     // the same in every lane and are moved to scalar registers, so that they
     // and everything derived from them take no vector registers in the loop)
-    const int L = xcd_remap(blockIdx.x, a.total);
+    const int L = xcd_remap(wg_x(), a.total);
     int bh, qb_first, qb_second = 0, nitems = 1, split = 0;
     if (a.nsplit > 0) {
         // split K/V: one query block and one chunk of its tiles (heaviest
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
         split = rem - qbi * a.nsplit;
         qb_first = CAUSAL ? a.nqb - 1 - qbi : qbi;
     } else if (CAUSAL && a.hgroup > 0) {
-        const int i = (int)blockIdx.x, x = i & 7, m = i >> 3;   // m-th workgroup of XCD x
+        const int i = wg_x(), x = i & 7, m = i >> 3;   // m-th workgroup of XCD x
         const int per = a.hgroup * a.nqb;                        // workgroups of one group
         const int g = m / per, rem = m - g * per;
         const int r = rem / a.hgroup, u = rem - r * a.hgroup;
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
                                                     int64_t rows, int nsplit, size_t split_o,
                                                     size_t split_lse) {
     constexpr int G = D / 4;   // 4-column groups per row
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t gid = (int64_t)wg_x() * 256 + tid_x();
     const int64_t row = gid / G;
     const int cg = (int)(gid - row * G);
     if (row >= rows) return;

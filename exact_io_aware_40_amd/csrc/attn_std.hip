@@ -42,10 +42,10 @@ __global__ __launch_bounds__(STD_NT, 2) void std_scores_kernel(const T* __restri
                                                                int nb, float scale) {
     typedef typename Elem<T>::v8 v8;
     constexpr int DK = D / 16;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = tid_x() & 63, w = tid_x() >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     // consecutive logical tiles (the tiles of one head) share an XCD and its L2
-    const unsigned L = (unsigned)xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const unsigned L = (unsigned)xcd_remap(wg_x(), num_wg_x());
     const int jb = (int)(L % (unsigned)nb);
     const unsigned rest = L / (unsigned)nb;
     const int ib = (int)(rest % (unsigned)nb);
@@ -121,8 +121,8 @@ __global__ __launch_bounds__(STD_NT) void std_softmax_kernel(const float* __rest
                                                              T* __restrict__ p,
                                                              float* __restrict__ lse,
                                                              size_t rows, int N, int causal) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const size_t row = (size_t)blockIdx.x * 4 + w;
+    const int lane = tid_x() & 63, w = tid_x() >> 6;
+    const size_t row = (size_t)wg_x() * 4 + w;
     if (row >= rows) return;   // the whole wave leaves; the kernel has no barrier
     const int i = (int)(row % (unsigned)N);
     const int lim = causal ? i + 1 : N;   // keys 0 .. lim-1 are visible (lim >= 1)
@@ -240,10 +240,10 @@ __global__ __launch_bounds__(STD_NT) void std_pv_kernel(const T* __restrict__ p,
     static_assert(G * STD_NT * 8 == KT * D, "the tile splits evenly over the workgroup");
     __shared__ __attribute__((aligned(16))) T vt[D * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = tid_x(), lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     // a head's query blocks share an XCD, so its V is read from HBM once
-    const unsigned L = (unsigned)xcd_remap((int)blockIdx.x, (int)gridDim.x);
+    const unsigned L = (unsigned)xcd_remap(wg_x(), num_wg_x());
     const int ib = (int)(L % (unsigned)nb);
     const size_t bh = L / (unsigned)nb;
     const int row = ib * PB + 32 * w + l32;
