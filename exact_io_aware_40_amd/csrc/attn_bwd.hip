@@ -266,8 +266,10 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
         // D_i, divided by the keep factor under dropout
         const float delta = sum32(dpart) * (DROP ? 1.f / a.drop.scale : 1.f);
         const float lse2 = live ? a.lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+        // (the dropout instantiation, short of registers for the generator,
+        // forms the same seed again before each chain instead of holding it)
         f32x16 ndseed = {};
-        if constexpr (SEED) {
+        if constexpr (SEED && !DROP) {
     #pragma unroll
             for (int r = 0; r < 16; ++r) ndseed[r] = -delta;
         }
@@ -357,8 +359,18 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
                     const int kk = i >> 1;
                     if ((i & 1) == 0)
                         s = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(qf[kk]), kk == 0 ? f32x16{} : s);
-                    else
-                        dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? ndseed : dp);
+                    else {
+                        f32x16 c0 = ndseed;
+                        if constexpr (SEED && DROP) {
+                            if (kk == 0) {
+                                float nd = -delta;
+                                __asm__ volatile("" : "+v"(nd));   // formed here, not held
+    #pragma unroll
+                                for (int r = 0; r < 16; ++r) c0[r] = nd;
+                            }
+                        }
+                        dp = Elem<T>::mma(bit_cast<v8>(fr[i % (DSD + 1)]), bit_cast<v8>(gf[kk]), kk == 0 ? c0 : dp);
+                    }
                     if (i + DSD < NSD) rd(i + DSD);
                 }
     #pragma unroll

@@ -146,3 +146,16 @@ def test_every_forward_and_standard_kernel_uses_no_scratch(objects):
     for name in ("attn_fwd", "attn_std"):
         for k, m in metadata(objects[name]).items():
             assert m.get("private_segment_fixed_size", 0) == 0, (k, m)
+
+
+def test_dropout_dq_loop_uses_no_scratch(objects):
+    """The dq kernel with dropout (bf16, d = 128, causal) forms its dP seed
+    before each chain instead of holding it, so its loop keeps everything in
+    registers (holding the seed cost 22 scratch accesses per key block)."""
+    ks = kernels(objects["attn_bwd"])
+    hits = [k for k in ks if re.search(r"dq_kernelIDF16bDF16bLi128ELb1ELb1E", k)]
+    assert hits
+    for k in hits:
+        for seg in segments(ks[k]):
+            if sum(i.startswith("v_mfma") for i in seg) >= 8:
+                assert not [i for i in seg if i.startswith("scratch_")], k
