@@ -25,6 +25,11 @@ WRITE_DIR turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
 such a command into profiles/traffic.json: HBM bytes per launch of each
 kernel, each counter scaled by the copy's known bytes over its reading.
 
+The default run also times the other workloads' forward and step, and the
+matrix cores' sustained bf16 rate on this board (attn_probe_mfma: products
+only, two workgroups per CU), against which each kernel's rate is stated
+beside the published 2.5 PFLOP/s; --no-other-workloads skips both.
+
 Side measurements (not the headline line): --decode NQ times a decode step
 against the HBM roofline, --dropout P the dropout path, and --fp8 the E4M3
 forward (attn_fwd_fp8) on the same workload quantised per tensor, against the
@@ -117,7 +122,10 @@ def parse():
     ap.add_argument("--counters", nargs="+", metavar="PMC_DIR",
                     help="write profiles/counters.json from rocprofv3 --pmc output dirs")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the forward and step timings of the other workloads")
+                    help="skip the context measurements: the other workloads' forward and step "
+                         "timings and the matrix-core ceiling")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the matrix cores' sustained bf16 rate (attn_probe_mfma)")
     ap.add_argument("--other-steps", type=int, default=10,
                     help="timed steps of each other workload")
     ap.add_argument("--standard", action="store_true",
@@ -173,6 +181,41 @@ def write_traffic(fetch_dir, write_dir, workload):
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps(rec[workload], indent=1))
+
+
+def mfma_ceiling(dev, rounds=15000, reps=5):
+    """The matrix cores' sustained bf16 rate on this board: attn_probe_mfma
+    (only products, on pseudo-random operands that change from one product
+    to the next, four chains per wave, two workgroups per CU) timed with HIP
+    events on the launch stream, median of `reps` launches after two warm-up
+    ones, at the clock the power limit allows (the probe runs right after
+    the timed steps, on a warm board)."""
+    props = torch.cuda.get_device_properties(dev)
+    wg = 2 * props.multi_processor_count
+    buf = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def launch():
+        st = attn.attn_probe_mfma(buf.data_ptr(), wg, rounds, sp)
+        if st != 0:
+            raise RuntimeError(attn.attn_status_str(st))
+
+    for _ in range(2):
+        launch()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = float(np.median(ms))
+    tflops = wg * 4 * 16 * rounds * 32768 / (med * 1e-3) / 1e12
+    return {"tflops": tflops, "frac_of_spec": tflops / PEAK_BF16_TFLOPS, "workgroups": wg, "rounds": rounds,
+            "ms_median": med, "launches": reps,
+            "kernel": "mfma_probe_kernel: v_mfma_f32_32x32x16_bf16 only, pseudo-random bf16 operands changing "
+                      "between products, 4 chains per wave, 2 waves per SIMD"}
 
 
 def cpu_baseline(w, t, scale, budget_s, gpu_out=None):
@@ -805,6 +848,16 @@ def main():
     if args.standard:
         bench_standard(args)
         return
+    if args.ceiling:
+        c = mfma_ceiling(torch.device("cuda:0"), reps=max(1, args.steps))
+        print(json.dumps({"metric": "bf16 matrix-core sustained rate (products only) at 1 GPU",
+                          "value": c["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": c["launches"],
+                          "warmup": 2, "ms_per_step": c["ms_median"], "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": "attn_probe_mfma: " + c["kernel"],
+                                     "workgroups": c["workgroups"], "rounds": c["rounds"]},
+                          "frac_of_peak": c["frac_of_spec"]}), flush=True)
+        return
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
     run = StepRunner(w, dev, dropout=args.dropout)
@@ -849,6 +902,16 @@ def main():
         "roofline": roofline,
         "kernel_source_hash": source_hash(),
     }
+    if not args.no_other_workloads:
+        # the matrix cores' sustained rate on this board: each kernel's rate
+        # against it, beside the published peak
+        ceil = mfma_ceiling(dev)
+        out["mfma_ceiling"] = ceil
+        out["frac_of_measured_ceiling"] = value / ceil["tflops"]
+        roofline["frac_of_measured_ceiling"] = achieved / ceil["tflops"]
+        for rec in list(phases.values()) + list(kernels.values()):
+            if "tflops" in rec:
+                rec["frac_of_measured_ceiling"] = rec["tflops"] / ceil["tflops"]
     o, lse = run.o, run.lse
     if not args.no_cpu_baseline and drop is None:
         torch.cuda.synchronize()

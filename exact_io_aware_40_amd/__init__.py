@@ -109,6 +109,8 @@ def _load():
     lib.attn_std_softmax.argtypes = [vp] * 3 + [i64, i64, i64, i32, i32, vp]
     lib.attn_std_pv.restype = i32
     lib.attn_std_pv.argtypes = [vp] * 3 + [i64, i64, i64, i64, i32, i32, vp]
+    lib.attn_probe_mfma.restype = i32
+    lib.attn_probe_mfma.argtypes = [vp, i64, i64, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -230,6 +232,10 @@ def attn_std_softmax(s: int, p: int, lse: int, B: int, H: int, N: int, causal: i
 def attn_std_pv(p: int, v: int, o: int, B: int, H: int, N: int, d: int, dtype: int,
                 out_dtype: int, stream: int) -> int:
     return _load().attn_std_pv(p, v, o, B, H, N, d, dtype, out_dtype, stream)
+
+
+def attn_probe_mfma(out: int, workgroups: int, rounds: int, stream: int) -> int:
+    return _load().attn_probe_mfma(out, workgroups, rounds, stream)
 
 
 def attn_status_str(status: int) -> str:

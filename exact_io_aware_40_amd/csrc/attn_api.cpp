@@ -624,4 +624,14 @@ int attn_std_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return std_pv(p, v, o, B, H, N, d, dtype, out_dtype, stream);
 }
 
+
+int attn_probe_mfma(float* out, int64_t workgroups, int64_t rounds, void* stream) {
+    if (workgroups < 1 || workgroups > (int64_t(1) << 20) || rounds < 1 || rounds > (int64_t(1) << 24))
+        return ATTN_ERR_SHAPE;
+    if (!out) return ATTN_ERR_NULL;
+    if (!aligned16(out)) return ATTN_ERR_ALIGN;
+    const hipError_t e = attn::launch_mfma_probe(out, int(workgroups), int(rounds), (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // extern "C"

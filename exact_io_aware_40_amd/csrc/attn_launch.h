@@ -94,4 +94,8 @@ hipError_t launch_std_softmax(const float* s, void* p, float* lse, int64_t BH, i
 hipError_t launch_std_pv(const void* p, const void* v, void* o, int64_t BH, int N, int d, int dtype,
                          bool out_f32, hipStream_t stream);
 
+// The matrix-core rate probe: `workgroups` workgroups of 256 threads, each
+// wave running 16 x rounds bf16 32x32x16 products; out gets one float per thread.
+hipError_t launch_mfma_probe(float* out, int workgroups, int rounds, hipStream_t stream);
+
 }  // namespace attn

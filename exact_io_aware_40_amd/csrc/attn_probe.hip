@@ -1,0 +1,73 @@
+// attn_probe.hip -- the matrix cores' sustained rate on this device.
+//
+// A kernel's utilisation is stated against two ceilings: the published dense
+// bf16 peak, and the rate a kernel doing nothing but products sustains on the
+// same board at the clock its power limit allows (the pages judge attention
+// kernels by the fraction of the hardware's peak they reach: "FlashAttention"
+// explainer, Step 6, and the section "IO-optimal is not occupancy-optimal").
+// The power a product draws depends on how its operand bits change, so the
+// operands are pseudo-random bf16 values of either sign in [0.5, 2), like
+// attention's Q, K, V and P, and consecutive products take different ones:
+// every wave keeps four chains of v_mfma_f32_32x32x16_bf16, chain j of round
+// step s multiplying A operand j by B operand (j + s) mod 4, four waves per
+// workgroup and two workgroups per CU, so that only the matrix pipes limit
+// the rate.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int PNT = 256;   // threads per workgroup: four waves, one per SIMD
+
+// The operands' bits: a 32-bit mixing function of x (the finaliser of
+// MurmurHash3), sign from bit 15, exponent 126 or 127 from bit 7, mantissa
+// from bits 0..6.
+__device__ __forceinline__ unsigned short probe_bits(unsigned x) {
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    x ^= x >> 16;
+    return (unsigned short)((x & 0x807Fu) | 0x3F00u | ((x >> 1) & 0x80u));
+}
+
+__global__ __launch_bounds__(PNT, 2) void mfma_probe_kernel(float* __restrict__ out, int rounds) {
+    typedef Elem<__bf16>::v8 v8;
+    const int tid = tid_x(), lane = tid & 63;
+    // operand j of this lane: element e = bits of (64 (8 j + e) + lane)
+    v8 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[j][e] = __builtin_bit_cast(__bf16, probe_bits((unsigned)(64 * (8 * j + e) + lane)));
+            b[j][e] = __builtin_bit_cast(__bf16, probe_bits((unsigned)(64 * (8 * (j + 4) + e) + lane)));
+        }
+    // Opaque to the compiler from here on, so it must hold the operands in
+    // registers and cannot move any part of their hashing into the loop.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(a[j]), "+v"(b[j]));
+    f32x16 c[4] = {};
+    for (int i = 0; i < rounds; ++i) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = Elem<__bf16>::mma(a[j], b[(j + s) & 3], c[j]);
+    }
+    // each lane's 64 accumulators summed and stored, so that every product
+    // is kept
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t += (c[0][r] + c[1][r]) + (c[2][r] + c[3][r]);
+    out[(size_t)wg_x() * PNT + tid] = t;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(float* out, int workgroups, int rounds, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(PNT), 0, stream, out, rounds);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -387,6 +387,32 @@ int attn_std_softmax(const float* s, void* p, float* lse, int64_t B, int64_t H, 
 int attn_std_pv(const void* p, const void* v, void* o, int64_t B, int64_t H, int64_t N,
                 int64_t d, int dtype, int out_dtype, void* stream);
 
+/*
+ * attn_probe_mfma -- a measurement aid, not part of the method: the rate the
+ * matrix cores sustain on this device, against which the kernels'
+ * utilisation is stated beside the published peak (the pages judge attention
+ * kernels by the fraction of the hardware's peak they reach: "FlashAttention"
+ * explainer, Step 6, "IO-optimal is not occupancy-optimal").  Launches
+ * `workgroups` workgroups of 256 threads (four waves); every wave runs
+ * `rounds` rounds of 16 v_mfma_f32_32x32x16_bf16 products (32768 FLOP each)
+ * in four chains: in step s = 0..3 of a round, chain j multiplies A operand
+ * j by B operand (j + s) mod 4, so consecutive products change operands.
+ * Element e of lane l's A operand j holds the bf16 bits h(64 (8 j + e) + l),
+ * of B operand j h(64 (8 (j + 4) + e) + l), where h(x) mixes x with the
+ * MurmurHash3 finaliser and keeps bit 15 (sign), bits 0..6 (mantissa) and
+ * bit 8 as the exponent's low bit (exponent 126 or 127): values of either
+ * sign in [0.5, 2), as random as attention's operands.  Every thread stores
+ * the sum of its 64 accumulators to out[workgroup * 256 + thread].  The
+ * caller times the launch (e.g. with HIP events): FLOP per launch =
+ * workgroups * 4 * 16 * rounds * 32768.
+ *   out        : device float array of workgroups * 256 elements (written)
+ *   workgroups : 1 .. 2^20 (two per compute unit fill the device)
+ *   rounds     : 1 .. 2^24
+ * Returns ATTN_OK, ATTN_ERR_SHAPE, ATTN_ERR_NULL, ATTN_ERR_ALIGN or
+ * ATTN_ERR_LAUNCH.
+ */
+int attn_probe_mfma(float* out, int64_t workgroups, int64_t rounds, void* stream);
+
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);
 

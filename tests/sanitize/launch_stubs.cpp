@@ -33,4 +33,6 @@ hipError_t launch_std_pv(const void*, const void*, void*, int64_t, int, int, int
     return hipErrorNotSupported;
 }
 
+hipError_t launch_mfma_probe(float*, int, int, hipStream_t) { return hipErrorNotSupported; }
+
 }  // namespace attn

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                                     "attn_bwd_noalloc",
                                     "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode", "attn_fwd_decode_fp8",
                                     "attn_fwd_dropout", "attn_fwd_fp8", "attn_fwd_split",
-                                    "attn_fwd_split_workspace_size", "attn_status_str", "attn_std_fwd",
+                                    "attn_fwd_split_workspace_size", "attn_probe_mfma", "attn_status_str",
+                                    "attn_std_fwd",
                                     "attn_std_pv", "attn_std_scores", "attn_std_softmax",
                                     "attn_std_workspace_size"]
 
@@ -411,6 +412,14 @@ def test_std_passes_reject():
     assert attn.attn_std_pv(P[0], P[1], P[0], 2, 3, 100, 64, 1, 1, 0) == E_ALIAS
     assert attn.attn_std_pv(P[0], P[1], P[2], 2, 3, 100, 64, 1, 0, 0) == E_DT
     assert attn.attn_std_pv(P[0], P[1], P[2], 0, 3, 100, 64, 1, 1, 0) == OK
+
+
+def test_mfma_probe_rejects():
+    """The matrix-core rate probe validates before launching (no GPU needed)."""
+    assert attn.attn_probe_mfma(0, 512, 100, 0) == E_NULL
+    assert attn.attn_probe_mfma(P[0] + 4, 512, 100, 0) == E_ALIGN
+    for wg, it in ((0, 100), (-1, 100), ((1 << 20) + 1, 100), (512, 0), (512, -3), (512, (1 << 24) + 1)):
+        assert attn.attn_probe_mfma(P[0], wg, it, 0) == E_SHAPE, (wg, it)
 
 
 # ---------------------------------------------------------------------------

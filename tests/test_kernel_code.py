@@ -13,7 +13,10 @@ changing any result, so no parity test would notice it:
     load it tracks (vmcnt counts the copies too) would make every tile
     position wait for copies started in the same position;
   * the kernels the benchmark times keep everything in registers (no
-    scratch memory).
+    scratch memory);
+  * the matrix-core probe's loop holds its products and the loop counter
+    and nothing else (the compiler is free to recompute the operands inside
+    the loop instead of holding them, which would measure the vector ALU).
 """
 import os
 import re
@@ -75,7 +78,7 @@ def metadata(co):
 @pytest.fixture(scope="module")
 def objects(tmp_path_factory):
     tmp = str(tmp_path_factory.mktemp("code"))
-    return {n: code_object(n, tmp) for n in ("attn_fwd", "attn_bwd", "attn_std")}
+    return {n: code_object(n, tmp) for n in ("attn_fwd", "attn_bwd", "attn_std", "attn_probe")}
 
 
 def test_tools_found():
@@ -159,3 +162,21 @@ def test_dropout_dq_loop_uses_no_scratch(objects):
         for seg in segments(ks[k]):
             if sum(i.startswith("v_mfma") for i in seg) >= 8:
                 assert not [i for i in seg if i.startswith("scratch_")], k
+
+
+def test_probe_loop_is_products_only(objects):
+    ks = {k: v for k, v in kernels(objects["attn_probe"]).items() if "mfma_probe_kernel" in k}
+    assert len(ks) == 1
+    (ins,) = ks.values()
+    loops = [s for s in segments(ins) if sum(i.startswith("v_mfma") for i in s) == 16]
+    assert len(loops) == 1
+    body = loops[0]
+    # the loop starts after the last accumulator initialisation
+    start = max(n for n, i in enumerate(body) if not i.startswith(("v_mfma", "s_"))) + 1
+    rest = [i.split()[0] for i in body[start:] if not i.startswith("v_mfma")]
+    assert set(rest) <= {"s_nop", "s_add_i32", "s_sub_i32", "s_cmp_lg_u32", "s_cmp_eq_u32", "s_cbranch_scc1",
+                         "s_cbranch_scc0"}, rest
+    assert sum(i.startswith("v_mfma_f32_32x32x16_bf16") for i in body[start:]) == 16
+    md = metadata(objects["attn_probe"])
+    (m,) = [v for k, v in md.items() if "mfma_probe_kernel" in k]
+    assert m.get("private_segment_fixed_size", 0) == 0 and m.get("vgpr_spill_count", 0) == 0
