@@ -510,12 +510,23 @@ __global__ __launch_bounds__(NT, OCC) void fwd_kernel(FwdArgs a) {
                 // b / 2; the row sum is that of the fp32 probabilities
                 const int jj = b >> 1, wd = 4 * (b & 1) + (e >> 2);
                 const bool hi = (e >> 1) & 1;
-                pw[r][jj][wd] = Elem<T>::cvt2_into(x0, x1, hi ? pw[r][jj][wd] : 0u, hi);
                 if (q == 0) {
                     st_l[r] = x0 + x1;
                 } else {
                     st_l[r] += x0;
                     st_l[r] += x1;
+                }
+                if (hi) {
+                    pw[r][jj][wd] = Elem<T>::cvt2_into(x0, x1, pw[r][jj][wd], true);
+                } else {
+                    // the low pair is written into x1's own register, whose
+                    // upper two bytes the hi call replaces: a zeroed word
+                    // would cost a register move per word.  The empty asm
+                    // takes the updated sum as input, so the sum reads x1
+                    // before the conversion overwrites it and no copy is made
+                    unsigned xb = __float_as_uint(x1);
+                    __asm__("" : "+v"(xb) : "v"(st_l[r]));
+                    pw[r][jj][wd] = Elem<T>::cvt2_into(x0, __uint_as_float(xb), xb, false);
                 }
             } else {
                 const unsigned pr = Elem<T>::cvt2(x0, x1);
