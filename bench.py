@@ -188,8 +188,8 @@ def mfma_ceiling(dev, rounds=15000, reps=5):
     (only products, on pseudo-random operands that change from one product
     to the next, four chains per wave, two workgroups per CU) timed with HIP
     events on the launch stream, median of `reps` launches after two warm-up
-    ones, at the clock the power limit allows (the probe runs right after
-    the timed steps, on a warm board)."""
+    ones, at whatever clock the board holds under that load (the probe runs
+    right after the timed steps, on a warm board)."""
     props = torch.cuda.get_device_properties(dev)
     wg = 2 * props.multi_processor_count
     buf = torch.empty(wg * 256, dtype=torch.float32, device=dev)
