@@ -16,7 +16,10 @@ changing any result, so no parity test would notice it:
     scratch memory);
   * the matrix-core probe's loop holds its products and the loop counter
     and nothing else (the compiler is free to recompute the operands inside
-    the loop instead of holding them, which would measure the vector ALU).
+    the loop instead of holding them, which would measure the vector ALU);
+  * the 8-bit forward zeroes no register for its probability conversions
+    (each P word is built by two 2-byte conversions; a zeroed start costs a
+    vector move per word on a loop the vector ALU bounds).
 """
 import os
 import re
@@ -180,3 +183,22 @@ def test_probe_loop_is_products_only(objects):
     md = metadata(objects["attn_probe"])
     (m,) = [v for k, v in md.items() if "mfma_probe_kernel" in k]
     assert m.get("private_segment_fixed_size", 0) == 0 and m.get("vgpr_spill_count", 0) == 0
+
+
+def test_fp8_probability_words_start_from_no_zeroed_register(objects):
+    """In every run of instructions that converts 8-bit probabilities, no
+    register a conversion writes was set to 0 first (an earlier form of the
+    kernel did so for every P word: 80 such moves per kernel)."""
+    ks = {k: v for k, v in kernels(objects["attn_fwd"]).items() if "fwd_kernel" in k and "fp8" in k}
+    assert len(ks) >= 6
+    for k, ins in ks.items():
+        ncvt = 0
+        for seg in segments(ins):
+            cvt = [i for i in seg if i.startswith("v_cvt_pk_fp8_f32")]
+            if not cvt:
+                continue
+            ncvt += len(cvt)
+            dests = {i.split()[1].rstrip(",") for i in cvt}
+            zeroed = [i for i in seg if re.fullmatch(r"v_mov_b32_e32 v\d+, 0", i) and i.split()[1].rstrip(",") in dests]
+            assert not zeroed, (k, zeroed[:4])
+        assert ncvt >= 16, k
