@@ -33,6 +33,18 @@ Range range(const void* p, size_t bytes) {
     return Range{lo, lo + bytes};
 }
 
+// A grid with one query block per (batch, head) and no dropout reads every
+// K/V tile in one workgroup only: those launches take the instantiation
+// whose copies are marked non-temporal (same outputs).
+hipError_t launch_forward(const attn::FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t s) {
+    return a.nqb == 1 && !a.drop.on ? attn::launch_fwd_once(a, dtype, out_f32, d, causal, s)
+                                    : attn::launch_fwd(a, dtype, out_f32, d, causal, s);
+}
+hipError_t launch_forward_fp8(const attn::FwdArgs& a, int out_dtype, int causal, hipStream_t s) {
+    return a.nqb == 1 ? attn::launch_fwd_fp8_once(a, out_dtype, causal, s)
+                      : attn::launch_fwd_fp8(a, out_dtype, causal, s);
+}
+
 // Common checks of sizes, flags and scale.  Returns ATTN_OK or an error;
 // sets *empty when there is nothing to compute.
 int check_common(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
@@ -158,8 +170,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     a.split_lse = 0;
     a.drop = drop;
     a.oscale = 1.f;
-    hipError_t e = attn::launch_fwd(a, dtype, out_dtype == ATTN_F32, int(d), causal,
-                                    (hipStream_t)stream);
+    hipError_t e = launch_forward(a, dtype, out_dtype == ATTN_F32, int(d), causal, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -230,7 +241,7 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
     a.split_lse = 0;
     a.drop = no_drop();
     a.oscale = v_descale;
-    hipError_t e = attn::launch_fwd_fp8(a, out_dtype, causal, (hipStream_t)stream);
+    hipError_t e = launch_forward_fp8(a, out_dtype, causal, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -317,8 +328,8 @@ int fwd_split_common(const void* q, const void* k, const void* v, void* o, float
     a.drop = no_drop();
     a.oscale = f8.on ? f8.vd : 1.f;
     // the partials are fp32 whatever the output type; the merge rounds once
-    hipError_t e = f8.on ? attn::launch_fwd_fp8(a, ATTN_F32, causal, (hipStream_t)stream)
-                         : attn::launch_fwd(a, dtype, true, int(d), causal, (hipStream_t)stream);
+    hipError_t e = f8.on ? launch_forward_fp8(a, ATTN_F32, causal, (hipStream_t)stream)
+                         : launch_forward(a, dtype, true, int(d), causal, (hipStream_t)stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
     e = attn::launch_fwd_merge(ws_o, ws_lse, o, lse, BH * Nq, nsplit, split_o, split_lse, int(d), dtype,
                                out_dtype == ATTN_F32, (hipStream_t)stream);
@@ -631,6 +642,19 @@ int attn_probe_mfma(float* out, int64_t workgroups, int64_t rounds, void* stream
     if (!out) return ATTN_ERR_NULL;
     if (!aligned16(out)) return ATTN_ERR_ALIGN;
     const hipError_t e = attn::launch_mfma_probe(out, int(workgroups), int(rounds), (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_probe_hbm(const void* buf, int64_t bytes, unsigned* out, int64_t workgroups, void* stream) {
+    if (workgroups < 1 || workgroups > (int64_t(1) << 20) || bytes < 16 || bytes % 16 != 0 ||
+        bytes > (int64_t(1) << 42))
+        return ATTN_ERR_SHAPE;
+    if (!buf || !out) return ATTN_ERR_NULL;
+    if (!aligned16(buf) || !aligned16(out)) return ATTN_ERR_ALIGN;
+    if (overlap(range(buf, size_t(bytes)), range(out, size_t(workgroups) * 256 * sizeof(unsigned))))
+        return ATTN_ERR_ALIAS;
+    const hipError_t e = attn::launch_hbm_probe(buf, (long long)(bytes / 16), out, int(workgroups),
+                                                (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

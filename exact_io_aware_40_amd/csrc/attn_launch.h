@@ -48,6 +48,11 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int caus
 // 8-bit E4M3 q, k, v (d = 128, whole query blocks, no dropout); out_dtype:
 // 0 fp16, 1 bf16, 2 fp32
 hipError_t launch_fwd_fp8(const FwdArgs& a, int out_dtype, int causal, hipStream_t stream);
+// The same launches for a grid with one query block per (batch, head) and no
+// dropout (a.nqb == 1, !a.drop.on): no two workgroups read the same K/V tile,
+// and the copies are marked non-temporal.  Same outputs bit for bit.
+hipError_t launch_fwd_once(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
+hipError_t launch_fwd_fp8_once(const FwdArgs& a, int out_dtype, int causal, hipStream_t stream);
 
 // Split K/V: workspace bytes for nsplit chunks (fp32 partial O and lse), and
 // the merge of the partials into o (dtype, or fp32) and lse.
@@ -97,5 +102,6 @@ hipError_t launch_std_pv(const void* p, const void* v, void* o, int64_t BH, int 
 // The matrix-core rate probe: `workgroups` workgroups of 256 threads, each
 // wave running 16 x rounds bf16 32x32x16 products; out gets one float per thread.
 hipError_t launch_mfma_probe(float* out, int workgroups, int rounds, hipStream_t stream);
+hipError_t launch_hbm_probe(const void* buf, long long n16, unsigned* out, int workgroups, hipStream_t stream);
 
 }  // namespace attn

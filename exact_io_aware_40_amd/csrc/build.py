@@ -14,7 +14,7 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 BUILD = os.environ.get("ATTN_BUILD_DIR", os.path.join(ROOT, "_build", "attn"))
 LIB = os.environ.get("ATTN_LIB_OUT", os.path.join(PKG, "libattn.so"))
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_std.hip", "attn_scratch.hip", "attn_probe.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_std.hip", "attn_scratch.hip", "attn_probe.hip", "attn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # The kernels never create NaN (masked scores are -inf, and every exponent

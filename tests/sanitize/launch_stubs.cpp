@@ -11,6 +11,8 @@ namespace attn {
 int fwd_block_rows() { return 128; }
 hipError_t launch_fwd(const FwdArgs&, int, bool, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_fwd_fp8(const FwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_fwd_once(const FwdArgs&, int, bool, int, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_fwd_fp8_once(const FwdArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
 size_t fwd_split_workspace_bytes(int64_t BH, int64_t N, int64_t d, int nsplit) {
     return size_t(nsplit) * size_t(BH) * size_t(N) * size_t(d + 1) * 4;
 }
@@ -34,5 +36,6 @@ hipError_t launch_std_pv(const void*, const void*, void*, int64_t, int, int, int
 }
 
 hipError_t launch_mfma_probe(float*, int, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_hbm_probe(const void*, long long, unsigned*, int, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace attn

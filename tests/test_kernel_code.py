@@ -19,7 +19,10 @@ changing any result, so no parity test would notice it:
     the loop instead of holding them, which would measure the vector ALU);
   * the 8-bit forward zeroes no register for its probability conversions
     (each P word is built by two 2-byte conversions; a zeroed start costs a
-    vector move per word on a loop the vector ALU bounds).
+    vector move per word on a loop the vector ALU bounds);
+  * the forward's K/V copies are non-temporal exactly in the instantiations
+    for single-reader grids (a decode step), where that streams faster, and
+    plain everywhere else, where it would evict tiles other workgroups read.
 """
 import os
 import re
@@ -81,7 +84,7 @@ def metadata(co):
 @pytest.fixture(scope="module")
 def objects(tmp_path_factory):
     tmp = str(tmp_path_factory.mktemp("code"))
-    return {n: code_object(n, tmp) for n in ("attn_fwd", "attn_bwd", "attn_std", "attn_probe")}
+    return {n: code_object(n, tmp) for n in ("attn_fwd", "attn_decode", "attn_bwd", "attn_std", "attn_probe")}
 
 
 def test_tools_found():
@@ -114,8 +117,8 @@ def test_forward_loop_waits_for_no_memory_operation(objects):
     32x32x16 products with 16-bit operands, 8 32x32x64 ones with 8-bit
     operands) -- the main loop's body -- contains no vmcnt wait; the waits
     for the copies sit only at the barriers between positions."""
-    ks = {k: v for k, v in kernels(objects["attn_fwd"]).items() if "fwd_kernel" in k}
-    assert len(ks) >= 38
+    ks = {k: v for n in ("attn_fwd", "attn_decode") for k, v in kernels(objects[n]).items() if "fwd_kernel" in k}
+    assert len(ks) >= 38 + 22
     for k, ins in ks.items():
         nmm = 8 if "fp8" in k else 16
         bodies = [s for s in segments(ins) if sum(i.startswith("v_mfma") for i in s) >= nmm]
@@ -149,7 +152,7 @@ def test_benchmarked_kernels_use_no_scratch(objects):
 
 
 def test_every_forward_and_standard_kernel_uses_no_scratch(objects):
-    for name in ("attn_fwd", "attn_std"):
+    for name in ("attn_fwd", "attn_decode", "attn_std"):
         for k, m in metadata(objects[name]).items():
             assert m.get("private_segment_fixed_size", 0) == 0, (k, m)
 
@@ -189,8 +192,9 @@ def test_fp8_probability_words_start_from_no_zeroed_register(objects):
     """In every run of instructions that converts 8-bit probabilities, no
     register a conversion writes was set to 0 first (an earlier form of the
     kernel did so for every P word: 80 such moves per kernel)."""
-    ks = {k: v for k, v in kernels(objects["attn_fwd"]).items() if "fwd_kernel" in k and "fp8" in k}
-    assert len(ks) >= 6
+    ks = {k: v for n in ("attn_fwd", "attn_decode") for k, v in kernels(objects[n]).items()
+          if "fwd_kernel" in k and "fp8" in k}
+    assert len(ks) >= 12
     for k, ins in ks.items():
         ncvt = 0
         for seg in segments(ins):
@@ -202,3 +206,17 @@ def test_fp8_probability_words_start_from_no_zeroed_register(objects):
             zeroed = [i for i in seg if re.fullmatch(r"v_mov_b32_e32 v\d+, 0", i) and i.split()[1].rstrip(",") in dests]
             assert not zeroed, (k, zeroed[:4])
         assert ncvt >= 16, k
+
+
+def test_forward_copies_are_non_temporal_only_for_single_reader_grids(objects):
+    def copies(ins):
+        c = [i for i in ins if i.startswith("buffer_load_dwordx4") and i.endswith(" lds")]
+        return sum(" nt lds" in i for i in c), sum(" nt lds" not in i for i in c)
+
+    for name, want_nt in (("attn_fwd", False), ("attn_decode", True)):
+        ks = {k: v for k, v in kernels(objects[name]).items() if "fwd_kernel" in k}
+        assert ks, name
+        for k, ins in ks.items():
+            nt, plain = copies(ins)
+            assert nt + plain >= 8, k
+            assert (plain == 0) if want_nt else (nt == 0), (name, k, nt, plain)

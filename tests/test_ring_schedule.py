@@ -34,7 +34,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "exact_io_aware_40_amd", "csrc", "attn_fwd.hip")
+SRC = os.path.join(ROOT, "exact_io_aware_40_amd", "csrc", "attn_fwd_kernel.h")
 
 
 def kernel_schedule():
