@@ -31,7 +31,8 @@ only, two workgroups per CU), against which each kernel's rate is stated
 beside the published 2.5 PFLOP/s; --no-other-workloads skips both.
 
 Side measurements (not the headline line): --decode NQ times a decode step
-against the HBM roofline, --dropout P the dropout path, and --fp8 the E4M3
+against the HBM roofline and the measured one-pass read rate (--hbm-ceiling
+prints that rate alone), --dropout P the dropout path, and --fp8 the E4M3
 forward (attn_fwd_fp8) on the same workload quantised per tensor, against the
 dense fp8 matrix peak.
 """
@@ -59,7 +60,9 @@ PEAK_HBM_GBS = 8000.0
 # the sources each kernel is built from: the fused kernels' and the
 # materialised baseline's counter data are keyed separately
 KERNEL_SOURCES = {
-    "fused": ["exact_io_aware_40_amd/csrc/attn_fwd.hip",
+    "fused": ["exact_io_aware_40_amd/csrc/attn_fwd_kernel.h",
+              "exact_io_aware_40_amd/csrc/attn_fwd.hip",
+              "exact_io_aware_40_amd/csrc/attn_decode.hip",
               "exact_io_aware_40_amd/csrc/attn_bwd.hip",
               "exact_io_aware_40_amd/csrc/attn_common.h"],
     "standard": ["exact_io_aware_40_amd/csrc/attn_std.hip",
@@ -129,6 +132,8 @@ def parse():
                          "timings and the matrix-core ceiling")
     ap.add_argument("--ceiling", action="store_true",
                     help="only measure the matrix cores' sustained bf16 rate (attn_probe_mfma)")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only measure the HBM read rate of a plain one-pass read (attn_probe_hbm)")
     ap.add_argument("--other-steps", type=int, default=10,
                     help="timed steps of each other workload")
     ap.add_argument("--standard", action="store_true",
@@ -219,6 +224,44 @@ def mfma_ceiling(dev, rounds=15000, reps=5):
             "ms_median": med, "launches": reps,
             "kernel": "mfma_probe_kernel: v_mfma_f32_32x32x16_bf16 only, pseudo-random bf16 operands changing "
                       "between products, 4 chains per wave, 2 waves per SIMD"}
+
+
+def hbm_ceiling(dev, nbytes=4 << 30, reps=5, wg_per_cu=(16, 32, 64)):
+    """The rate at which this board streams a buffer from HBM:
+    attn_probe_hbm (16-byte non-temporal loads, eight in flight per thread,
+    a checksum kept) over `nbytes`, for a few grid sizes, each the median of
+    `reps` launches after two warm-up ones; the best of them."""
+    props = torch.cuda.get_device_properties(dev)
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    sweep = {}
+    for m in wg_per_cu:
+        wg = m * props.multi_processor_count
+        out = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+
+        def launch():
+            st = attn.attn_probe_hbm(buf.data_ptr(), nbytes, out.data_ptr(), wg, sp)
+            if st != 0:
+                raise RuntimeError(attn.attn_status_str(st))
+
+        for _ in range(2):
+            launch()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        sweep[wg] = nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+        del out
+    best = max(sweep, key=sweep.get)
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbs": sweep[best], "frac_of_spec": sweep[best] / PEAK_HBM_GBS, "bytes": nbytes,
+            "workgroups": best, "gbs_by_workgroups": sweep, "launches": reps,
+            "kernel": "hbm_probe_kernel: one pass over the buffer, 16-byte non-temporal loads, eight in flight per thread"}
 
 
 def cpu_baseline(w, t, scale, budget_s, gpu_out=None):
@@ -312,7 +355,9 @@ def bench_decode(args):
     Algorithmic bytes: K and V read once, q read, o and lse written, and the
     fp32 partials written and read back by the merge.  With --fp8 the step
     is attn_fwd_decode_fp8 on E4M3 q, k, v (inputs.make_decode_fp8_inputs),
-    one byte per element read, bf16 output."""
+    one byte per element read, bf16 output.  Unless --no-other-workloads,
+    the rate of a plain one-pass HBM read (attn_probe_hbm) is measured after
+    the timed calls, and the roofline also states the step against it."""
     dev = torch.device("cuda:0")
     B, H, Nk, d, Nq, ns = 16, 32, 16384, 128, int(args.decode), int(args.nsplit)
     f8 = bool(args.fp8)
@@ -376,6 +421,13 @@ def bench_decode(args):
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_call": byts,
                      "call_ms": ms},
     }
+    if not args.no_other_workloads:
+        # the rate a plain one-pass read of HBM reaches on this board
+        del qd, kd, vd, ws
+        torch.cuda.empty_cache()
+        c = hbm_ceiling(dev)
+        out["hbm_read_ceiling"] = c
+        out["roofline"]["frac_of_measured_ceiling"] = gbs / c["gbs"]
     print(json.dumps(out), flush=True)
 
 
@@ -861,6 +913,18 @@ def main():
         return
     if args.standard:
         bench_standard(args)
+        return
+    if args.hbm_ceiling:
+        c = hbm_ceiling(torch.device("cuda:0"), reps=max(1, args.steps))
+        print(json.dumps({"metric": "HBM read rate (one pass over a 4 GiB buffer) at 1 GPU",
+                          "value": c["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": c["launches"],
+                          "warmup": 2, "ms_per_step": c["bytes"] / (c["gbs"] * 1e9) * 1e3,
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i32",
+                          "data": "synthetic",
+                          "config": {"workload": "attn_probe_hbm: " + c["kernel"], "bytes": c["bytes"],
+                                     "workgroups": c["workgroups"]},
+                          "frac_of_peak": c["frac_of_spec"], "gbs_by_workgroups": c["gbs_by_workgroups"]}),
+              flush=True)
         return
     if args.ceiling:
         c = mfma_ceiling(torch.device("cuda:0"), reps=max(1, args.steps))

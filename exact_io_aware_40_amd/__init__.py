@@ -111,6 +111,8 @@ def _load():
     lib.attn_std_pv.argtypes = [vp] * 3 + [i64, i64, i64, i64, i32, i32, vp]
     lib.attn_probe_mfma.restype = i32
     lib.attn_probe_mfma.argtypes = [vp, i64, i64, vp]
+    lib.attn_probe_hbm.restype = i32
+    lib.attn_probe_hbm.argtypes = [vp, i64, vp, i64, vp]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [i32]
     _lib = lib
@@ -236,6 +238,10 @@ def attn_std_pv(p: int, v: int, o: int, B: int, H: int, N: int, d: int, dtype: i
 
 def attn_probe_mfma(out: int, workgroups: int, rounds: int, stream: int) -> int:
     return _load().attn_probe_mfma(out, workgroups, rounds, stream)
+
+
+def attn_probe_hbm(buf: int, nbytes: int, out: int, workgroups: int, stream: int) -> int:
+    return _load().attn_probe_hbm(buf, nbytes, out, workgroups, stream)
 
 
 def attn_status_str(status: int) -> str:

@@ -12,6 +12,13 @@
 // step s multiplying A operand j by B operand (j + s) mod 4, four waves per
 // workgroup and two workgroups per CU, so that only the matrix pipes limit
 // the rate.
+//
+// The HBM read probe does the same for memory-bound kernels (a decode step
+// reads its key/value cache once, and the pages measure such kernels by the
+// bytes they move: "13% more FLOPs, 5.7x faster", "The takeaway that
+// outlives the kernel"): it streams a buffer once with 16-byte loads, eight
+// in flight per thread, and keeps only a checksum, so HBM reads are all it
+// costs.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -63,7 +70,41 @@ __global__ __launch_bounds__(PNT, 2) void mfma_probe_kernel(float* __restrict__ 
     out[(size_t)wg_x() * PNT + tid] = t;
 }
 
+// Thread t of T adds, modulo 2^32, the four words of every 16-byte granule
+// t + k T below n16 and stores the sum to out[t].  Eight loads are in flight
+// per thread, each marked non-temporal (every byte is read once): of 4, 8
+// and 16 loads, with and without the hint, this form streamed fastest.
+constexpr int HBM_INFLIGHT = 8;
+
+__global__ __launch_bounds__(PNT) void hbm_probe_kernel(const i32x4* __restrict__ p, long long n16,
+                                                       unsigned* __restrict__ out) {
+    const long long T = (long long)num_wg_x() * PNT;
+    const long long t = (long long)wg_x() * PNT + tid_x();
+    auto words = [](i32x4 x) {
+        return ((unsigned)x[0] + (unsigned)x[1]) + ((unsigned)x[2] + (unsigned)x[3]);
+    };
+    unsigned acc[HBM_INFLIGHT] = {};
+    long long g = t;
+    for (; g + (HBM_INFLIGHT - 1) * T < n16; g += HBM_INFLIGHT * T) {
+        i32x4 x[HBM_INFLIGHT];
+#pragma unroll
+        for (int u = 0; u < HBM_INFLIGHT; ++u) x[u] = __builtin_nontemporal_load(&p[g + u * T]);
+#pragma unroll
+        for (int u = 0; u < HBM_INFLIGHT; ++u) acc[u] += words(x[u]);
+    }
+    for (; g < n16; g += T) acc[0] += words(__builtin_nontemporal_load(&p[g]));
+    unsigned sum = 0;
+#pragma unroll
+    for (int u = 0; u < HBM_INFLIGHT; ++u) sum += acc[u];
+    out[t] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_hbm_probe(const void* buf, long long n16, unsigned* out, int workgroups, hipStream_t stream) {
+    hipLaunchKernelGGL(hbm_probe_kernel, dim3(workgroups), dim3(PNT), 0, stream, (const i32x4*)buf, n16, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(float* out, int workgroups, int rounds, hipStream_t stream) {
     hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(PNT), 0, stream, out, rounds);

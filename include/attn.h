@@ -413,6 +413,27 @@ int attn_std_pv(const void* p, const void* v, void* o, int64_t B, int64_t H, int
  */
 int attn_probe_mfma(float* out, int64_t workgroups, int64_t rounds, void* stream);
 
+/*
+ * attn_probe_hbm -- a measurement aid, not part of the method: the rate at
+ * which this device streams a buffer from HBM, against which memory-bound
+ * kernels (the decode step reads its key/value cache once) are stated beside
+ * the published 8 TB/s (the pages measure such kernels by the bytes they
+ * move: "13% more FLOPs, 5.7x faster", "The takeaway that outlives the
+ * kernel").  Launches `workgroups` workgroups of 256 threads; thread t of
+ * T = workgroups * 256 reads the 16-byte granules t, t + T, t + 2T, ... of
+ * `buf` (eight non-temporal loads in flight) and stores to out[t] the sum,
+ * modulo 2^32, of the 32-bit words it read.  Every byte of `buf` is read
+ * once; the caller times the launch.
+ *   buf        : device buffer, 16-byte aligned, `bytes` long (read only)
+ *   bytes      : 16 .. 2^42, a multiple of 16
+ *   out        : device array of workgroups * 256 unsigned ints (written),
+ *                16-byte aligned, not overlapping buf
+ *   workgroups : 1 .. 2^20
+ * Returns ATTN_OK, ATTN_ERR_SHAPE, ATTN_ERR_NULL, ATTN_ERR_ALIGN,
+ * ATTN_ERR_ALIAS or ATTN_ERR_LAUNCH.
+ */
+int attn_probe_hbm(const void* buf, int64_t bytes, unsigned* out, int64_t workgroups, void* stream);
+
 /* attn_status_str -- static, human-readable name of a status code. */
 const char* attn_status_str(int status);
 

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
                                     "attn_bwd_noalloc",
                                     "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_decode", "attn_fwd_decode_fp8",
                                     "attn_fwd_dropout", "attn_fwd_fp8", "attn_fwd_split",
-                                    "attn_fwd_split_workspace_size", "attn_probe_mfma", "attn_status_str",
+                                    "attn_fwd_split_workspace_size", "attn_probe_hbm", "attn_probe_mfma", "attn_status_str",
                                     "attn_std_fwd",
                                     "attn_std_pv", "attn_std_scores", "attn_std_softmax",
                                     "attn_std_workspace_size"]
@@ -420,6 +420,18 @@ def test_mfma_probe_rejects():
     assert attn.attn_probe_mfma(P[0] + 4, 512, 100, 0) == E_ALIGN
     for wg, it in ((0, 100), (-1, 100), ((1 << 20) + 1, 100), (512, 0), (512, -3), (512, (1 << 24) + 1)):
         assert attn.attn_probe_mfma(P[0], wg, it, 0) == E_SHAPE, (wg, it)
+
+
+def test_hbm_probe_rejects():
+    """The HBM read probe validates before launching (no GPU needed)."""
+    assert attn.attn_probe_hbm(0, 1 << 20, P[1], 64, 0) == E_NULL
+    assert attn.attn_probe_hbm(P[0], 1 << 20, 0, 64, 0) == E_NULL
+    assert attn.attn_probe_hbm(P[0] + 8, 1 << 20, P[1], 64, 0) == E_ALIGN
+    assert attn.attn_probe_hbm(P[0], 1 << 20, P[1] + 4, 64, 0) == E_ALIGN
+    for nb, wg in ((0, 64), (8, 64), (24, 64), ((1 << 42) + 16, 64), (1 << 20, 0), (1 << 20, (1 << 20) + 1)):
+        assert attn.attn_probe_hbm(P[0], nb, P[1], wg, 0) == E_SHAPE, (nb, wg)
+    # the sums may not land in the buffer being read
+    assert attn.attn_probe_hbm(P[0], 1 << 20, P[0] + (1 << 19), 64, 0) == E_ALIAS
 
 
 # ---------------------------------------------------------------------------

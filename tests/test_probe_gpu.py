@@ -1,6 +1,8 @@
-"""The matrix-core rate probe (attn_probe_mfma) on the GPU: its products
-are those its operand definition gives (checked on the host in fp64), and
-its timed rate is a plausible fraction of the published peak."""
+"""The measurement probes on the GPU.  attn_probe_mfma: its products are
+those its operand definition gives (checked on the host in fp64), and its
+timed rate is a plausible fraction of the published peak.  attn_probe_hbm:
+every thread's checksum is the host's for the granules it reads, and its
+timed read rate is plausible."""
 import numpy as np
 import pytest
 import torch
@@ -101,3 +103,48 @@ def test_probe_rate_is_plausible():
     print(f"[probe] {wg} workgroups x {rounds} rounds: {ms:.3f} ms, {tflops:.0f} TFLOP/s", flush=True)
     assert 200.0 < tflops < 2600.0
     assert bool(torch.isfinite(out).all())
+
+
+def expected_thread_sums(words, T):
+    """Thread t's sum (mod 2^32) of the words of 16-byte granules t + k T."""
+    g = words.reshape(-1, 4).astype(np.uint64).sum(axis=1) & 0xFFFFFFFF
+    pad = (-len(g)) % T
+    g = np.concatenate([g, np.zeros(pad, dtype=np.uint64)]).reshape(-1, T)
+    return (g.sum(axis=0) & 0xFFFFFFFF).astype(np.uint32)
+
+
+@pytest.mark.parametrize("granules,wg", [(1, 1), (255, 1), (1000003, 37), (1 << 20, 512), (777, 4096)])
+def test_hbm_probe_sums(granules, wg):
+    """Every thread's checksum equals the host's, for ragged sizes, fewer
+    granules than threads, and more than four granules per thread."""
+    announce(f"hbm probe granules={granules} wg={wg}")
+    rng = np.random.default_rng(granules)
+    words = rng.integers(0, 1 << 32, size=4 * granules, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(DEV)
+    out = torch.full((wg * 256,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    st = attn.attn_probe_hbm(buf.data_ptr(), 16 * granules, out.data_ptr(), wg,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == 0, attn.attn_status_str(st)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, expected_thread_sums(words, wg * 256))
+
+
+def test_hbm_probe_rate_is_plausible():
+    announce("hbm probe rate")
+    nbytes = 1 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+    wg = 16 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(wg * 256, dtype=torch.int32, device=DEV)
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        assert attn.attn_probe_hbm(buf.data_ptr(), nbytes, out.data_ptr(), wg, sp) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    assert attn.attn_probe_hbm(buf.data_ptr(), nbytes, out.data_ptr(), wg, sp) == 0
+    e1.record()
+    e1.synchronize()
+    gbs = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    print(f"[probe] hbm read {nbytes >> 20} MiB, {wg} workgroups: {gbs:.0f} GB/s", flush=True)
+    assert 1000.0 < gbs < 9000.0
+    assert bool((out == 0).all())
