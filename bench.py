@@ -226,11 +226,12 @@ def mfma_ceiling(dev, rounds=15000, reps=5):
                       "between products, 4 chains per wave, 2 waves per SIMD"}
 
 
-def hbm_ceiling(dev, nbytes=4 << 30, reps=5, wg_per_cu=(16, 32, 64)):
+def hbm_ceiling(dev, nbytes=4 << 30, reps=5, wg_per_cu=(2, 4, 8, 16)):
     """The rate at which this board streams a buffer from HBM:
-    attn_probe_hbm (16-byte non-temporal loads, eight in flight per thread,
-    a checksum kept) over `nbytes`, for a few grid sizes, each the median of
-    `reps` launches after two warm-up ones; the best of them."""
+    attn_probe_hbm (each workgroup streams a contiguous range with the
+    kernels' non-temporal direct-to-LDS copies, eight 1 KiB chunks in flight
+    per wave, a checksum kept) over `nbytes`, for a few grid sizes, each the
+    median of `reps` launches after two warm-up ones; the best of them."""
     props = torch.cuda.get_device_properties(dev)
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
@@ -261,7 +262,7 @@ def hbm_ceiling(dev, nbytes=4 << 30, reps=5, wg_per_cu=(16, 32, 64)):
     torch.cuda.empty_cache()
     return {"gbs": sweep[best], "frac_of_spec": sweep[best] / PEAK_HBM_GBS, "bytes": nbytes,
             "workgroups": best, "gbs_by_workgroups": sweep, "launches": reps,
-            "kernel": "hbm_probe_kernel: one pass over the buffer, 16-byte non-temporal loads, eight in flight per thread"}
+            "kernel": "hbm_probe_kernel: one pass over the buffer, a contiguous range per workgroup, non-temporal direct-to-LDS copies, eight 1 KiB chunks in flight per wave"}
 
 
 def cpu_baseline(w, t, scale, budget_s, gpu_out=None):

@@ -16,8 +16,8 @@
 // The HBM read probe does the same for memory-bound kernels (a decode step
 // reads its key/value cache once, and the pages measure such kernels by the
 // bytes they move: "13% more FLOPs, 5.7x faster", "The takeaway that
-// outlives the kernel"): it streams a buffer once with 16-byte loads, eight
-// in flight per thread, and keeps only a checksum, so HBM reads are all it
+// outlives the kernel"): it streams a buffer once with the kernels' own
+// direct-to-LDS copies and keeps only a checksum, so HBM reads are all it
 // costs.
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -70,39 +70,56 @@ __global__ __launch_bounds__(PNT, 2) void mfma_probe_kernel(float* __restrict__ 
     out[(size_t)wg_x() * PNT + tid] = t;
 }
 
-// Thread t of T adds, modulo 2^32, the four words of every 16-byte granule
-// t + k T below n16 and stores the sum to out[t].  Eight loads are in flight
-// per thread, each marked non-temporal (every byte is read once): of 4, 8
-// and 16 loads, with and without the hint, this form streamed fastest.
+// The buffer is cut into 1 KiB chunks (chunk c: the 16-byte granules 64 c
+// .. 64 c + 63) and each workgroup takes a contiguous range of them, as each
+// workgroup of a decode step streams its own part of the key/value cache:
+// workgroup b of B gets chunks b C .. min((b + 1) C, chunks) - 1 with C =
+// ceil(chunks / B), and its wave w the chunks w, w + 4, w + 8, ... of that
+// range.  A wave copies eight chunks at a time into its own LDS slots with
+// the forward's non-temporal direct-to-LDS copy, and lane l adds, modulo
+// 2^32, the four words of granule 64 c + l of every chunk it copied; thread
+// 64 (4 b + w) + l stores that sum.  A copy outside the workgroup's range is
+// zero-length (it reads zeros, as does a partial chunk past the end).  Loads
+// into registers instead (8 in flight, non-temporal, the best of 4, 8 and 16
+// with and without the hint) streamed at 6.3-6.4 TB/s, and so did these
+// copies when each wave's chunks were spread over the whole buffer.
 constexpr int HBM_INFLIGHT = 8;
 
-__global__ __launch_bounds__(PNT) void hbm_probe_kernel(const i32x4* __restrict__ p, long long n16,
+__global__ __launch_bounds__(PNT) void hbm_probe_kernel(const char* __restrict__ p, long long n16,
                                                        unsigned* __restrict__ out) {
-    const long long T = (long long)num_wg_x() * PNT;
-    const long long t = (long long)wg_x() * PNT + tid_x();
-    auto words = [](i32x4 x) {
-        return ((unsigned)x[0] + (unsigned)x[1]) + ((unsigned)x[2] + (unsigned)x[3]);
-    };
-    unsigned acc[HBM_INFLIGHT] = {};
-    long long g = t;
-    for (; g + (HBM_INFLIGHT - 1) * T < n16; g += HBM_INFLIGHT * T) {
-        i32x4 x[HBM_INFLIGHT];
+    __shared__ __attribute__((aligned(1024))) i32x4 slot[HBM_INFLIGHT][PNT];   // 32 KiB
+    const int tid = tid_x(), lane = tid & 63, w = tid >> 6;
+    const long long nbytes = n16 * 16, nchunks = (n16 + 63) / 64, nwg = num_wg_x();
+    const long long per = (nchunks + nwg - 1) / nwg;
+    const long long cb = (long long)wg_x() * per;
+    const long long ce = cb + per < nchunks ? cb + per : nchunks;
+    const unsigned lbase = lds_addr(&slot[0][64 * w]);
+    unsigned acc = 0;
+    for (long long c0 = cb + w; c0 < ce; c0 += HBM_INFLIGHT * (PNT / 64)) {
 #pragma unroll
-        for (int u = 0; u < HBM_INFLIGHT; ++u) x[u] = __builtin_nontemporal_load(&p[g + u * T]);
+        for (int u = 0; u < HBM_INFLIGHT; ++u) {
+            const long long c = c0 + u * (PNT / 64);
+            const long long rem = c < ce ? nbytes - c * 1024 : 0;
+            const unsigned len = rem <= 0 ? 0u : (unsigned)(rem < 1024 ? rem : 1024);
+            dma16_async_once(make_rsrc(p + (rem > 0 ? c * 1024 : 0), len), lbase + u * PNT * 16, 16 * lane);
+        }
+        wait_vmem();
 #pragma unroll
-        for (int u = 0; u < HBM_INFLIGHT; ++u) acc[u] += words(x[u]);
+        for (int u = 0; u < HBM_INFLIGHT; ++u) {
+            const i32x4 x = slot[u][64 * w + lane];
+            acc += ((unsigned)x[0] + (unsigned)x[1]) + ((unsigned)x[2] + (unsigned)x[3]);
+        }
+        // every LDS read of the slots completes before the next copies
+        // overwrite them (lgkmcnt 0; vmcnt and expcnt left alone)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
     }
-    for (; g < n16; g += T) acc[0] += words(__builtin_nontemporal_load(&p[g]));
-    unsigned sum = 0;
-#pragma unroll
-    for (int u = 0; u < HBM_INFLIGHT; ++u) sum += acc[u];
-    out[t] = sum;
+    out[(size_t)wg_x() * PNT + tid] = acc;
 }
 
 }  // namespace
 
 hipError_t launch_hbm_probe(const void* buf, long long n16, unsigned* out, int workgroups, hipStream_t stream) {
-    hipLaunchKernelGGL(hbm_probe_kernel, dim3(workgroups), dim3(PNT), 0, stream, (const i32x4*)buf, n16, out);
+    hipLaunchKernelGGL(hbm_probe_kernel, dim3(workgroups), dim3(PNT), 0, stream, (const char*)buf, n16, out);
     return hipGetLastError();
 }
 

@@ -419,11 +419,16 @@ int attn_probe_mfma(float* out, int64_t workgroups, int64_t rounds, void* stream
  * kernels (the decode step reads its key/value cache once) are stated beside
  * the published 8 TB/s (the pages measure such kernels by the bytes they
  * move: "13% more FLOPs, 5.7x faster", "The takeaway that outlives the
- * kernel").  Launches `workgroups` workgroups of 256 threads; thread t of
- * T = workgroups * 256 reads the 16-byte granules t, t + T, t + 2T, ... of
- * `buf` (eight non-temporal loads in flight) and stores to out[t] the sum,
- * modulo 2^32, of the 32-bit words it read.  Every byte of `buf` is read
- * once; the caller times the launch.
+ * kernel").  Launches `workgroups` workgroups of 256 threads (four waves).
+ * `buf` is cut into 1 KiB chunks (chunk c = bytes 1024 c .. 1024 c + 1023);
+ * workgroup b takes chunks b C .. min((b + 1) C, chunks) - 1, C =
+ * ceil(chunks / workgroups), and its wave w the chunks w, w + 4, w + 8, ...
+ * of that range, copied into LDS with the kernels' non-temporal
+ * direct-to-LDS copy, eight in flight.  Thread 64 (4 b + w) + l stores to
+ * out[256 b + 64 w + l] the sum, modulo 2^32, of the four 32-bit words at
+ * bytes 1024 c + 16 l of every chunk c its wave copied (bytes past the end
+ * of `buf` count as 0).  Every byte of `buf` is read once; the caller times
+ * the launch.
  *   buf        : device buffer, 16-byte aligned, `bytes` long (read only)
  *   bytes      : 16 .. 2^42, a multiple of 16
  *   out        : device array of workgroups * 256 unsigned ints (written),

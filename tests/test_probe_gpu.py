@@ -105,15 +105,35 @@ def test_probe_rate_is_plausible():
     assert bool(torch.isfinite(out).all())
 
 
-def expected_thread_sums(words, T):
-    """Thread t's sum (mod 2^32) of the words of 16-byte granules t + k T."""
-    g = words.reshape(-1, 4).astype(np.uint64).sum(axis=1) & 0xFFFFFFFF
-    pad = (-len(g)) % T
-    g = np.concatenate([g, np.zeros(pad, dtype=np.uint64)]).reshape(-1, T)
-    return (g.sum(axis=0) & 0xFFFFFFFF).astype(np.uint32)
+def expected_thread_sums(words, wg):
+    """Thread 64 (4 b + w) + l's sum (mod 2^32) of the words of granule
+    64 c + l of the 1 KiB chunks c of workgroup b's range (b C .. (b + 1) C,
+    C = ceil(chunks / wg)) with c - b C = w mod 4."""
+    g = words.reshape(-1, 4).astype(np.uint64).sum(axis=1) & 0xFFFFFFFF   # per 16-byte granule
+    g = np.concatenate([g, np.zeros((-len(g)) % 64, dtype=np.uint64)]).reshape(-1, 64)   # [chunk, lane]
+    per = -(-len(g) // wg)
+    g = np.concatenate([g, np.zeros((wg * per - len(g), 64), dtype=np.uint64)]).reshape(wg, per, 64)
+    g = np.concatenate([g, np.zeros((wg, (-per) % 4, 64), dtype=np.uint64)], axis=1).reshape(wg, -1, 4, 64)
+    return (g.sum(axis=1) & 0xFFFFFFFF).astype(np.uint32).reshape(-1)
 
 
-@pytest.mark.parametrize("granules,wg", [(1, 1), (255, 1), (1000003, 37), (1 << 20, 512), (777, 4096)])
+def test_expected_thread_sums_by_brute_force():
+    rng = np.random.default_rng(7)
+    for granules, wg in ((1, 1), (65, 1), (1000, 2), (3000, 5), (64 * 7 + 3, 3)):
+        w = rng.integers(0, 1 << 32, size=4 * granules, dtype=np.uint64).astype(np.uint32)
+        want = [0] * (256 * wg)
+        nch = -(-granules // 64)
+        per = -(-nch // wg)
+        for gi in range(granules):
+            c = gi // 64
+            b = c // per
+            t = 256 * b + 64 * ((c - b * per) % 4) + gi % 64
+            want[t] = (want[t] + int(w[4 * gi:4 * gi + 4].astype(np.uint64).sum())) % (1 << 32)
+        assert np.array_equal(expected_thread_sums(w, wg), np.array(want, dtype=np.uint32))
+
+
+@pytest.mark.parametrize("granules,wg", [(1, 1), (255, 1), (1000003, 37), (1 << 20, 512), (777, 4096),
+                                         (64 * 8 * 4 * 3 + 5, 1)])
 def test_hbm_probe_sums(granules, wg):
     """Every thread's checksum equals the host's, for ragged sizes, fewer
     granules than threads, and more than four granules per thread."""
@@ -127,7 +147,7 @@ def test_hbm_probe_sums(granules, wg):
     assert st == 0, attn.attn_status_str(st)
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint32)
-    assert np.array_equal(got, expected_thread_sums(words, wg * 256))
+    assert np.array_equal(got, expected_thread_sums(words, wg))
 
 
 def test_hbm_probe_rate_is_plausible():
