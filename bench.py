@@ -118,7 +118,9 @@ def parse():
                     help="time a decode step instead: attn_fwd_decode of NQ new queries against "
                          "a 16384-key cache (B=16, H=32, d=128, bf16, causal), against the HBM "
                          "roofline")
-    ap.add_argument("--nsplit", type=int, default=8, help="key chunks of the decode step")
+    ap.add_argument("--nsplit", type=int, default=None,
+                    help="key chunks of the decode step (default: 4 for the 16-bit cache, 8 for the 8-bit one, "
+                         "the faster of the two for each at 1 to 16 queries)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the E4M3 forward (attn_fwd_fp8) on the workload quantised per "
                          "tensor, against the dense fp8 matrix peak; with --decode, the E4M3 "
@@ -360,7 +362,8 @@ def bench_decode(args):
     the rate of a plain one-pass HBM read (attn_probe_hbm) is measured after
     the timed calls, and the roofline also states the step against it."""
     dev = torch.device("cuda:0")
-    B, H, Nk, d, Nq, ns = 16, 32, 16384, 128, int(args.decode), int(args.nsplit)
+    B, H, Nk, d, Nq = 16, 32, 16384, 128, int(args.decode)
+    ns = int(args.nsplit) if args.nsplit is not None else (8 if args.fp8 else 4)
     f8 = bool(args.fp8)
     if f8:
         x, desc = inputs.make_decode_fp8_inputs(B, H, Nq, Nk, d, seed=12)
