@@ -1,6 +1,7 @@
-// attn_fwd_kernel.h -- the fused attention forward kernel for gfx950,
-// included by attn_fwd.hip (every launch) and attn_decode.hip (launches
-// whose K/V tiles each have a single reader).
+// attn_fwd_kernel.h -- the fused attention forward kernel for gfx950.
+// attn_decode.hip instantiates it for grids whose K/V tiles each have a
+// single reader (ONCE: one query block per (batch, head), no dropout), with
+// non-temporal K/V copies; attn_fwd.hip for every other launch.
 //
 // One workgroup owns BR = 128 query rows of one (batch, head) -- under causal
 // masking a pair of such blocks, one after the other -- and streams the K/V
