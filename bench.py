@@ -614,7 +614,7 @@ class StepRunner:
         kernels = {}
         for j_, (nm, _) in enumerate(calls):
             m = float(per[:, j_].mean())
-            kernels[nm] = {"ms_mean": m, "ms_min": float(per[:, j_].min()),
+            kernels[nm] = {"ms_mean": m, "ms_median": float(np.median(per[:, j_])), "ms_min": float(per[:, j_].min()),
                            "algorithmic_tflop": algo[nm] / 1e12,
                            "tflops": algo[nm] / (m * 1e-3) / 1e12,
                            "frac_of_peak": algo[nm] / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
