@@ -2,7 +2,7 @@
 //
 // A kernel's utilisation is stated against two ceilings: the published dense
 // bf16 peak, and the rate a kernel doing nothing but products sustains on the
-// same board at the clock the board holds under it (the pages judge attention
+// same board at the clock the board holds under it (the pages rate attention
 // kernels by the fraction of the hardware's peak they reach: "FlashAttention"
 // explainer, Step 6, and the section "IO-optimal is not occupancy-optimal").
 // The power a product draws depends on how its operand bits change, so the

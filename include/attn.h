@@ -390,7 +390,7 @@ int attn_std_pv(const void* p, const void* v, void* o, int64_t B, int64_t H, int
 /*
  * attn_probe_mfma -- a measurement aid, not part of the method: the rate the
  * matrix cores sustain on this device, against which the kernels'
- * utilisation is stated beside the published peak (the pages judge attention
+ * utilisation is stated beside the published peak (the pages rate attention
  * kernels by the fraction of the hardware's peak they reach: "FlashAttention"
  * explainer, Step 6, "IO-optimal is not occupancy-optimal").  Launches
  * `workgroups` workgroups of 256 threads (four waves); every wave runs
