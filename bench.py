@@ -758,9 +758,14 @@ def attach_counters(w, kernels):
                 "gbs": (rd + wr) / (kern["ms_mean"] * 1e-3) / 1e9,
                 "frac_of_hbm_peak": (rd + wr) / (kern["ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "n2_matrix_bytes": n2,
-                # writes within 10% of the outputs, and reads far below one
-                # N x N matrix: nothing of size N x N reaches HBM
-                "no_n2_traffic": bool(wr <= 1.1 * a["write"] and rd < 0.5 * n2),
+                # reads beyond the algorithmic bytes are tiles of the inputs
+                # fetched again by other workgroups (L2 misses); their total
+                # grows as N^2 d^2 / (tile size) and can reach N^2 itself
+                "excess_read_bytes": rd - a["read"],
+                # S or P in HBM would have to be written there first: every
+                # kernel of the step writing within 10% of its outputs, and
+                # far less than one N x N matrix beyond them, rules it out
+                "no_n2_traffic": bool(wr <= 1.1 * a["write"] and wr - a["write"] < 0.05 * n2),
             }
         c = _committed("counters.json", w.name, k)
         if c:
