@@ -489,6 +489,12 @@ def bench_fp8(args):
                      "launch_ms_min": float(per.min())},
         "kernel_source_hash": source_hash(),
     }
+    c = _committed("counters.json", w.name + "_fp8", "fwd_kernel")
+    if c:
+        # matrix pipes against vector ALU over a profiled launch (8-bit
+        # products take 64 busy cycles each, 2048 FLOP per clock per SIMD)
+        out["roofline"]["counters"] = {x: c[x] for x in ("mfma_busy_frac", "valu_active_frac",
+                                                         "clock_ghz", "duration_ns_median") if x in c}
     print(json.dumps(out), flush=True)
 
 
@@ -711,6 +717,9 @@ def write_counters(dirs, workload):
             if "clock_ghz" in e:
                 e["mfma_frac_of_clock_peak"] = (e["mfma_tflops_by_mops"] * 1e12
                                                 / (e["clock_ghz"] * 1e9 * SIMDS * 1024.0))
+        va = valu_active_frac(e)
+        if va is not None:
+            e["valu_active_frac"] = va
         nmf = e.get("SQ_INSTS_VALU_MFMA_BF16", 0.0) + e.get("SQ_INSTS_VALU_MFMA_F16", 0.0)
         if nmf and "SQ_INSTS_LDS" in e:
             e["lds_insts_per_mfma"] = e["SQ_INSTS_LDS"] / nmf
@@ -776,6 +785,19 @@ def attach_counters(w, kernels):
             if "mfma_flop_by_mops" in c:
                 kern["counters"]["mfma_tflops_by_mops"] = (c["mfma_flop_by_mops"]
                                                            / (kern["ms_mean"] * 1e-3) / 1e12)
+            if "valu_active_frac" in c:
+                kern["counters"]["valu_active_frac"] = c["valu_active_frac"]
+
+
+def valu_active_frac(e):
+    """The SIMDs' vector-ALU issue cycles over their active cycles.
+    SQ_ACTIVE_INST_VALU counts in units of four cycles, the time a SIMD
+    takes to issue one plain wave64 vector instruction (a fit over the
+    forward and both backward kernels gives 1.00 unit per plain
+    instruction, 2.00 per transcendental and 1.00 per matrix product)."""
+    if "SQ_ACTIVE_INST_VALU" in e and "active_cycles_per_xcd" in e:
+        return e["SQ_ACTIVE_INST_VALU"] * 4.0 / (e["active_cycles_per_xcd"] * SIMDS)
+    return None
 
 
 OTHER_WORKLOADS = ("gpt2_medium_fwd", "long_context_fwd", "recompute_bwd")
