@@ -151,15 +151,9 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     const int br = attn::fwd_block_rows();
     a.nqb = int((N + br - 1) / br);
     // causal: when B*H is a multiple of 8, one workgroup per query block in
-    // each XCD's heaviest-first order over groups of heads (the largest of 4,
-    // 3, 2, 1 that divides an XCD's B*H/8 heads); otherwise one per pair of
-    // query blocks (a heavy and a light one)
-    const int64_t per_xcd = BH / 8;
-    int64_t hg = 0;
-    if (causal && BH % 8 == 0)
-        for (hg = 4; per_xcd % hg != 0; --hg) {
-        }
-    a.hgroup = int(hg);
+    // each XCD's heaviest-first order over groups of heads; otherwise one per
+    // pair of query blocks (a heavy and a light one)
+    a.hgroup = attn::xcd_head_group(BH, causal);
     const int64_t total = a.hgroup ? BH * a.nqb : BH * (causal ? (a.nqb + 1) / 2 : a.nqb);
     if (total > 0x7fffffff) return ATTN_ERR_SHAPE;
     a.total = int(total);

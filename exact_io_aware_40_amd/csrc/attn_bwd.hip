@@ -188,7 +188,7 @@ __device__ __forceinline__ void tile_sources(unsigned* src, int w, int lane) {
 //   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 // --------------------------------------------------------------------------
 template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total) {
+__global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total, int hgroup) {
     typedef typename Elem<T>::v8 v8;
     constexpr int ROWB = D * 2, TILE = BKT * ROWB, LOADS = TILE / (NT * 16);
     constexpr int KB = BKT / 32, DK = D / 16, DB = D / 32;
@@ -210,12 +210,26 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a, int nqb, int total
     const int s16 = lane & 15, grp = lane >> 4;
 
     const int L = xcd_remap(wg_x(), total);
-    // Work: one query block of one (batch, head); under causal masking the
-    // pair of blocks nqb-1-p and p of one head, one after the other, so that
-    // every workgroup streams about as many K/V tiles as any other and the
-    // grid has no tail of heavy blocks (wave-uniform: kept in scalar registers)
+    // Work: one query block of one (batch, head).  Under causal masking (the
+    // dispatcher hands workgroup i to XCD i % 8, then to whichever of its
+    // slots frees first):
+    //  - hgroup > 0 (B*H a multiple of 8): XCD x takes the heads congruent to
+    //    x modulo 8, hgroup heads at a time, each group's blocks heaviest
+    //    first, so that the light blocks fill the slots the heavy ones free
+    //    and only the last group's lightest blocks form the tail;
+    //  - otherwise the pair of blocks nqb-1-p and p of one head, one after the
+    //    other, so that every workgroup streams about as many K/V tiles as any
+    //    other.
+    // (wave-uniform: kept in scalar registers)
     int bh, qb_first, qb_second = 0, nitems = 1;
-    if (CAUSAL) {
+    if (CAUSAL && hgroup > 0) {
+        const int i = wg_x(), x = i & 7, m = i >> 3;   // m-th workgroup of XCD x
+        const int per = hgroup * nqb;                    // workgroups of one group
+        const int g = m / per, rem = m - g * per;
+        const int r = rem / hgroup, u = rem - r * hgroup;
+        bh = 8 * (g * hgroup + u) + x;
+        qb_first = nqb - 1 - r;
+    } else if (CAUSAL) {
         const int npairs = (nqb + 1) >> 1;
         bh = L / npairs;
         const int p = L - bh * npairs;
@@ -802,8 +816,10 @@ template <typename T, typename TO, int D, bool CAUSAL, bool DROP>
 hipError_t launch(const BwdArgs& a, int which, hipStream_t stream) {
     if (which & 1) {
         const int nqb = (a.N + BQ - 1) / BQ;
-        const int tq = a.BH * (CAUSAL ? (nqb + 1) / 2 : nqb);   // causal: pairs of query blocks
-        hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL, DROP>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq);
+        const int hg = xcd_head_group(a.BH, CAUSAL);
+        // causal: every query block on its own (head groups) or pairs of them
+        const int tq = hg ? a.BH * nqb : a.BH * (CAUSAL ? (nqb + 1) / 2 : nqb);
+        hipLaunchKernelGGL((dq_kernel<T, TO, D, CAUSAL, DROP>), dim3(tq), dim3(NT), 0, stream, a, nqb, tq, hg);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

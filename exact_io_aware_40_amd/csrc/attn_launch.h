@@ -43,6 +43,17 @@ struct FwdArgs {
                        // each XCD's heaviest-first order (total = B*H*nqb); 0: pairs
 };
 
+// Causal grids with B*H a multiple of 8 (0 otherwise): one workgroup per
+// query block, and XCD x takes the heads congruent to x modulo 8 in groups of
+// this many (the largest of 4, 3, 2, 1 that divides its B*H/8 heads), each
+// group's blocks heaviest first.  The forward and the dq kernel use it.
+inline int xcd_head_group(int64_t BH, int causal) {
+    if (!causal || BH % 8 != 0) return 0;
+    int hg = 4;
+    while ((BH / 8) % hg != 0) --hg;
+    return hg;
+}
+
 int fwd_block_rows();
 hipError_t launch_fwd(const FwdArgs& a, int dtype, bool out_f32, int d, int causal, hipStream_t stream);
 // 8-bit E4M3 q, k, v (d = 128, whole query blocks, no dropout); out_dtype:

@@ -194,6 +194,34 @@ def test_workload_full_size():
     report("full dv(fp32 out)", sel(dv), rv, tol)
 
 
+@pytest.mark.parametrize("B,H,N,d,dtype", [
+    (8, 16, 1153, 64, torch.bfloat16),     # 128 heads: groups of 4, 10 query blocks each
+    (2, 12, 2200, 128, torch.float16),     # 24 heads: groups of 3, ragged tail
+    (1, 16, 3000, 64, torch.bfloat16),     # 16 heads: groups of 2
+    (1, 8, 2500, 128, torch.bfloat16),     # 8 heads: one head per XCD
+    (1, 13, 1500, 64, torch.float16),      # 13 heads: pairs of query blocks
+])
+def test_many_blocks_causal(B, H, N, d, dtype):
+    """Causal grids of several rounds of workgroups over the dq kernel's two
+    mappings (head counts that are and are not multiples of 8): whole heads
+    spread over the grid against the oracle, every gradient finite."""
+    tag = f"many blocks B={B} H={H} N={N} d={d}"
+    announce(f"bwd {tag} {dtype} causal")
+    q, k, v, dO = (randn((B, H, N, d), dtype, 700 + N + d + i) for i in range(4))
+    scale = 1 / math.sqrt(d)
+    BH = B * H
+    heads = sorted({0, 1, BH // 3, BH // 2, (2 * BH) // 3, BH - 1})
+    sel = lambda x: f64(x.reshape(BH, N, d)[heads]).reshape(1, len(heads), N, d)  # noqa: E731
+    tol = TOL[dtype]
+    rq, rk, rv = check_16bit(q, k, v, dO, True, scale, tag, heads=heads)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, dO, True, scale, out_dtype=torch.float32)
+    for g in (dq, dk, dv):
+        assert bool(torch.isfinite(g).all())
+    report(f"{tag} dq(fp32 out)", sel(dq), rq, tol)
+    report(f"{tag} dk(fp32 out)", sel(dk), rk, tol)
+    report(f"{tag} dv(fp32 out)", sel(dv), rv, tol)
+
+
 def test_many_heads():
     """4,097 (batch, head) pairs of 70 rows (a prime-ish count of workgroups
     for both kernels): every gradient element against the oracle."""
