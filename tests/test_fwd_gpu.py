@@ -288,6 +288,9 @@ def test_workload_full_size(name):
     (3, 7, 2560, 64, torch.bfloat16, True),        # 21 heads, pairs
     (4, 64, 777, 128, torch.float16, False),       # 1792 blocks, ragged tail
     (8, 16, 1153, 64, torch.bfloat16, True),       # odd block count (10), head groups
+    (1, 24, 1000, 128, torch.bfloat16, True),      # head groups of 3, ragged tail
+    (2, 8, 1500, 64, torch.float16, True),         # head groups of 2
+    (1, 8, 2000, 128, torch.bfloat16, True),       # one head per XCD
 ])
 def test_many_blocks(B, H, N, d, dtype, causal):
     """Grids of several rounds of workgroups over many heads and blocks:
