@@ -222,6 +222,36 @@ def test_many_blocks_causal(B, H, N, d, dtype):
     report(f"{tag} dv(fp32 out)", sel(dv), rv, tol)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(8, 16, 1153, 64), (2, 12, 2200, 128), (1, 16, 3000, 64),
+                                     (1, 8, 2500, 128), (1, 13, 1500, 64)])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_every_output_written(B, H, N, d, out_f32):
+    """Causal grids over the forward's and dq's head groups (1 to 4 heads)
+    and pairs: o, lse, dq, dk and dv start as NaN and come out finite in
+    every element, so every (head, block) of every grid was computed."""
+    announce(f"every output written B={B} H={H} N={N} d={d} fp32 out={out_f32}")
+    dt = torch.bfloat16
+    q, k, v, dO = (randn((B, H, N, d), dt, 900 + N + i).to(DEV) for i in range(4))
+    code = attn.ATTN_BF16
+    oc = attn.ATTN_F32 if out_f32 else code
+    odt = torch.float32 if out_f32 else dt
+    o, dq, dk, dv = (torch.full((B, H, N, d), float("nan"), dtype=odt, device=DEV) for _ in range(4))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    sp = torch.cuda.current_stream().cuda_stream
+    sc = 1 / math.sqrt(d)
+    assert attn.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         B, H, N, d, sc, 1, code, oc, sp) == 0
+    nbytes = attn.attn_bwd_workspace_size(B, H, N, d, code)
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device=DEV)
+    assert attn.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dO.data_ptr(),
+                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                         nbytes, B, H, N, d, sc, 1, code, oc, sp) == 0
+    torch.cuda.synchronize()
+    for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        bad = (~torch.isfinite(t)).sum().item()
+        assert bad == 0, (name, bad)
+
+
 def test_many_heads():
     """4,097 (batch, head) pairs of 70 rows (a prime-ish count of workgroups
     for both kernels): every gradient element against the oracle."""
