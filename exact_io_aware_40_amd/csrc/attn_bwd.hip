@@ -11,9 +11,10 @@
 //
 // Two kernels, both deterministic (every output element is owned by one
 // lane of one wave, no atomics):
-//   dq_kernel   one workgroup per 128 query rows (under causal masking per
-//               pair of a heavy and a light block of one head); streams K/V
-//               tiles.  It also stores -D_i and lse_i log2(e) of its rows in
+//   dq_kernel   one workgroup per 128 query rows (under causal masking in
+//               the forward's XCD head groups when B*H is a multiple of 8,
+//               else per pair of a heavy and a light block of one head);
+//               streams K/V tiles.  It also stores -D_i and lse_i log2(e) of its rows in
 //               the workspace for the second kernel.
 //   dkdv_kernel one workgroup per 128 keys (under causal masking per pair of
 //               a heavy and a light block of one head); streams Q/dO tiles

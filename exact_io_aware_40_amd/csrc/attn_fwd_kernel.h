@@ -4,7 +4,8 @@
 // non-temporal K/V copies; attn_fwd.hip for every other launch.
 //
 // One workgroup owns BR = 128 query rows of one (batch, head) -- under causal
-// masking a pair of such blocks, one after the other -- and streams the K/V
+// masking with B*H not a multiple of 8, a pair of such blocks, one after the
+// other (otherwise XCD head groups, below) -- and streams the K/V
 // tiles those rows can see through LDS ("FlashAttention" explainer, Step 3
 // "Tiling": a Q block stays on chip while K/V tiles stream past, and each
 // block's output is written once).  Each of its four waves owns 32 of the
