@@ -158,7 +158,7 @@ def _pmc_rows(d):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir, workload):
+def derive_traffic(fetch_dir, write_dir):
     """Per-launch HBM bytes of each kernel from FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch), scaled by copy-bytes / counter-reading of the copy."""
     res = {}
@@ -182,6 +182,14 @@ def write_traffic(fetch_dir, write_dir, workload):
                 e[counter.lower() + "_bytes"] = factor * sum(per[k]) / len(per[k])
     for k, e in res.items():
         e["bytes"] = e.get("fetch_size_bytes", 0.0) + e.get("write_size_bytes", 0.0)
+    return res
+
+
+def write_traffic(fetch_dir, write_dir, workload):
+    """profiles/traffic.json from the two rocprofv3 --pmc runs (derive_traffic),
+    keyed by the kernels' source hash."""
+    res = derive_traffic(fetch_dir, write_dir)
+    for k, e in res.items():
         e["source_hash"] = source_hash(_family(k))
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = {}
@@ -673,9 +681,9 @@ def _num_xcc(dirs):
     return 8
 
 
-def write_counters(dirs, workload):
-    """profiles/counters.json from rocprofv3 --pmc output dirs (any counter
-    set per dir): per kernel, every counter averaged over its dispatches
+def derive_counters(dirs):
+    """Per kernel from rocprofv3 --pmc output dirs (any counter set per
+    dir): every counter averaged over its dispatches
     (each value summed over the GPU's blocks), plus derived figures:
       - the dispatch's duration and the shader clock GRBM_GUI_ACTIVE implies
         (it counts on every XCD, so it is divided by their number);
@@ -698,7 +706,7 @@ def write_counters(dirs, workload):
     res = {}
     for k, cs in per.items():
         e = {c: sum(v) / len(v) for c, v in cs.items()}
-        e["dispatches"] = max(len(v) for v in cs.values())
+        e["dispatches"] = min(len(v) for v in cs.values())   # per pass (GRBM_GUI_ACTIVE is in every pass)
         ns = sorted(dur[k].values())
         e["duration_ns_median"] = ns[len(ns) // 2]
         g = e.get("GRBM_GUI_ACTIVE")
@@ -725,8 +733,16 @@ def write_counters(dirs, workload):
             e["lds_insts_per_mfma"] = e["SQ_INSTS_LDS"] / nmf
         if nmf and "SQ_INSTS_VALU" in e:
             e["valu_insts_per_mfma"] = (e["SQ_INSTS_VALU"] - nmf) / nmf
-        e["source_hash"] = source_hash(_family(k))
         res[k] = e
+    return res
+
+
+def write_counters(dirs, workload):
+    """profiles/counters.json from rocprofv3 --pmc output dirs
+    (derive_counters), keyed by the kernels' source hash."""
+    res = derive_counters(dirs)
+    for k, e in res.items():
+        e["source_hash"] = source_hash(_family(k))
     path = os.path.join(ROOT, "profiles", "counters.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     rec.setdefault(workload, {}).update(res)
@@ -748,6 +764,28 @@ def _committed(name, workload, kernel):
     return None
 
 
+def hbm_entry(rd, wr, alg, n2, ms):
+    """A kernel's counter bytes read (rd) and written (wr) per launch against
+    its algorithmic bytes (alg: {"read", "write"}), one N x N matrix in 16
+    bits (n2) and its launch time in ms."""
+    return {
+        "read_bytes": rd, "write_bytes": wr,
+        "algorithmic_read_bytes": alg["read"], "algorithmic_write_bytes": alg["write"],
+        "read_ratio": rd / alg["read"], "write_ratio": wr / alg["write"],
+        "gbs": (rd + wr) / (ms * 1e-3) / 1e9,
+        "frac_of_hbm_peak": (rd + wr) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "n2_matrix_bytes": n2,
+        # reads beyond the algorithmic bytes are tiles of the inputs fetched
+        # again by other workgroups (L2 misses); their total grows as
+        # N^2 d^2 / (tile size) and can reach N^2 itself
+        "excess_read_bytes": rd - alg["read"],
+        # S or P in HBM would have to be written there first: every kernel of
+        # the step writing within 10% of its outputs, and far less than one
+        # N x N matrix beyond them, rules it out
+        "no_n2_traffic": bool(wr <= 1.1 * alg["write"] and wr - alg["write"] < 0.05 * n2),
+    }
+
+
 def attach_counters(w, kernels):
     """Per kernel: HBM bytes from the committed FETCH/WRITE counters against
     the algorithmic bytes (and the GB/s they mean at the live launch time),
@@ -758,24 +796,8 @@ def attach_counters(w, kernels):
     for k, kern in kernels.items():
         tr = _committed("traffic.json", w.name, k)
         if tr and k in alg:
-            rd, wr = tr.get("fetch_size_bytes", 0.0), tr.get("write_size_bytes", 0.0)
-            a = alg[k]
-            kern["hbm"] = {
-                "read_bytes": rd, "write_bytes": wr,
-                "algorithmic_read_bytes": a["read"], "algorithmic_write_bytes": a["write"],
-                "read_ratio": rd / a["read"], "write_ratio": wr / a["write"],
-                "gbs": (rd + wr) / (kern["ms_mean"] * 1e-3) / 1e9,
-                "frac_of_hbm_peak": (rd + wr) / (kern["ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                "n2_matrix_bytes": n2,
-                # reads beyond the algorithmic bytes are tiles of the inputs
-                # fetched again by other workgroups (L2 misses); their total
-                # grows as N^2 d^2 / (tile size) and can reach N^2 itself
-                "excess_read_bytes": rd - a["read"],
-                # S or P in HBM would have to be written there first: every
-                # kernel of the step writing within 10% of its outputs, and
-                # far less than one N x N matrix beyond them, rules it out
-                "no_n2_traffic": bool(wr <= 1.1 * a["write"] and wr - a["write"] < 0.05 * n2),
-            }
+            kern["hbm"] = hbm_entry(tr.get("fetch_size_bytes", 0.0), tr.get("write_size_bytes", 0.0),
+                                    alg[k], n2, kern["ms_mean"])
         c = _committed("counters.json", w.name, k)
         if c:
             kern["counters"] = {x: c[x] for x in ("mfma_busy_frac", "mfma_flop_by_mops",
